@@ -1,0 +1,222 @@
+"""Python handle on the CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE. Only the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module. It shares no code with
+the GPU library and never imports it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+Q8_0 = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc: -O2, no fast-math, no fp contraction."""
+    src = os.path.join(_HERE, "oracle.c")
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-fPIC", "-shared", "-o", tmp, src, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def bind(path: str):
+    """Load an oracle shared library at path and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    sig = {
+        "or_open": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(_vp)]),
+        "or_close": (None, [_vp]),
+        "or_reset_kv": (None, [_vp]),
+        "or_key_cache": (_vp, [_vp]),
+        "or_value_cache": (_vp, [_vp]),
+        "or_logits": (_vp, [_vp]),
+        "or_residual": (_vp, [_vp]),
+        "or_attn_out": (_vp, [_vp]),
+        "or_set_threads": (None, [ctypes.c_int]),
+        "or_threads": (ctypes.c_int, []),
+        "or_quantize": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int, _vp, _vp]),
+        "or_group_dots": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int, _vp]),
+        "or_rope_freqs": (None, [ctypes.c_int64, _vp]),
+        "or_rope": (None, [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+        "or_argmax": (ctypes.c_int, [_vp, ctypes.c_int64]),
+        "or_trace_layer": (None, [_vp, ctypes.c_int]),
+        "or_trace_codes": (_vp, [_vp, ctypes.c_int]),
+        "or_trace_scales": (_vp, [_vp, ctypes.c_int]),
+        "or_trace_input": (_vp, [_vp, ctypes.c_int]),
+        "or_forward": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        _lib = bind(_SO)
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_vp)
+
+
+def set_threads(n: int) -> None:
+    _load().or_set_threads(n)
+
+
+def threads() -> int:
+    return int(_load().or_threads())
+
+
+def quantize(x: np.ndarray, gs: int = 64):
+    """Q8_0 quantise an fp32 vector: (codes int8[n], scales fp32[n/gs])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.empty(x.size, dtype=np.int8)
+    s = np.empty(x.size // gs if gs > 0 else 0, dtype=np.float32)
+    rc = _load().or_quantize(_ptr(x), x.size, gs, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("or_quantize: invalid size/group")
+    return q, s
+
+
+def group_dots(wq: np.ndarray, xq: np.ndarray, gs: int = 64) -> np.ndarray:
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    out = np.empty(wq.size // gs, dtype=np.int32)
+    rc = _load().or_group_dots(_ptr(wq), _ptr(xq), wq.size, gs, _ptr(out))
+    if rc != 0:
+        raise ValueError("or_group_dots: invalid size/group")
+    return out
+
+
+def rope_freqs(hs: int) -> np.ndarray:
+    out = np.empty(hs // 2, dtype=np.float32)
+    _load().or_rope_freqs(hs, _ptr(out))
+    return out
+
+
+def rope(vec: np.ndarray, nheads: int, hs: int, pos: int) -> np.ndarray:
+    v = np.array(vec, dtype=np.float32, copy=True)
+    _load().or_rope(_ptr(v), nheads, hs, pos)
+    return v
+
+
+def argmax(v: np.ndarray) -> int:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    return int(_load().or_argmax(_ptr(v), v.size))
+
+
+class Model:
+    """The oracle over a weight blob (numpy uint8, kept alive here)."""
+
+    def __init__(self, blob: np.ndarray, dtype: int, gs: int = 64):
+        self._blob = blob
+        h = ctypes.c_void_p()
+        rc = _load().or_open(_ptr(blob), blob.size, dtype, gs, ctypes.byref(h))
+        if rc != 0:
+            raise ValueError(f"or_open failed: {rc}")
+        self._h = h
+        hdr = np.frombuffer(blob[:28].tobytes(), dtype=np.int32)
+        (self.dim, self.hidden_dim, self.n_layers, self.n_heads, self.n_kv_heads,
+         vs, self.seq_len) = (int(v) for v in hdr)
+        self.vocab = abs(vs)
+        self.head_size = self.dim // self.n_heads
+        self.kv_dim = self.n_kv_heads * self.head_size
+        self.dtype = dtype
+        self.gs = gs
+
+    def close(self):
+        if self._h:
+            _load().or_close(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _view(self, addr, n, dt):
+        buf = (ctypes.c_byte * (n * np.dtype(dt).itemsize)).from_address(addr)
+        return np.frombuffer(buf, dtype=dt)
+
+    def forward(self, token: int, pos: int) -> np.ndarray:
+        rc = _load().or_forward(self._h, int(token), int(pos))
+        if rc != 0:
+            raise ValueError(f"or_forward failed: {rc}")
+        return self._view(_load().or_logits(self._h), self.vocab, np.float32).copy()
+
+    def reset_kv(self):
+        _load().or_reset_kv(self._h)
+
+    def key_cache(self) -> np.ndarray:
+        n = self.n_layers * self.seq_len * self.kv_dim
+        return self._view(_load().or_key_cache(self._h), n, np.float32).reshape(
+            self.n_layers, self.seq_len, self.kv_dim)
+
+    def value_cache(self) -> np.ndarray:
+        n = self.n_layers * self.seq_len * self.kv_dim
+        return self._view(_load().or_value_cache(self._h), n, np.float32).reshape(
+            self.n_layers, self.seq_len, self.kv_dim)
+
+    def residual(self) -> np.ndarray:
+        return self._view(_load().or_residual(self._h), self.dim, np.float32).copy()
+
+    def attn_out(self) -> np.ndarray:
+        """The last layer's attention output of the last forward."""
+        return self._view(_load().or_attn_out(self._h), self.dim, np.float32).copy()
+
+    def trace_layer(self, layer: int):
+        _load().or_trace_layer(self._h, layer)
+
+    def trace(self, slot: int):
+        """(codes, scales, fp32 input) of the traced layer's matvec input `slot`."""
+        n = self.hidden_dim if slot == 3 else self.dim
+        lib = _load()
+        q = self._view(lib.or_trace_codes(self._h, slot), n, np.int8).copy()
+        s = self._view(lib.or_trace_scales(self._h, slot), n // self.gs, np.float32).copy()
+        f = self._view(lib.or_trace_input(self._h, slot), n, np.float32).copy()
+        return q, s, f
+
+
+def trajectory(model: Model, forced: np.ndarray, n_steps: int, keep_logits: bool = True):
+    """Greedy decode with forced prompt ids from pos 0.
+
+    Returns (tokens fed at each pos, argmax at each pos, logits per pos or None).
+    The token fed at pos p is forced[p] while p < len(forced), else the argmax
+    of pos p-1.
+    """
+    fed = np.empty(n_steps, dtype=np.int32)
+    am = np.empty(n_steps, dtype=np.int32)
+    logits = np.empty((n_steps, model.vocab), dtype=np.float32) if keep_logits else None
+    tok = int(forced[0])
+    for p in range(n_steps):
+        if p < len(forced):
+            tok = int(forced[p])
+        fed[p] = tok
+        lg = model.forward(tok, p)
+        am[p] = argmax(lg)
+        if keep_logits:
+            logits[p] = lg
+        tok = int(am[p])
+    return fed, am, logits

@@ -1,0 +1,527 @@
+/*
+ * oracle.c - plain, slow CPU oracle of the Llama-2 single-token decode step
+ * (llama2.c run.c in fp32, runq.c in Q8_0).
+ *
+ * TEST INFRASTRUCTURE. Only the test-suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or constant with the GPU library, and parses the weight blob
+ * with its own code.
+ *
+ * Precision. Every tensor the model stores (weights, KV cache, the residual
+ * stream and each activation vector handed from one step to the next) is
+ * fp32, as in the pages' C engine (the KV cache is an array of float, gitcode
+ * porting guide, section "memory optimisation"). Every reduction (sum of
+ * squares, dot products, softmax max/sum, the attention weighted sum, the
+ * Q8_0 group combine) runs in fp64 and is rounded to fp32 where the model
+ * stores the value. Three places run in fp32 because the pages fix them
+ * there: the RoPE angle pos*freq and its cosf/sinf (Karpathy tech notes, Q&A
+ * page, question on RoPE in C versus PyTorch), and the Q8_0 quantiser
+ * (gitcode porting guide, section "1. INT8 quantisation", the quantize
+ * listing), where a float max, a float division by 127 and a rounding of a
+ * float quotient decide the integer codes.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp (no -Ofast / -ffast-math: the
+ * gitcode guide's Makefile section notes that -Ofast trades precision).
+ * Rows of every matvec are split over OpenMP threads; the summation order
+ * inside a row is fixed, so results do not depend on the thread count.
+ *
+ * Readings of the pages where they are silent (each also listed in the design
+ * notes): RMSNorm y = g * x / sqrt(mean(x^2) + 1e-5); RoPE rotates interleaved
+ * pairs (2j, 2j+1) of each q and k head by pos * 10000^(-2j/hs); attention
+ * scores are scaled by 1/sqrt(head_size); query head h reads kv head
+ * h / (n_heads / n_kv_heads); SwiGLU is silu(w1 x) * (w3 x); pre-norm
+ * residuals; an all-zero Q8_0 group gets scale 0 and codes 0; argmax ties go
+ * to the lowest index.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_F32 0
+#define OR_Q8_0 1
+
+#define OR_OK 0
+#define OR_EINVAL -1
+#define OR_EFORMAT -2
+#define OR_ENOMEM -3
+
+typedef struct {
+    int32_t dim, hidden_dim, n_layers, n_heads, n_kv_heads, vocab_size, seq_len;
+} or_config;
+
+/* one matrix: fp32 values, or Q8_0 codes + one fp32 scale per gs elements */
+typedef struct {
+    const float* f;
+    const int8_t* q;
+    const float* s;
+} or_mat;
+
+typedef struct {
+    or_config c;
+    int dtype, gs;
+    int64_t d, h, L, V, S, nh, nkv, hs, kvd, kvmul;
+    or_mat emb, wq, wk, wv, wo, w1, w2, w3, wcls;
+    const float *rms_att, *rms_ffn, *rms_final;
+    float* kc; /* [L][S][kvd] */
+    float* vc;
+    /* activations, fp32 as stored by the model */
+    float *x, *xb, *q, *k, *v, *o, *y, *h1, *h3, *hb, *logits;
+    int8_t* aq; /* quantised activation codes (Q8_0 path) */
+    float* as;
+    /* trace of one layer's quantised matvec inputs (Q8_0 path) */
+    int trace_layer;
+    int8_t* tq[4];
+    float* ts[4];
+    float* tf[4];
+} or_model;
+
+/* ---------------------------------------------------------------- parsing */
+
+static int64_t i64abs(int64_t v) { return v < 0 ? -v : v; }
+
+static int take(const uint8_t** p, const uint8_t* end, int64_t bytes, const void** out)
+{
+    if (bytes < 0 || (int64_t)(end - *p) < bytes) return 0;
+    *out = *p;
+    *p += bytes;
+    return 1;
+}
+
+static int take_mat(or_model* m, const uint8_t** p, const uint8_t* end, int64_t n, or_mat* w)
+{
+    const void* a;
+    memset(w, 0, sizeof(*w));
+    if (m->dtype == OR_F32) {
+        if (!take(p, end, 4 * n, &a)) return 0;
+        w->f = (const float*)a;
+    } else {
+        if (!take(p, end, n, &a)) return 0;
+        w->q = (const int8_t*)a;
+        if (!take(p, end, 4 * (n / m->gs), &a)) return 0;
+        w->s = (const float*)a;
+    }
+    return 1;
+}
+
+/*
+ * Open a model over a blob (borrowed, must outlive the model).
+ * Header: seven int32 config fields, then the arrays in the llama2.c order
+ * (pomoai.com hub page, data-format section). vocab_size < 0 means the
+ * classifier is a separate array after the legacy tables (Karpathy tech
+ * notes, Q&A page, shared_weights question). The two legacy freq_cis tables,
+ * seq_len*head_size/2 floats each, are skipped (same Q&A page, question on
+ * skipping freq_cis in memory_map_weights).
+ */
+int or_open(const void* blob, int64_t nbytes, int dtype, int gs, or_model** out)
+{
+    *out = NULL;
+    if (!blob || nbytes < 28 || (dtype != OR_F32 && dtype != OR_Q8_0)) return OR_EINVAL;
+    or_model* m = (or_model*)calloc(1, sizeof(or_model));
+    if (!m) return OR_ENOMEM;
+    memcpy(&m->c, blob, 28);
+    m->dtype = dtype;
+    m->gs = gs;
+    m->d = m->c.dim;
+    m->h = m->c.hidden_dim;
+    m->L = m->c.n_layers;
+    m->nh = m->c.n_heads;
+    m->nkv = m->c.n_kv_heads;
+    m->V = i64abs(m->c.vocab_size);
+    m->S = m->c.seq_len;
+    if (m->d <= 0 || m->h <= 0 || m->L <= 0 || m->nh <= 0 || m->nkv <= 0 || m->V <= 0 ||
+        m->S <= 0 || m->d % m->nh || m->nh % m->nkv || (m->d / m->nh) % 2) {
+        free(m);
+        return OR_EINVAL;
+    }
+    m->hs = m->d / m->nh;
+    m->kvd = m->nkv * m->hs;
+    m->kvmul = m->nh / m->nkv;
+    if (dtype == OR_Q8_0 && (gs <= 0 || m->d % gs || m->h % gs)) {
+        free(m);
+        return OR_EINVAL;
+    }
+    const uint8_t* p = (const uint8_t*)blob + 28;
+    const uint8_t* end = (const uint8_t*)blob + nbytes;
+    const void* a;
+    int64_t d = m->d, h = m->h, L = m->L, kvd = m->kvd;
+    int ok = take_mat(m, &p, end, m->V * d, &m->emb);
+    ok = ok && take(&p, end, 4 * L * d, &a);
+    if (ok) m->rms_att = (const float*)a;
+    ok = ok && take_mat(m, &p, end, L * d * d, &m->wq);
+    ok = ok && take_mat(m, &p, end, L * kvd * d, &m->wk);
+    ok = ok && take_mat(m, &p, end, L * kvd * d, &m->wv);
+    ok = ok && take_mat(m, &p, end, L * d * d, &m->wo);
+    ok = ok && take(&p, end, 4 * L * d, &a);
+    if (ok) m->rms_ffn = (const float*)a;
+    ok = ok && take_mat(m, &p, end, L * h * d, &m->w1);
+    ok = ok && take_mat(m, &p, end, L * d * h, &m->w2);
+    ok = ok && take_mat(m, &p, end, L * h * d, &m->w3);
+    ok = ok && take(&p, end, 4 * d, &a);
+    if (ok) m->rms_final = (const float*)a;
+    ok = ok && take(&p, end, 4 * m->S * (m->hs / 2), &a); /* legacy freq_cis_real */
+    ok = ok && take(&p, end, 4 * m->S * (m->hs / 2), &a); /* legacy freq_cis_imag */
+    if (ok) {
+        if (m->c.vocab_size > 0)
+            m->wcls = m->emb;
+        else
+            ok = take_mat(m, &p, end, m->V * d, &m->wcls);
+    }
+    if (!ok || p != end) {
+        free(m);
+        return OR_EFORMAT;
+    }
+    int64_t kvn = L * m->S * kvd;
+    m->kc = (float*)calloc((size_t)kvn, sizeof(float));
+    m->vc = (float*)calloc((size_t)kvn, sizeof(float));
+    int64_t big = d > h ? d : h;
+    m->x = (float*)calloc(d, 4);
+    m->xb = (float*)calloc(d, 4);
+    m->q = (float*)calloc(d, 4);
+    m->k = (float*)calloc(kvd, 4);
+    m->v = (float*)calloc(kvd, 4);
+    m->o = (float*)calloc(d, 4);
+    m->y = (float*)calloc(d, 4);
+    m->h1 = (float*)calloc(h, 4);
+    m->h3 = (float*)calloc(h, 4);
+    m->hb = (float*)calloc(h, 4);
+    m->logits = (float*)calloc(m->V, 4);
+    m->aq = (int8_t*)calloc(big, 1);
+    m->as = (float*)calloc(big, 4);
+    m->trace_layer = -1;
+    if (!m->kc || !m->vc || !m->x || !m->xb || !m->q || !m->k || !m->v || !m->o || !m->y ||
+        !m->h1 || !m->h3 || !m->hb || !m->logits || !m->aq || !m->as) {
+        /* leak-free enough for a test oracle: release what exists */
+        free(m->kc); free(m->vc); free(m->x); free(m->xb); free(m->q); free(m->k);
+        free(m->v); free(m->o); free(m->y); free(m->h1); free(m->h3); free(m->hb);
+        free(m->logits); free(m->aq); free(m->as); free(m);
+        return OR_ENOMEM;
+    }
+    *out = m;
+    return OR_OK;
+}
+
+void or_close(or_model* m)
+{
+    if (!m) return;
+    free(m->kc); free(m->vc); free(m->x); free(m->xb); free(m->q); free(m->k);
+    free(m->v); free(m->o); free(m->y); free(m->h1); free(m->h3); free(m->hb);
+    free(m->logits); free(m->aq); free(m->as);
+    for (int i = 0; i < 4; i++) { free(m->tq[i]); free(m->ts[i]); free(m->tf[i]); }
+    free(m);
+}
+
+void or_reset_kv(or_model* m)
+{
+    int64_t kvn = m->L * m->S * m->kvd;
+    memset(m->kc, 0, (size_t)kvn * 4);
+    memset(m->vc, 0, (size_t)kvn * 4);
+}
+
+float* or_key_cache(or_model* m) { return m->kc; }
+float* or_value_cache(or_model* m) { return m->vc; }
+float* or_logits(or_model* m) { return m->logits; }
+float* or_residual(or_model* m) { return m->x; }
+/* the last layer's attention output o (n_heads*head_size) of the last forward */
+float* or_attn_out(or_model* m) { return m->o; }
+
+void or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int or_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------- the method */
+
+/*
+ * Q8_0 quantisation of a vector, group by group, as the quantize listing of
+ * the gitcode porting guide (section "1. INT8 quantisation") computes it:
+ * the group's largest |x| in float, scale = that max / 127 as a float
+ * division, code = the float quotient x/scale rounded half away from zero
+ * (C round) and cast to int8. A group whose max is 0 (the listing would
+ * divide 0 by 0) gets scale 0 and codes 0. n must be a multiple of gs.
+ */
+int or_quantize(const float* x, int64_t n, int gs, int8_t* q, float* s)
+{
+    if (gs <= 0 || n < 0 || n % gs) return OR_EINVAL;
+    int64_t ng = n / gs;
+    #pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; g++) {
+        const float* xg = x + g * gs;
+        float wmax = 0.0f;
+        for (int i = 0; i < gs; i++) {
+            float a = fabsf(xg[i]);
+            if (a > wmax) wmax = a;
+        }
+        float scale = wmax / 127.0f;
+        s[g] = scale;
+        for (int i = 0; i < gs; i++) {
+            if (scale == 0.0f) {
+                q[g * gs + i] = 0;
+            } else {
+                float r = xg[i] / scale;
+                q[g * gs + i] = (int8_t)roundf(r);
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * RMSNorm (pomoai.com hub page, architecture list; it replaces LayerNorm):
+ * out_i = g_i * x_i / sqrt(sum(x^2)/n + eps), eps = 1e-5, in fp64, stored fp32.
+ */
+static void rmsnorm(float* out, const float* x, const float* g, int64_t n)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; i++) ss += (double)x[i] * (double)x[i];
+    double r = 1.0 / sqrt(ss / (double)n + 1e-5);
+    for (int64_t i = 0; i < n; i++) out[i] = (float)((double)g[i] * ((double)x[i] * r));
+}
+
+/*
+ * Matrix-vector product out = W x with W row-major [rows][cols] (the
+ * hand-written matmul the ainews article's technical section describes; the
+ * toy forward pass of the mht18 essay, section 2.3, ends with one).
+ * fp32: fp64 dot of fp32 values, stored fp32.
+ * Q8_0: x is first quantised (int8 activations; the Q&A page explains the
+ * int8 speed-up by integer multiply-adds); per group the int8 dot is exact
+ * in integers, then scaled by the weight and activation scales and summed
+ * in fp64.
+ */
+static void matvec(or_model* m, float* out, const float* x, const or_mat* w, int64_t woff,
+                   int64_t rows, int64_t cols, int trace_slot)
+{
+    if (m->dtype == OR_F32) {
+        const float* W = w->f + woff;
+        #pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < rows; i++) {
+            const float* wr = W + i * cols;
+            double acc = 0.0;
+            for (int64_t j = 0; j < cols; j++) acc += (double)wr[j] * (double)x[j];
+            out[i] = (float)acc;
+        }
+        return;
+    }
+    int gs = m->gs;
+    or_quantize(x, cols, gs, m->aq, m->as);
+    if (trace_slot >= 0) {
+        memcpy(m->tq[trace_slot], m->aq, (size_t)cols);
+        memcpy(m->ts[trace_slot], m->as, (size_t)(cols / gs) * 4);
+        memcpy(m->tf[trace_slot], x, (size_t)cols * 4);
+    }
+    const int8_t* Q = w->q + woff;
+    const float* S = w->s + woff / gs;
+    const int8_t* aq = m->aq;
+    const float* as = m->as;
+    int64_t ng = cols / gs;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; i++) {
+        const int8_t* qr = Q + i * cols;
+        const float* sr = S + i * ng;
+        double acc = 0.0;
+        for (int64_t g = 0; g < ng; g++) {
+            int64_t dot = 0;
+            for (int j = 0; j < gs; j++) dot += (int64_t)qr[g * gs + j] * (int64_t)aq[g * gs + j];
+            acc += (double)dot * (double)sr[g] * (double)as[g];
+        }
+        out[i] = (float)acc;
+    }
+}
+
+/* the int32 group dot products of one Q8_0 matvec row: out[g] for g < cols/gs */
+int or_group_dots(const int8_t* wq, const int8_t* xq, int64_t cols, int gs, int32_t* out)
+{
+    if (gs <= 0 || cols % gs) return OR_EINVAL;
+    for (int64_t g = 0; g < cols / gs; g++) {
+        int64_t dot = 0;
+        for (int j = 0; j < gs; j++) dot += (int64_t)wq[g * gs + j] * (int64_t)xq[g * gs + j];
+        out[g] = (int32_t)dot;
+    }
+    return OR_OK;
+}
+
+/*
+ * RoPE computed on the fly (Karpathy tech notes, Q&A page, question on RoPE
+ * in C versus PyTorch: the C engine evaluates cosf/sinf of pos*freq in every
+ * forward instead of reading a table). Reading: within each head the pairs
+ * (2j, 2j+1) rotate by pos * freq_j, freq_j = 10000^(-2j/hs) (computed in
+ * fp64, rounded to fp32), angle = (float)pos * freq_j in fp32, then cosf and
+ * sinf; the rotation itself runs in fp64 and is stored fp32.
+ */
+static void rope(float* vec, int64_t nheads, int64_t hs, int pos)
+{
+    for (int64_t hd = 0; hd < nheads; hd++) {
+        float* hv = vec + hd * hs;
+        for (int64_t j = 0; j < hs / 2; j++) {
+            float freq = (float)pow(10000.0, -(double)(2 * j) / (double)hs);
+            float ang = (float)pos * freq;
+            double c = (double)cosf(ang), sn = (double)sinf(ang);
+            double a = hv[2 * j], b = hv[2 * j + 1];
+            hv[2 * j] = (float)(a * c - b * sn);
+            hv[2 * j + 1] = (float)(a * sn + b * c);
+        }
+    }
+}
+
+/* the fp32 frequency table the rope above uses (exposed for tests) */
+void or_rope_freqs(int64_t hs, float* out)
+{
+    for (int64_t j = 0; j < hs / 2; j++) out[j] = (float)pow(10000.0, -(double)(2 * j) / (double)hs);
+}
+
+/* apply rope to an arbitrary vector of nheads heads (exposed for tests) */
+void or_rope(float* vec, int64_t nheads, int64_t hs, int pos) { rope(vec, nheads, hs, pos); }
+
+/*
+ * Attention of one layer over cached positions 0..pos (Karpathy tech notes,
+ * Q&A page: the KV-cache question places k, v of position pos at offset
+ * loff + pos*kv_dim; the GQA question gives q n_heads*head_size and k, v
+ * n_kv_heads*head_size, query heads sharing a kv head). For query head hd
+ * and kv head g = hd / kvmul: score_t = q.k_t / sqrt(hs); a = softmax(score);
+ * o = sum_t a_t v_t. All in fp64, o stored fp32.
+ */
+static void attention(or_model* m, int64_t l, int pos)
+{
+    int64_t hs = m->hs, kvd = m->kvd;
+    const float* kl = m->kc + l * m->S * kvd;
+    const float* vl = m->vc + l * m->S * kvd;
+    double scale = 1.0 / sqrt((double)hs);
+    #pragma omp parallel for schedule(static)
+    for (int64_t hd = 0; hd < m->nh; hd++) {
+        int64_t g = hd / m->kvmul;
+        const float* qh = m->q + hd * hs;
+        double* sc = (double*)malloc(sizeof(double) * (size_t)(pos + 1));
+        double mx = -INFINITY;
+        for (int64_t t = 0; t <= pos; t++) {
+            const float* kt = kl + t * kvd + g * hs;
+            double dot = 0.0;
+            for (int64_t i = 0; i < hs; i++) dot += (double)qh[i] * (double)kt[i];
+            sc[t] = dot * scale;
+            if (sc[t] > mx) mx = sc[t];
+        }
+        double z = 0.0;
+        for (int64_t t = 0; t <= pos; t++) {
+            sc[t] = exp(sc[t] - mx);
+            z += sc[t];
+        }
+        for (int64_t i = 0; i < hs; i++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t <= pos; t++) acc += sc[t] * (double)vl[t * kvd + g * hs + i];
+            m->o[hd * hs + i] = (float)(acc / z);
+        }
+        free(sc);
+    }
+}
+
+/* residual add x += y, the sum of two stored fp32 vectors, stored fp32 */
+static void residual(float* x, const float* y, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) x[i] = (float)((double)x[i] + (double)y[i]);
+}
+
+/* first index of the largest value (sample_argmax in the gitcode guide's
+   embedded main loop); ties go to the lowest index */
+int or_argmax(const float* v, int64_t n)
+{
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; i++)
+        if (v[i] > v[best]) best = i;
+    return (int)best;
+}
+
+static void trace_alloc(or_model* m)
+{
+    int64_t sizes[4] = {m->d, m->d, m->d, m->h};
+    for (int i = 0; i < 4; i++) {
+        if (!m->tq[i]) {
+            m->tq[i] = (int8_t*)calloc(sizes[i], 1);
+            m->ts[i] = (float*)calloc(sizes[i], 4);
+            m->tf[i] = (float*)calloc(sizes[i], 4);
+        }
+    }
+}
+
+/* record the quantised inputs of layer l's four matvecs (Q8_0 only):
+   slot 0 QKV input, 1 output-projection input, 2 W1/W3 input, 3 W2 input */
+void or_trace_layer(or_model* m, int l)
+{
+    m->trace_layer = l;
+    if (l >= 0) trace_alloc(m);
+}
+
+int8_t* or_trace_codes(or_model* m, int slot) { return m->tq[slot]; }
+float* or_trace_scales(or_model* m, int slot) { return m->ts[slot]; }
+float* or_trace_input(or_model* m, int slot) { return m->tf[slot]; }
+
+/*
+ * One decode step: token at position pos -> logits[V]; writes KV slot pos.
+ * Order of the step (pomoai.com hub page architecture list; Q&A page on the
+ * KV cache, GQA and RoPE; mht18 essay section 2.3): embedding row; per layer
+ * pre-norm attention block (RMSNorm, q/k/v matvecs, RoPE on q and k, K/V
+ * cache write, attention, output matvec, residual) and pre-norm SwiGLU block
+ * (RMSNorm, w1 and w3 matvecs, silu(w1 x) * w3 x, w2 matvec, residual); final
+ * RMSNorm; classifier matvec (the embedding table when vocab_size > 0).
+ */
+int or_forward(or_model* m, int token, int pos)
+{
+    if (token < 0 || token >= m->V || pos < 0 || pos >= m->S) return OR_EINVAL;
+    int64_t d = m->d, h = m->h, kvd = m->kvd, hs = m->hs;
+
+    /* embedding row; Q8_0 dequantises it (code times its group scale) */
+    if (m->dtype == OR_F32) {
+        memcpy(m->x, m->emb.f + (int64_t)token * d, (size_t)d * 4);
+    } else {
+        const int8_t* qr = m->emb.q + (int64_t)token * d;
+        const float* sr = m->emb.s + (int64_t)token * d / m->gs;
+        for (int64_t i = 0; i < d; i++)
+            m->x[i] = (float)((double)qr[i] * (double)sr[i / m->gs]);
+    }
+
+    for (int64_t l = 0; l < m->L; l++) {
+        int tr = (m->dtype == OR_Q8_0 && m->trace_layer == (int)l);
+        rmsnorm(m->xb, m->x, m->rms_att + l * d, d);
+        matvec(m, m->q, m->xb, &m->wq, l * d * d, d, d, tr ? 0 : -1);
+        matvec(m, m->k, m->xb, &m->wk, l * kvd * d, kvd, d, -1);
+        matvec(m, m->v, m->xb, &m->wv, l * kvd * d, kvd, d, -1);
+        rope(m->q, m->nh, hs, pos);
+        rope(m->k, m->nkv, hs, pos);
+        float* kslot = m->kc + (l * m->S + pos) * kvd;
+        float* vslot = m->vc + (l * m->S + pos) * kvd;
+        memcpy(kslot, m->k, (size_t)kvd * 4);
+        memcpy(vslot, m->v, (size_t)kvd * 4);
+        attention(m, l, pos);
+        matvec(m, m->y, m->o, &m->wo, l * d * d, d, d, tr ? 1 : -1);
+        residual(m->x, m->y, d);
+
+        rmsnorm(m->xb, m->x, m->rms_ffn + l * d, d);
+        matvec(m, m->h1, m->xb, &m->w1, l * h * d, h, d, tr ? 2 : -1);
+        matvec(m, m->h3, m->xb, &m->w3, l * h * d, h, d, -1);
+        for (int64_t i = 0; i < h; i++) {
+            double z = m->h1[i];
+            double silu = z / (1.0 + exp(-z));
+            m->hb[i] = (float)(silu * (double)m->h3[i]);
+        }
+        matvec(m, m->y, m->hb, &m->w2, l * d * h, d, h, tr ? 3 : -1);
+        residual(m->x, m->y, d);
+    }
+
+    rmsnorm(m->xb, m->x, m->rms_final, d);
+    matvec(m, m->logits, m->xb, &m->wcls, 0, m->V, d, -1);
+    return OR_OK;
+}

@@ -1,0 +1,90 @@
+"""The pins bite: plant one plausible mistake at a time in a copy of the
+oracle (on the CPU), rebuild it, and require that at least one pin fails.
+
+Each mutation is a textual substitution in oracle.c: a dropped term, a wrong
+sign or index, a transposed operand, the wrong rounding. The mutant is a
+separate shared library; the real oracle is untouched.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+MUTATIONS = {
+    "rope_sign": ("hv[2 * j] = (float)(a * c - b * sn);", "hv[2 * j] = (float)(a * c + b * sn);"),
+    "rope_freq_index": ("-(double)(2 * j) / (double)hs);\n            float ang",
+                        "-(double)(j) / (double)hs);\n            float ang"),
+    "rope_k_dropped": ("rope(m->k, m->nkv, hs, pos);", ";"),
+    "attn_scale": ("double scale = 1.0 / sqrt((double)hs);", "double scale = 1.0 / (double)hs;"),
+    "gqa_index": ("int64_t g = hd / m->kvmul;", "int64_t g = hd % m->nkv;"),
+    "attn_drops_current_pos": ("for (int64_t t = 0; t <= pos; t++) {\n            const float* kt",
+                               "for (int64_t t = 0; t < pos; t++) {\n            const float* kt"),
+    "rmsnorm_eps_dropped": ("ss / (double)n + 1e-5", "ss / (double)n"),
+    "rmsnorm_sum_not_mean": ("ss / (double)n + 1e-5", "ss + 1e-5"),
+    "quant_half_even": ("q[g * gs + i] = (int8_t)roundf(r);", "q[g * gs + i] = (int8_t)rintf(r);"),
+    "quant_scale_255": ("float scale = wmax / 127.0f;", "float scale = wmax / 255.0f;"),
+    "q8_act_scale_dropped": ("acc += (double)dot * (double)sr[g] * (double)as[g];",
+                             "acc += (double)dot * (double)sr[g];"),
+    "swiglu_branches_swapped": ("double z = m->h1[i];", "double z = m->h3[i];"),
+    "residual_dropped": ("matvec(m, m->y, m->o, &m->wo, l * d * d, d, d, tr ? 1 : -1);\n        residual(m->x, m->y, d);",
+                         "matvec(m, m->y, m->o, &m->wo, l * d * d, d, d, tr ? 1 : -1);"),
+    "matvec_transposed": ("for (int64_t j = 0; j < cols; j++) acc += (double)wr[j] * (double)x[j];",
+                          "for (int64_t j = 0; j < cols; j++) acc += (double)W[j * rows + i] * (double)x[j];"),
+    "kv_slot_off_by_layer": ("float* kslot = m->kc + (l * m->S + pos) * kvd;",
+                             "float* kslot = m->kc + (pos) * kvd;"),
+    "emb_dequant_scale_dropped": ("m->x[i] = (float)((double)qr[i] * (double)sr[i / m->gs]);",
+                                  "m->x[i] = (float)((double)qr[i]);"),
+}
+
+PIN_TESTS = [
+    pins.test_quantize_handworked_golden,
+    pins.test_quantize_exact_rational_bruteforce,
+    pins.test_rope_unit_pair_gives_cos_sin,
+    pins.test_rope_preserves_pair_norms_and_relative_position,
+    lambda: pins.test_oracle_matches_full_sequence_bruteforce(pins.TINY, 0, 12),
+    lambda: pins.test_oracle_matches_full_sequence_bruteforce(pins.TINY_Q8, 1, 8),
+    pins.test_attention_pos0_is_v_and_equal_keys_give_mean_v,
+    pins.test_rmsnorm_closed_form_through_embedding,
+]
+
+
+def _any_pin_fails(lib) -> bool:
+    saved = oracle._lib
+    oracle._lib = lib
+    try:
+        for t in PIN_TESTS:
+            try:
+                with np.errstate(all="ignore"):
+                    t()
+            except (AssertionError, ValueError, FloatingPointError):
+                return True
+        return False
+    finally:
+        oracle._lib = saved
+
+
+def test_unmutated_copy_passes(tmp_path):
+    so = tmp_path / "liboracle_copy.so"
+    shutil.copy(SRC, tmp_path / "o.c")
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                           "-o", str(so), str(tmp_path / "o.c"), "-lm"])
+    assert not _any_pin_fails(oracle.bind(str(so)))
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    (tmp_path / "m.c").write_text(src.replace(old, new))
+    so = tmp_path / f"liboracle_{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                           "-o", str(so), str(tmp_path / "m.c"), "-lm"])
+    assert _any_pin_fails(oracle.bind(str(so))), f"no pin catches mutation {name}"
