@@ -1,0 +1,202 @@
+/*
+ * l2d.h - C ABI of the MI355X (gfx950) single-token Llama-2 decode step.
+ *
+ * The step is llama2.c's forward(token, pos) -> logits, in fp32 (run.c) and
+ * in Q8_0 (runq.c: int8 codes with one fp32 scale per group of GS values,
+ * activations quantised before every matvec). The interface follows the shape
+ * the pages show: build the transformer from a weight file, call
+ * forward(transformer, token, pos) for a float* of logits, then take the
+ * argmax (gitcode porting guide, embedded main-loop example); quantize(x, n)
+ * with a global group size (same guide, INT8 quantisation section); a KV
+ * cache that starts zeroed (same guide, memory section).
+ *
+ * Conventions for every entry point:
+ *   - return 0 (L2D_OK) on success or a negative L2D_E* code; nothing here
+ *     calls exit() or abort(). l2d_last_error() describes the last failure.
+ *   - "device" pointers are HIP device memory on the current device; "host"
+ *     pointers are ordinary process memory.
+ *   - a context is not thread-safe: one context per host thread/stream.
+ *   - all work of a context is enqueued on its stream, in order.
+ */
+#ifndef L2D_H
+#define L2D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define L2D_F32 0  /* fp32 weights and activations (run.c) */
+#define L2D_Q8_0 1 /* int8 weight/activation codes, fp32 group scales (runq.c) */
+
+#define L2D_OK 0
+#define L2D_EINVAL (-1)  /* bad argument: config, group size, token, pos, size */
+#define L2D_EFORMAT (-2) /* blob size or layout does not match its header */
+#define L2D_ENOMEM (-3)  /* host or device allocation failed */
+#define L2D_EHIP (-4)    /* a HIP runtime call failed */
+
+/*
+ * Model configuration. The first seven fields are the blob header, in its
+ * order: seven little-endian int32 (pomoai.com hub page, data-format
+ * section). head_size = dim / n_heads; kv_dim = n_kv_heads * head_size (Q&A
+ * page, GQA question). vocab_size > 0: the classifier is the embedding table;
+ * vocab_size < 0: a separate classifier array of |vocab_size| rows follows
+ * the legacy tables (Q&A page, shared_weights question).
+ */
+typedef struct {
+    int32_t dim, hidden_dim, n_layers, n_heads, n_kv_heads, vocab_size, seq_len;
+    int32_t dtype;      /* L2D_F32 or L2D_Q8_0 */
+    int32_t group_size; /* Q8_0 group size GS (64 for the workloads); ignored for fp32 */
+    float rope_theta;   /* 10000 */
+    float norm_eps;     /* 1e-5 */
+} l2d_config;
+
+/*
+ * Host views of the weights, borrowed from the caller (normally pointers into
+ * a blob parsed by l2d_blob_parse). Matrices are row-major [rows][cols] with
+ * cols the input size. fp32: the matrix pointer is float*, the *_s scale
+ * pointer is NULL. Q8_0: the matrix pointer is int8_t codes[rows*cols] and
+ * *_s is float scales[rows*cols/GS], one per group of GS consecutive codes.
+ * Per-layer arrays are stacked over layers: wq is [n_layers][dim][dim], etc.
+ */
+typedef struct {
+    const void* emb;  const float* emb_s;   /* [vocab][dim] */
+    const float* rms_att;                   /* [n_layers][dim] */
+    const void* wq;   const float* wq_s;    /* [n_layers][dim][dim] */
+    const void* wk;   const float* wk_s;    /* [n_layers][kv_dim][dim] */
+    const void* wv;   const float* wv_s;    /* [n_layers][kv_dim][dim] */
+    const void* wo;   const float* wo_s;    /* [n_layers][dim][dim] */
+    const float* rms_ffn;                   /* [n_layers][dim] */
+    const void* w1;   const float* w1_s;    /* [n_layers][hidden_dim][dim] */
+    const void* w2;   const float* w2_s;    /* [n_layers][dim][hidden_dim] */
+    const void* w3;   const float* w3_s;    /* [n_layers][hidden_dim][dim] */
+    const float* rms_final;                 /* [dim] */
+    const void* wcls; const float* wcls_s;  /* [vocab][dim]; == emb when shared */
+} l2d_weights;
+
+typedef struct l2d_ctx l2d_ctx;
+
+/*
+ * Parse a weight blob held in host memory (zero-copy: w points into blob).
+ * Layout: the seven-int32 header, then emb, rms_att, wq, wk, wv, wo, rms_ffn,
+ * w1, w2, w3, rms_final, the two legacy freq_cis tables of
+ * seq_len*head_size/2 floats each (skipped: RoPE is computed on the fly,
+ * Q&A page, freq_cis question), then wcls when vocab_size < 0. In a Q8_0 blob
+ * each matrix is codes[n] then scales[n/GS]. cfg gets the header plus dtype,
+ * group_size, rope_theta = 10000, norm_eps = 1e-5.
+ * Errors: L2D_EINVAL for a bad dtype/GS or an invalid header (dim % n_heads,
+ * n_heads % n_kv_heads, odd head_size, GS not dividing dim and hidden_dim,
+ * a non-positive field); L2D_EFORMAT when nbytes differs from the size the
+ * header implies. All offsets are 64-bit.
+ */
+int l2d_blob_parse(const void* blob, uint64_t nbytes, int32_t dtype, int32_t group_size,
+                   l2d_config* cfg, l2d_weights* w);
+
+/*
+ * Create a context on the current HIP device: allocate device weights (in the
+ * library's own layout), the zeroed KV cache [n_layers][seq_len][kv_dim] fp32
+ * (gitcode guide, memory section; Q&A page, KV-cache question), activations
+ * and scratch; copy the weights host->device; capture one decode step as a
+ * HIP graph. stream: a hipStream_t to run on, or NULL for a stream the
+ * context creates and owns. The host weights may be freed after return.
+ * Supported: dim and hidden_dim multiples of 4; head_size even and <= 256;
+ * Q8_0 group size a power of two in [16, 1024] dividing dim and hidden_dim.
+ * Errors: L2D_EINVAL, L2D_ENOMEM (device memory), L2D_EHIP.
+ */
+int l2d_init(const l2d_config* cfg, const l2d_weights* w, void* stream, l2d_ctx** out);
+
+/*
+ * One decode step: the embedding row of token, every layer at position pos
+ * (k and v are written to cache slot pos, attention reads slots 0..pos),
+ * final norm, classifier and argmax. Returns a device pointer to
+ * logits[|vocab_size|] fp32, owned by the context and valid until the next
+ * forward; the values are ready once the context's stream has reached this
+ * point (l2d_sync). Returns NULL on error (token not in [0, vocab), pos not
+ * in [0, seq_len)). Re-running the same (token, pos) rewrites the same cache
+ * slot with the same values.
+ */
+const float* l2d_forward(l2d_ctx* ctx, int32_t token, int32_t pos);
+
+/*
+ * Like l2d_forward, with the token taken on the device from the argmax of
+ * the previous step (greedy decoding without a host round trip). pos must be
+ * >= 1 and the previous forward of this context must have been at pos - 1.
+ */
+const float* l2d_forward_greedy(l2d_ctx* ctx, int32_t pos);
+
+/* Wait for the context's stream. */
+int l2d_sync(l2d_ctx* ctx);
+
+/*
+ * Argmax of the last forward's logits: the lowest index among equal maxima
+ * (sample_argmax of the gitcode guide's main loop). Waits for the stream.
+ */
+int l2d_last_token(l2d_ctx* ctx, int32_t* token);
+
+/* Copy the last forward's logits to host memory (|vocab_size| floats). Waits. */
+int l2d_read_logits(l2d_ctx* ctx, float* host_dst);
+
+/*
+ * Q8_0-quantise n fp32 values (device x) into device q[n] and s[n/gs], group
+ * by group as the quantize listing of the gitcode porting guide (section
+ * "1. INT8 quantisation") does: the group's largest |x|, scale = that / 127
+ * (fp32 division), code = round half away from zero of the fp32 quotient x /
+ * scale. An all-zero group gets scale 0 and codes 0. stream: hipStream_t or
+ * NULL (the null stream). Asynchronous. Errors: L2D_EINVAL when gs <= 0,
+ * n < 0 or n % gs != 0, or a pointer is NULL while n > 0.
+ */
+int l2d_quantize_q80(const float* x, int64_t n, int32_t gs, int8_t* q, float* s, void* stream);
+
+/* Zero the KV cache (the calloc'd state of a fresh run). Asynchronous. */
+int l2d_reset_kv(l2d_ctx* ctx);
+
+/* Release everything the context owns. NULL is a no-op. */
+void l2d_free(l2d_ctx* ctx);
+
+/* Message for the last error of ctx, or of the calling thread when ctx is NULL. */
+const char* l2d_last_error(const l2d_ctx* ctx);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics and test hooks. They expose intermediate results of the same
+ * kernels the decode step runs; none is needed to decode.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Device pointers to the KV cache, [n_layers][seq_len][kv_dim] fp32 each.
+ * Writing them (e.g. to place synthetic keys/values at deep positions) is
+ * allowed between steps.
+ */
+int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache);
+
+/*
+ * Matvec out = W x with the decode step's GEMV kernel (all device pointers):
+ * W is fp32 [rows][cols] (dtype L2D_F32, W_s NULL) or Q8_0 codes with scales
+ * W_s [rows][cols/gs]; x is fp32 [cols] (quantised inside the kernel for
+ * Q8_0, as in the decode step); out is fp32 [rows]. group_dots, when not NULL
+ * (Q8_0 only), receives the exact int32 dot of every (row, group):
+ * [rows][cols/gs]. rows must be even. Asynchronous on stream.
+ */
+int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
+             int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream);
+
+/*
+ * Trace the quantised matvec inputs of one layer (Q8_0): after l2d_trace_layer
+ * (ctx, layer) the next forwards record, for that layer, the codes and scales
+ * the kernels computed for slot 0 (q/k/v input), 1 (output-projection input),
+ * 2 (w1/w3 input), 3 (w2 input); l2d_trace_read copies one slot to host
+ * (codes n, scales n/gs; n = dim, or hidden_dim for slot 3). layer -1 stops
+ * tracing. Tracing runs the step without the captured graph.
+ */
+int l2d_trace_layer(l2d_ctx* ctx, int32_t layer);
+int l2d_trace_read(l2d_ctx* ctx, int32_t slot, int8_t* host_q, float* host_s);
+
+/* 1: replay the captured graph (default); 0: launch the step's kernels one by one. */
+int l2d_use_graph(l2d_ctx* ctx, int32_t enable);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* L2D_H */

@@ -13,7 +13,7 @@
  * porting guide, section "memory optimisation"). Every reduction (sum of
  * squares, dot products, softmax max/sum, the attention weighted sum, the
  * Q8_0 group combine) runs in fp64 and is rounded to fp32 where the model
- * stores the value. Three places run in fp32 because the pages fix them
+ * stores the value. Two places run in fp32 because the pages fix them
  * there: the RoPE angle pos*freq and its cosf/sinf (Karpathy tech notes, Q&A
  * page, question on RoPE in C versus PyTorch), and the Q8_0 quantiser
  * (gitcode porting guide, section "1. INT8 quantisation", the quantize
@@ -361,8 +361,10 @@ int or_group_dots(const int8_t* wq, const int8_t* xq, int64_t cols, int gs, int3
  * in C versus PyTorch: the C engine evaluates cosf/sinf of pos*freq in every
  * forward instead of reading a table). Reading: within each head the pairs
  * (2j, 2j+1) rotate by pos * freq_j, freq_j = 10000^(-2j/hs) (computed in
- * fp64, rounded to fp32), angle = (float)pos * freq_j in fp32, then cosf and
- * sinf; the rotation itself runs in fp64 and is stored fp32.
+ * fp64, rounded to fp32), angle = (float)pos * freq_j in fp32; cosf and sinf
+ * are taken as the fp32 cosine and sine of that fp32 angle, correctly
+ * rounded (the fp64 value rounded to fp32), so the result does not depend on
+ * one libm's last-bit behaviour; the rotation runs in fp64 and is stored fp32.
  */
 static void rope(float* vec, int64_t nheads, int64_t hs, int pos)
 {
@@ -371,7 +373,7 @@ static void rope(float* vec, int64_t nheads, int64_t hs, int pos)
         for (int64_t j = 0; j < hs / 2; j++) {
             float freq = (float)pow(10000.0, -(double)(2 * j) / (double)hs);
             float ang = (float)pos * freq;
-            double c = (double)cosf(ang), sn = (double)sinf(ang);
+            double c = (double)(float)cos((double)ang), sn = (double)(float)sin((double)ang);
             double a = hv[2 * j], b = hv[2 * j + 1];
             hv[2 * j] = (float)(a * c - b * sn);
             hv[2 * j + 1] = (float)(a * sn + b * c);

@@ -175,8 +175,9 @@ def test_rope_unit_pair_gives_cos_sin():
         r = oracle.rope(v, 1, hs, pos)
         for j in range(hs // 2):
             ang = float(np.float32(np.float32(pos) * freqs[j]))
-            assert abs(r[2 * j] - math.cos(ang)) <= 2e-7 * max(1, abs(math.cos(ang))) + 1e-7
-            assert abs(r[2 * j + 1] - math.sin(ang)) <= 2e-7 * max(1, abs(math.sin(ang))) + 1e-7
+            # rotating (1, 0) gives exactly the fp32 cosine / sine of the fp32 angle
+            assert r[2 * j] == np.float32(math.cos(ang))
+            assert r[2 * j + 1] == np.float32(math.sin(ang))
 
 
 def test_rope_preserves_pair_norms_and_relative_position():
