@@ -1,0 +1,228 @@
+"""Decode-step benchmark of the MI355X Llama-2 decode library.
+
+One step = one pass of the whole decode step (embedding, every layer's
+RMSNorm, q/k/v matvec, RoPE, KV-cache write, GQA attention, output matvec,
+SwiGLU FFN, residuals, final norm, classifier and argmax) for one token at
+batch 1, replayed as the captured HIP graph. Weights are random N(0, 0.02)
+of the 7B shape (synthetic, seeded), resident in HBM before timing starts.
+
+The cache is filled by a real greedy decode from pos 0 (on device, no host
+round trip). At each reported position the step is replayed K times at that
+same position (re-running (token, pos) rewrites the same cache slot with the
+same values), timed with HIP events on the context's stream between two
+synchronisations.
+
+Prints one JSON line. value = tokens/s of the Q8_0 step at the headline
+position; per-position and fp32 figures ride along under "detail".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(cfg, dtype: int, pos: int, gs: int = 64) -> dict:
+    """Algorithmic HBM bytes of one step at pos: every matvec weight once
+    (with Q8_0 scales), one embedding row, the KV rows read (slots 0..pos)
+    and the k/v slot written."""
+    d, h, L, V = cfg.dim, cfg.hidden_dim, cfg.n_layers, cfg.vocab
+    kvd = cfg.kv_dim
+    bpp = 4.0 if dtype == 0 else 1.0 + 4.0 / gs
+    qkv = (d + 2 * kvd) * d * bpp
+    wo = d * d * bpp
+    w13 = 2 * h * d * bpp
+    w2 = d * h * bpp
+    cls = V * d * bpp
+    emb_row = d * bpp
+    kv_read = 2 * (pos + 1) * kvd * 4
+    kv_write = 2 * kvd * 4
+    total = L * (qkv + wo + w13 + w2 + kv_read + kv_write) + cls + emb_row
+    return {"total": total, "qkv": qkv, "wo": wo, "w13": w13, "w2": w2, "cls": cls,
+            "attn": kv_read}
+
+
+def time_replays(ctx, token: int, pos: int, steps: int, warmup: int, torch) -> float:
+    """Seconds per step over `steps` graph replays at (token, pos)."""
+    stream = torch.cuda.ExternalStream(ctx.stream_handle())
+    for _ in range(warmup):
+        ctx.forward(token, pos)
+    ctx.sync()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        ctx.forward(token, pos)
+    end.record(stream)
+    ctx.sync()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def kernel_times(ctx, token: int, pos: int, reps: int) -> dict:
+    """Average duration (s) of each kernel class of the step, from HIP events
+    recorded around every launch on the context's stream (kernel-by-kernel
+    launches, same kernels and grids as the graph)."""
+    return ctx.kernel_profile(token, pos, reps)
+
+
+def decode_to(ctx, positions, torch):
+    """Greedy decode from pos 0 through max(positions); returns the token fed
+    at each requested position."""
+    last = max(positions)
+    fed = {}
+    ctx.forward(1, 0)
+    if 0 in positions:
+        fed[0] = 1
+    for p in range(1, last + 1):
+        if p in positions:
+            ctx.sync()
+            fed[p] = ctx.last_token()
+            ctx.forward(fed[p], p)
+        else:
+            ctx.forward_greedy(p)
+    ctx.sync()
+    return fed
+
+
+def bench_dtype(cfg, dtype, positions, steps, warmup, torch, l2d, synth):
+    t = time.time()
+    blob = synth.make_blob(cfg, dtype)
+    log(f"[bench] {cfg.name} dtype={'q8_0' if dtype else 'fp32'}: blob {blob.size / 1e9:.2f} GB "
+        f"generated in {time.time() - t:.1f}s")
+    t = time.time()
+    ctx = l2d.Context(blob, dtype)
+    del blob
+    log(f"[bench] upload + graph capture {time.time() - t:.1f}s")
+    t = time.time()
+    fed = decode_to(ctx, positions, torch)
+    log(f"[bench] greedy decode 0..{max(positions)} in {time.time() - t:.1f}s")
+    res = {}
+    for p in positions:
+        sec = time_replays(ctx, fed[p], p, steps, warmup, torch)
+        b = step_bytes(cfg, dtype, p)
+        res[p] = {"tok_s": 1.0 / sec, "ms": sec * 1e3,
+                  "step_gbs": b["total"] / sec / 1e9, "step_bytes": b["total"]}
+        log(f"[bench]   pos {p}: {sec * 1e3:.3f} ms/step, {1 / sec:.1f} tok/s, "
+            f"{b['total'] / sec / 1e9:.0f} GB/s algorithmic")
+    return ctx, fed, res
+
+
+def cpu_baseline(cfg, dtype, budget_s: float = 15.0) -> dict:
+    """The oracle, untuned, on this host's cores: greedy decode from pos 0 for
+    about budget_s seconds (at least 2 steps)."""
+    import oracle
+    import synth
+    blob = synth.make_blob(cfg, dtype)
+    m = oracle.Model(blob, dtype)
+    t0 = time.time()
+    n = 0
+    tok = 1
+    import numpy as np
+    while n < 2 or time.time() - t0 < budget_s:
+        lg = m.forward(tok, n)
+        tok = int(np.argmax(lg))
+        n += 1
+    dt = time.time() - t0
+    cores = oracle.threads()
+    m.close()
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} greedy decode steps of the {cfg.name}-shape "
+                      f"{'Q8_0' if dtype else 'fp32'} model from pos 0 ({dt:.1f}s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="7B")
+    ap.add_argument("--positions", default="1,512,2048")
+    ap.add_argument("--headline-pos", type=int, default=512)
+    ap.add_argument("--dtypes", default="q8_0,fp32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the multi-GPU split is described in the design notes, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import llama_transformer_decode_amd as l2d
+    import synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    positions = sorted({int(p) for p in args.positions.split(",")} | {args.headline_pos})
+    dtypes = [0 if d.strip() == "fp32" else 1 for d in args.dtypes.split(",")]
+    detail = {}
+    head = None
+    for dt in dtypes:
+        name = "q8_0" if dt else "fp32"
+        ctx, fed, res = bench_dtype(cfg, dt, positions, args.steps, args.warmup, torch, l2d, synth)
+        # per-kernel HIP-event timing at the headline position
+        kt = kernel_times(ctx, fed[args.headline_pos], args.headline_pos, 3)
+        b = step_bytes(cfg, dt, args.headline_pos)
+        kern = {}
+        for k, sec in kt.items():
+            kb = b.get(k)
+            kern[k] = {"avg_us": sec * 1e6}
+            if kb:
+                kern[k]["gbs"] = kb / sec / 1e9
+        detail[name] = {"per_pos": {str(p): res[p] for p in positions}, "kernels": kern}
+        log(f"[bench] {name} kernels at pos {args.headline_pos}: " +
+            ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['gbs']:.0f}GB/s" if 'gbs' in v else "")
+                      for k, v in kern.items()))
+        if head is None:
+            head = (dt, res[args.headline_pos], kt, b)
+        ctx.close()
+        del ctx
+        torch.cuda.empty_cache()
+
+    dt, r, kt, b = head
+    w13 = b["w13"] / kt["w13"] / 1e9
+    out = {
+        "metric": "decode tokens/sec at batch 1 + achieved HBM GB/s vs peak (7B-shape Q8_0 & fp32)",
+        "value": r["tok_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xint8->int32, fp32/fp64" if dt else "f32 (fp64 accumulate)",
+        "data": "synthetic: seeded random N(0,0.02)-like weights of the 7B shape",
+        "config": {"workload": f"{cfg.name}-shape Llama-2 decode step, "
+                               f"{'Q8_0 GS=64' if dt else 'fp32'}, batch 1, pos {args.headline_pos}",
+                   "global_batch": 1, "seq_len": cfg.seq_len, "pos": args.headline_pos,
+                   "parallelism": "single GPU"},
+        "hbm_step_gbs": r["step_gbs"],
+        "hbm_step_frac": r["step_gbs"] / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "kernel": "gemv w1/w3 + SwiGLU",
+                     "achieved": w13, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": w13 / PEAK_HBM_GBS, "traffic": None},
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        out["cpu_baseline"] = cpu_baseline(cfg, dt, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

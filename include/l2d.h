@@ -49,8 +49,8 @@ typedef struct {
     int32_t dim, hidden_dim, n_layers, n_heads, n_kv_heads, vocab_size, seq_len;
     int32_t dtype;      /* L2D_F32 or L2D_Q8_0 */
     int32_t group_size; /* Q8_0 group size GS (64 for the workloads); ignored for fp32 */
-    float rope_theta;   /* 10000 */
-    float norm_eps;     /* 1e-5 */
+    double rope_theta;  /* 10000 */
+    double norm_eps;    /* 1e-5 */
 } l2d_config;
 
 /*
@@ -191,6 +191,19 @@ int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int
  */
 int l2d_trace_layer(l2d_ctx* ctx, int32_t layer);
 int l2d_trace_read(l2d_ctx* ctx, int32_t slot, int8_t* host_q, float* host_s);
+
+/* The hipStream_t the context enqueues on. */
+void* l2d_stream(l2d_ctx* ctx);
+
+/*
+ * Run the step at (token, pos) reps times with the kernels launched one by
+ * one and HIP events recorded around every launch on the context's stream;
+ * avg_seconds[7] receives the mean duration per launch of each kernel class:
+ * 0 q/k/v matvec (+norm, RoPE, cache write), 1 attention, 2 output matvec,
+ * 3 w1/w3 matvec (+norm, SwiGLU), 4 w2 matvec, 5 classifier (+norm, argmax),
+ * 6 step start (embedding row). Synchronous.
+ */
+int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, double* avg_seconds);
 
 /* 1: replay the captured graph (default); 0: launch the step's kernels one by one. */
 int l2d_use_graph(l2d_ctx* ctx, int32_t enable);

@@ -1,0 +1,725 @@
+// ctx.cpp - the C ABI: context creation, weight upload, the decode step as a
+// captured HIP graph, and the diagnostic hooks.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "internal.hpp"
+#include "l2d.h"
+#include "runtime.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+}  // namespace
+
+namespace l2d {
+
+int fail(l2d_ctx* ctx, int code, const std::string& msg)
+{
+    if (ctx)
+        ctx->err = msg;
+    else
+        g_err = msg;
+    return code;
+}
+
+static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int validate_config(const l2d_config* c)
+{
+    auto bad = [](const char* m) { return fail(nullptr, L2D_EINVAL, m); };
+    if (c->dim <= 0 || c->hidden_dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 ||
+        c->n_kv_heads <= 0 || c->vocab_size == 0 || c->seq_len <= 0)
+        return bad("config: every header field must be positive (vocab_size non-zero)");
+    if (c->dim % c->n_heads) return bad("config: dim must be a multiple of n_heads");
+    if (c->n_heads % c->n_kv_heads) return bad("config: n_heads must be a multiple of n_kv_heads");
+    const int hs = c->dim / c->n_heads;
+    if (hs % 2) return bad("config: head_size must be even (RoPE rotates pairs)");
+    if (c->dtype != L2D_F32 && c->dtype != L2D_Q8_0) return bad("config: unknown dtype");
+    if (c->dtype == L2D_Q8_0) {
+        const int gs = c->group_size;
+        if (!pow2(gs) || gs < 16 || gs > 1024)
+            return bad("config: Q8_0 group size must be a power of two in [16, 1024]");
+        if (c->dim % gs || c->hidden_dim % gs)
+            return bad("config: Q8_0 group size must divide dim and hidden_dim");
+    }
+    return L2D_OK;
+}
+
+// limits of the kernels beyond the format's own rules
+static int check_supported(l2d_ctx* ctx, const l2d_config* c)
+{
+    const int hs = c->dim / c->n_heads;
+    if (c->dim % 4 || c->hidden_dim % 4)
+        return fail(ctx, L2D_EINVAL, "init: dim and hidden_dim must be multiples of 4");
+    if (hs % 4 || hs > 256) return fail(ctx, L2D_EINVAL, "init: head_size must be a multiple of 4 and <= 256");
+    if (c->n_heads / c->n_kv_heads > 64) return fail(ctx, L2D_EINVAL, "init: at most 64 query heads per kv head");
+    if (c->dtype == L2D_F32 && (c->dim > 16384 || c->hidden_dim > 16384))
+        return fail(ctx, L2D_EINVAL, "init: fp32 matvec inputs are limited to 16384 values (64 KiB of LDS)");
+    if (c->dim > 65536 || c->hidden_dim > 65536)
+        return fail(ctx, L2D_EINVAL, "init: matvec inputs are limited to 65536 values");
+    if (attention_lds_bytes(c->n_heads / c->n_kv_heads, hs, 64) > 64 * 1024)
+        return fail(ctx, L2D_EINVAL, "init: attention working set exceeds 64 KiB of LDS");
+    return L2D_OK;
+}
+
+}  // namespace l2d
+
+using namespace l2d;
+
+#define HIP_TRY(ctx, call)                                                                  \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return fail((ctx), L2D_EHIP, std::string(#call ": ") + hipGetErrorString(e_));  \
+    } while (0)
+
+namespace {
+
+int dev_alloc(l2d_ctx* ctx, void** p, size_t bytes)
+{
+    *p = nullptr;
+    if (bytes == 0) bytes = 16;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        char buf[128];
+        snprintf(buf, sizeof(buf), "init: hipMalloc of %zu bytes failed", bytes);
+        return fail(ctx, e == hipErrorOutOfMemory ? L2D_ENOMEM : L2D_EHIP, buf);
+    }
+    ctx->allocs.push_back(*p);
+    return L2D_OK;
+}
+
+#define ALLOC(ptr, bytes)                                               \
+    do {                                                                \
+        void* p_ = nullptr;                                             \
+        int rc_ = dev_alloc(ctx, &p_, (bytes));                         \
+        if (rc_ != L2D_OK) return rc_;                                  \
+        (ptr) = (decltype(ptr))p_;                                      \
+    } while (0)
+
+// host -> device copy of `rows` rows of `width` bytes each, placed at a
+// device pitch of `dpitch` bytes: one contiguous upload into a staging
+// buffer, then a device-side strided copy
+int upload_rows(l2d_ctx* ctx, void* dst, size_t dpitch, const void* src, size_t width, size_t rows,
+                void* staging)
+{
+    HIP_TRY(ctx, hipMemcpyAsync(staging, src, width * rows, hipMemcpyHostToDevice, ctx->stream));
+    HIP_TRY(ctx, hipMemcpy2DAsync(dst, dpitch, staging, width, width, rows,
+                                  hipMemcpyDeviceToDevice, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return L2D_OK;
+}
+
+int upload(l2d_ctx* ctx, void* dst, const void* src, size_t bytes)
+{
+    HIP_TRY(ctx, hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, ctx->stream));
+    return L2D_OK;
+}
+
+void release(l2d_ctx* ctx)
+{
+    if (ctx->exec) hipGraphExecDestroy(ctx->exec);
+    if (ctx->graph) hipGraphDestroy(ctx->graph);
+    if (ctx->stream) hipStreamSynchronize(ctx->stream);
+    for (void* p : ctx->allocs) hipFree(p);
+    ctx->allocs.clear();
+    if (ctx->own_stream && ctx->stream) hipStreamDestroy(ctx->stream);
+    ctx->stream = nullptr;
+}
+
+size_t elt(int dt) { return dt == DT_F32 ? 4 : 1; }
+
+// HIP events around each launch of the kernel-by-kernel step, by kernel class
+struct KernelTimer {
+    std::vector<hipEvent_t> ev;
+    std::vector<int> cls;
+    size_t used = 0;
+    hipStream_t s = nullptr;
+
+    hipError_t mark(int c)
+    {
+        if (used + 2 > ev.size()) {
+            for (int i = 0; i < 2; i++) {
+                hipEvent_t e;
+                hipError_t r = hipEventCreate(&e);
+                if (r != hipSuccess) return r;
+                ev.push_back(e);
+            }
+            cls.resize(ev.size() / 2);
+        }
+        cls[used / 2] = c;
+        return hipEventRecord(ev[used], s);
+    }
+    hipError_t done() { hipError_t r = hipEventRecord(ev[used + 1], s); used += 2; return r; }
+    ~KernelTimer()
+    {
+        for (hipEvent_t e : ev) hipEventDestroy(e);
+    }
+};
+
+enum { KC_QKV = 0, KC_ATTN, KC_WO, KC_W13, KC_W2, KC_CLS, KC_BEGIN, KC_COUNT };
+
+// All kernels of one decode step after the step-start kernel.
+int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
+{
+    const int64_t d = ctx->d, h = ctx->h, kvd = ctx->kvd;
+    const int64_t nqkv = d + 2 * kvd;
+    const size_t es = elt(ctx->dt);
+    const int64_t gs = ctx->gs;
+    hipStream_t s = ctx->stream;
+    auto scales = [&](float* base, int64_t off_elems) -> const float* {
+        return ctx->dt == DT_Q8 ? base + off_elems / gs : nullptr;
+    };
+    for (int64_t l = 0; l < ctx->L; l++) {
+        const bool tr = tracing && l == ctx->trace_layer;
+        GemvParams p;
+        memset(&p, 0, sizeof(p));
+        p.gs = (int32_t)gs;
+        p.eps = ctx->cfg.norm_eps;
+        p.step = ctx->step;
+
+        // RMSNorm -> q/k/v matvec -> RoPE -> KV-cache slot pos
+        p.W = (const uint8_t*)ctx->wqkv + (size_t)(l * nqkv * d) * es;
+        p.Ws = scales(ctx->wqkv_s, l * nqkv * d);
+        p.M = nqkv;
+        p.K = d;
+        p.x = ctx->x;
+        p.gain = ctx->rms_att + l * d;
+        p.out = ctx->q;
+        p.kcache = ctx->kc + l * ctx->S * kvd;
+        p.vcache = ctx->vc + l * ctx->S * kvd;
+        p.d = (int32_t)d;
+        p.kvd = (int32_t)kvd;
+        p.hs = (int32_t)ctx->hs;
+        p.freqs = ctx->freqs;
+        p.trace_q = tr ? ctx->trace_q[0] : nullptr;
+        p.trace_s = tr ? ctx->trace_s[0] : nullptr;
+        if (kt) HIP_TRY(ctx, kt->mark(KC_QKV));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_QKV, p, ctx->max_blocks, s));
+        if (kt) HIP_TRY(ctx, kt->done());
+
+        // attention over positions 0..pos
+        AttnParams a;
+        a.q = ctx->q;
+        a.kc = ctx->kc + l * ctx->S * kvd;
+        a.vc = ctx->vc + l * ctx->S * kvd;
+        a.o = ctx->o;
+        a.part_o = ctx->part_o;
+        a.part_ml = ctx->part_ml;
+        a.counters = ctx->counters;
+        a.step = ctx->step;
+        a.S = (int32_t)ctx->S;
+        a.nkv = (int32_t)ctx->nkv;
+        a.hs = (int32_t)ctx->hs;
+        a.kvd = (int32_t)kvd;
+        a.G = (int32_t)ctx->G;
+        a.nsplit = ctx->nsplit;
+        a.chunk = ctx->chunk;
+        if (kt) HIP_TRY(ctx, kt->mark(KC_ATTN));
+        HIP_TRY(ctx, launch_attention(a, s));
+        if (kt) HIP_TRY(ctx, kt->done());
+
+        // output projection + residual
+        p.W = (const uint8_t*)ctx->wo + (size_t)(l * d * d) * es;
+        p.Ws = scales(ctx->wo_s, l * d * d);
+        p.M = d;
+        p.K = d;
+        p.x = ctx->o;
+        p.gain = nullptr;
+        p.out = ctx->x;
+        p.trace_q = tr ? ctx->trace_q[1] : nullptr;
+        p.trace_s = tr ? ctx->trace_s[1] : nullptr;
+        if (kt) HIP_TRY(ctx, kt->mark(KC_WO));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s));
+        if (kt) HIP_TRY(ctx, kt->done());
+
+        // RMSNorm -> w1/w3 matvec -> SwiGLU
+        p.W = (const uint8_t*)ctx->w13 + (size_t)(l * 2 * h * d) * es;
+        p.Ws = scales(ctx->w13_s, l * 2 * h * d);
+        p.M = 2 * h;
+        p.K = d;
+        p.x = ctx->x;
+        p.gain = ctx->rms_ffn + l * d;
+        p.out = ctx->hb;
+        p.trace_q = tr ? ctx->trace_q[2] : nullptr;
+        p.trace_s = tr ? ctx->trace_s[2] : nullptr;
+        if (kt) HIP_TRY(ctx, kt->mark(KC_W13));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s));
+        if (kt) HIP_TRY(ctx, kt->done());
+
+        // w2 matvec + residual
+        p.W = (const uint8_t*)ctx->w2 + (size_t)(l * d * h) * es;
+        p.Ws = scales(ctx->w2_s, l * d * h);
+        p.M = d;
+        p.K = h;
+        p.x = ctx->hb;
+        p.gain = nullptr;
+        p.out = ctx->x;
+        p.trace_q = tr ? ctx->trace_q[3] : nullptr;
+        p.trace_s = tr ? ctx->trace_s[3] : nullptr;
+        if (kt) HIP_TRY(ctx, kt->mark(KC_W2));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s));
+        if (kt) HIP_TRY(ctx, kt->done());
+    }
+    // final RMSNorm -> classifier -> argmax
+    GemvParams p;
+    memset(&p, 0, sizeof(p));
+    p.gs = (int32_t)gs;
+    p.eps = ctx->cfg.norm_eps;
+    p.step = ctx->step;
+    p.W = ctx->wcls;
+    p.Ws = ctx->dt == DT_Q8 ? ctx->wcls_s : nullptr;
+    p.M = ctx->V;
+    p.K = d;
+    p.x = ctx->x;
+    p.gain = ctx->rms_final;
+    p.out = ctx->logits;
+    p.argmax = ctx->argmax;
+    if (kt) HIP_TRY(ctx, kt->mark(KC_CLS));
+    HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_LOGITS, p, ctx->max_blocks, s));
+    if (kt) HIP_TRY(ctx, kt->done());
+    return L2D_OK;
+}
+
+int capture(l2d_ctx* ctx)
+{
+    HIP_TRY(ctx, hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
+    int rc = enqueue_layers(ctx, false);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(ctx->stream, &g);
+    if (rc != L2D_OK) {
+        if (g) hipGraphDestroy(g);
+        return rc;
+    }
+    if (e != hipSuccess) return fail(ctx, L2D_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    ctx->graph = g;
+    HIP_TRY(ctx, hipGraphInstantiate(&ctx->exec, g, nullptr, nullptr, 0));
+    return L2D_OK;
+}
+
+int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* stream)
+{
+    int rc = validate_config(cfg);
+    if (rc != L2D_OK) return fail(ctx, rc, g_err);
+    rc = check_supported(ctx, cfg);
+    if (rc != L2D_OK) return rc;
+    ctx->cfg = *cfg;
+    ctx->dt = cfg->dtype == L2D_F32 ? DT_F32 : DT_Q8;
+    ctx->d = cfg->dim;
+    ctx->h = cfg->hidden_dim;
+    ctx->L = cfg->n_layers;
+    ctx->V = cfg->vocab_size < 0 ? -(int64_t)cfg->vocab_size : cfg->vocab_size;
+    ctx->S = cfg->seq_len;
+    ctx->nh = cfg->n_heads;
+    ctx->nkv = cfg->n_kv_heads;
+    ctx->hs = ctx->d / ctx->nh;
+    ctx->kvd = ctx->nkv * ctx->hs;
+    ctx->G = ctx->nh / ctx->nkv;
+    ctx->gs = ctx->dt == DT_Q8 ? cfg->group_size : 1;
+    const bool q8 = ctx->dt == DT_Q8;
+    if (!w || !w->emb || !w->rms_att || !w->wq || !w->wk || !w->wv || !w->wo || !w->rms_ffn ||
+        !w->w1 || !w->w2 || !w->w3 || !w->rms_final || !w->wcls)
+        return fail(ctx, L2D_EINVAL, "init: a weight pointer is NULL");
+    if (q8 && (!w->emb_s || !w->wq_s || !w->wk_s || !w->wv_s || !w->wo_s || !w->w1_s ||
+               !w->w2_s || !w->w3_s || !w->wcls_s))
+        return fail(ctx, L2D_EINVAL, "init: a Q8_0 scale pointer is NULL");
+
+    HIP_TRY(ctx, hipGetDevice(&ctx->device));
+    int cus = 0;
+    HIP_TRY(ctx, hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ctx->device));
+    int per_cu = 2;
+    if (const char* e = getenv("L2D_GEMV_WG_PER_CU")) per_cu = atoi(e) > 0 ? atoi(e) : per_cu;
+    ctx->max_blocks = cus * per_cu;
+    if (stream) {
+        ctx->stream = (hipStream_t)stream;
+    } else {
+        HIP_TRY(ctx, hipStreamCreateWithFlags(&ctx->stream, hipStreamNonBlocking));
+        ctx->own_stream = true;
+    }
+
+    const int64_t d = ctx->d, h = ctx->h, L = ctx->L, V = ctx->V, kvd = ctx->kvd;
+    const int64_t gs = ctx->gs;
+    const size_t es = elt(ctx->dt);
+    const int64_t nqkv = d + 2 * kvd;
+    auto sbytes = [&](int64_t n) -> size_t { return q8 ? (size_t)(n / gs) * 4 : 0; };
+
+    ALLOC(ctx->emb, (size_t)(V * d) * es);
+    if (q8) ALLOC(ctx->emb_s, sbytes(V * d));
+    ALLOC(ctx->wqkv, (size_t)(L * nqkv * d) * es);
+    if (q8) ALLOC(ctx->wqkv_s, sbytes(L * nqkv * d));
+    ALLOC(ctx->wo, (size_t)(L * d * d) * es);
+    if (q8) ALLOC(ctx->wo_s, sbytes(L * d * d));
+    ALLOC(ctx->w13, (size_t)(L * 2 * h * d) * es);
+    if (q8) ALLOC(ctx->w13_s, sbytes(L * 2 * h * d));
+    ALLOC(ctx->w2, (size_t)(L * d * h) * es);
+    if (q8) ALLOC(ctx->w2_s, sbytes(L * d * h));
+    const bool shared = cfg->vocab_size > 0;
+    if (!shared) {
+        ALLOC(ctx->wcls, (size_t)(V * d) * es);
+        if (q8) ALLOC(ctx->wcls_s, sbytes(V * d));
+    }
+    ALLOC(ctx->rms_att, (size_t)(L * d) * 4);
+    ALLOC(ctx->rms_ffn, (size_t)(L * d) * 4);
+    ALLOC(ctx->rms_final, (size_t)d * 4);
+    ALLOC(ctx->freqs, (size_t)(ctx->hs / 2) * 4);
+    const size_t kvbytes = (size_t)(L * ctx->S * kvd) * 4;
+    ALLOC(ctx->kc, kvbytes);
+    ALLOC(ctx->vc, kvbytes);
+    ALLOC(ctx->x, (size_t)d * 4);
+    ALLOC(ctx->q, (size_t)d * 4);
+    ALLOC(ctx->o, (size_t)d * 4);
+    ALLOC(ctx->hb, (size_t)h * 4);
+    ALLOC(ctx->logits, (size_t)V * 4);
+    ALLOC(ctx->step, 64);
+    ALLOC(ctx->argmax, 64);
+    ctx->chunk = 64;
+    ctx->nsplit = (int)((ctx->S + ctx->chunk - 1) / ctx->chunk);
+    const size_t nparts = (size_t)ctx->nkv * ctx->nsplit * ctx->G;
+    ALLOC(ctx->part_o, nparts * ctx->hs * 8);
+    ALLOC(ctx->part_ml, nparts * 2 * 8);
+    ALLOC(ctx->counters, (size_t)ctx->nkv * 4);
+    for (int i = 0; i < 4; i++) {
+        const int64_t n = i == 3 ? h : d;
+        ALLOC(ctx->trace_q[i], (size_t)n);
+        ALLOC(ctx->trace_s[i], (size_t)(n / gs + 1) * 4);
+    }
+
+    // staging buffer for the strided (re-laid-out) uploads: the largest of
+    // the arrays that go through it
+    size_t stage = 0;
+    for (int64_t n : {L * d * d, L * kvd * d, L * h * d}) {
+        if ((size_t)n * es > stage) stage = (size_t)n * es;
+        if (sbytes(n) > stage) stage = sbytes(n);
+    }
+    void* staging = nullptr;
+    {
+        hipError_t e = hipMalloc(&staging, stage);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ctx, L2D_ENOMEM, "init: no device memory for the upload staging buffer");
+        }
+    }
+    auto up_all = [&]() -> int {
+        int r;
+        // embedding (and its scales)
+        if ((r = upload(ctx, ctx->emb, w->emb, (size_t)(V * d) * es))) return r;
+        if (q8 && (r = upload(ctx, ctx->emb_s, w->emb_s, sbytes(V * d)))) return r;
+        // q, k, v rows of each layer side by side: [L][d + 2kvd][d]
+        const size_t lpitch = (size_t)(nqkv * d) * es;
+        if ((r = upload_rows(ctx, ctx->wqkv, lpitch, w->wq, (size_t)(d * d) * es, L, staging))) return r;
+        if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)(d * d) * es, lpitch, w->wk,
+                             (size_t)(kvd * d) * es, L, staging))) return r;
+        if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)((d + kvd) * d) * es, lpitch, w->wv,
+                             (size_t)(kvd * d) * es, L, staging))) return r;
+        if (q8) {
+            const size_t sp = sbytes(nqkv * d);
+            if ((r = upload_rows(ctx, ctx->wqkv_s, sp, w->wq_s, sbytes(d * d), L, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv_s + sbytes(d * d), sp, w->wk_s,
+                                 sbytes(kvd * d), L, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv_s + sbytes((d + kvd) * d), sp, w->wv_s,
+                                 sbytes(kvd * d), L, staging))) return r;
+        }
+        if ((r = upload(ctx, ctx->wo, w->wo, (size_t)(L * d * d) * es))) return r;
+        if (q8 && (r = upload(ctx, ctx->wo_s, w->wo_s, sbytes(L * d * d)))) return r;
+        // w1 / w3 rows interleaved: [L][h][2][d]
+        const size_t rb = (size_t)d * es;
+        if ((r = upload_rows(ctx, ctx->w13, 2 * rb, w->w1, rb, L * h, staging))) return r;
+        if ((r = upload_rows(ctx, (uint8_t*)ctx->w13 + rb, 2 * rb, w->w3, rb, L * h, staging))) return r;
+        if (q8) {
+            const size_t sb = sbytes(d);
+            if ((r = upload_rows(ctx, ctx->w13_s, 2 * sb, w->w1_s, sb, L * h, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->w13_s + sb, 2 * sb, w->w3_s, sb, L * h, staging))) return r;
+        }
+        if ((r = upload(ctx, ctx->w2, w->w2, (size_t)(L * d * h) * es))) return r;
+        if (q8 && (r = upload(ctx, ctx->w2_s, w->w2_s, sbytes(L * d * h)))) return r;
+        if (!shared) {
+            if ((r = upload(ctx, ctx->wcls, w->wcls, (size_t)(V * d) * es))) return r;
+            if (q8 && (r = upload(ctx, ctx->wcls_s, w->wcls_s, sbytes(V * d)))) return r;
+        }
+        if ((r = upload(ctx, ctx->rms_att, w->rms_att, (size_t)(L * d) * 4))) return r;
+        if ((r = upload(ctx, ctx->rms_ffn, w->rms_ffn, (size_t)(L * d) * 4))) return r;
+        if ((r = upload(ctx, ctx->rms_final, w->rms_final, (size_t)d * 4))) return r;
+        return L2D_OK;
+    };
+    rc = up_all();
+    hipStreamSynchronize(ctx->stream);
+    hipFree(staging);
+    if (rc != L2D_OK) return rc;
+    if (shared) {
+        ctx->wcls = ctx->emb;
+        ctx->wcls_s = ctx->emb_s;
+    }
+
+    // RoPE frequencies theta^(-2j/hs), computed in fp64 and rounded once
+    {
+        std::vector<float> f((size_t)(ctx->hs / 2));
+        for (int64_t j = 0; j < ctx->hs / 2; j++)
+            f[(size_t)j] = (float)pow(cfg->rope_theta, -(double)(2 * j) / (double)ctx->hs);
+        HIP_TRY(ctx, hipMemcpyAsync(ctx->freqs, f.data(), f.size() * 4, hipMemcpyHostToDevice, ctx->stream));
+        HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    }
+    HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->counters, 0, (size_t)ctx->nkv * 4, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, 64, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return capture(ctx);
+}
+
+hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
+{
+    BeginParams b;
+    b.emb = ctx->emb;
+    b.emb_s = ctx->emb_s;
+    b.dtype = ctx->dt;
+    b.gs = ctx->gs;
+    b.d = (int32_t)ctx->d;
+    b.vocab = (int32_t)ctx->V;
+    b.x = ctx->x;
+    b.step = ctx->step;
+    b.argmax = ctx->argmax;
+    b.token = token;
+    b.pos = pos;
+    b.greedy = greedy ? 1 : 0;
+    return launch_begin(b, ctx->stream);
+}
+
+const float* forward_impl(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
+{
+    if (!ctx) {
+        fail(nullptr, L2D_EINVAL, "forward: null context");
+        return nullptr;
+    }
+    if (pos < 0 || pos >= ctx->S) {
+        fail(ctx, L2D_EINVAL, "forward: pos outside [0, seq_len)");
+        return nullptr;
+    }
+    if (!greedy && (token < 0 || token >= ctx->V)) {
+        fail(ctx, L2D_EINVAL, "forward: token outside [0, vocab)");
+        return nullptr;
+    }
+    if (greedy && (pos < 1 || ctx->last_pos != pos - 1)) {
+        fail(ctx, L2D_EINVAL, "forward_greedy: the previous step must be at pos - 1");
+        return nullptr;
+    }
+    hipError_t e = begin(ctx, token, pos, greedy);
+    if (e != hipSuccess) {
+        fail(ctx, L2D_EHIP, std::string("begin_step launch: ") + hipGetErrorString(e));
+        return nullptr;
+    }
+    const bool tracing = ctx->trace_layer >= 0;
+    if (ctx->use_graph && !tracing) {
+        e = hipGraphLaunch(ctx->exec, ctx->stream);
+        if (e != hipSuccess) {
+            fail(ctx, L2D_EHIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
+            return nullptr;
+        }
+    } else if (enqueue_layers(ctx, tracing) != L2D_OK) {
+        return nullptr;
+    }
+    ctx->last_pos = pos;
+    return ctx->logits;
+}
+
+}  // namespace
+
+extern "C" {
+
+int l2d_init(const l2d_config* cfg, const l2d_weights* w, void* stream, l2d_ctx** out)
+{
+    if (!out || !cfg) return fail(nullptr, L2D_EINVAL, "init: null argument");
+    *out = nullptr;
+    l2d_ctx* ctx = new (std::nothrow) l2d_ctx();
+    if (!ctx) return fail(nullptr, L2D_ENOMEM, "init: out of host memory");
+    int rc = init_impl(ctx, cfg, w, stream);
+    if (rc != L2D_OK) {
+        g_err = ctx->err;
+        release(ctx);
+        delete ctx;
+        return rc;
+    }
+    *out = ctx;
+    return L2D_OK;
+}
+
+const float* l2d_forward(l2d_ctx* ctx, int32_t token, int32_t pos)
+{
+    return forward_impl(ctx, token, pos, false);
+}
+
+const float* l2d_forward_greedy(l2d_ctx* ctx, int32_t pos)
+{
+    return forward_impl(ctx, 0, pos, true);
+}
+
+int l2d_sync(l2d_ctx* ctx)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "sync: null context");
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return L2D_OK;
+}
+
+int l2d_last_token(l2d_ctx* ctx, int32_t* token)
+{
+    if (!ctx || !token) return fail(ctx, L2D_EINVAL, "last_token: null argument");
+    if (ctx->last_pos < 0) return fail(ctx, L2D_EINVAL, "last_token: no forward yet");
+    unsigned long long v = 0;
+    HIP_TRY(ctx, hipMemcpyAsync(&v, ctx->argmax + (ctx->last_pos & 1), 8, hipMemcpyDeviceToHost,
+                                ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    *token = (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
+    return L2D_OK;
+}
+
+int l2d_read_logits(l2d_ctx* ctx, float* host_dst)
+{
+    if (!ctx || !host_dst) return fail(ctx, L2D_EINVAL, "read_logits: null argument");
+    HIP_TRY(ctx, hipMemcpyAsync(host_dst, ctx->logits, (size_t)ctx->V * 4, hipMemcpyDeviceToHost,
+                                ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return L2D_OK;
+}
+
+int l2d_quantize_q80(const float* x, int64_t n, int32_t gs, int8_t* q, float* s, void* stream)
+{
+    if (gs <= 0 || n < 0 || n % gs) return fail(nullptr, L2D_EINVAL, "quantize_q80: need gs > 0, n >= 0, n % gs == 0");
+    if (!((gs <= 64 && (gs & (gs - 1)) == 0) || gs % 64 == 0))
+        return fail(nullptr, L2D_EINVAL, "quantize_q80: gs must be a power of two <= 64 or a multiple of 64");
+    if (n == 0) return L2D_OK;
+    if (!x || !q || !s) return fail(nullptr, L2D_EINVAL, "quantize_q80: null pointer");
+    hipError_t e = launch_quantize(x, n, gs, q, s, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("quantize_q80: ") + hipGetErrorString(e));
+    return L2D_OK;
+}
+
+int l2d_reset_kv(l2d_ctx* ctx)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "reset_kv: null context");
+    const size_t kvbytes = (size_t)(ctx->L * ctx->S * ctx->kvd) * 4;
+    HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
+    ctx->last_pos = -1;
+    return L2D_OK;
+}
+
+void l2d_free(l2d_ctx* ctx)
+{
+    if (!ctx) return;
+    release(ctx);
+    delete ctx;
+}
+
+const char* l2d_last_error(const l2d_ctx* ctx)
+{
+    return ctx ? ctx->err.c_str() : g_err.c_str();
+}
+
+int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache)
+{
+    if (!ctx || !key_cache || !value_cache) return fail(ctx, L2D_EINVAL, "kv_cache: null argument");
+    *key_cache = ctx->kc;
+    *value_cache = ctx->vc;
+    return L2D_OK;
+}
+
+int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
+             int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream)
+{
+    if (dtype != L2D_F32 && dtype != L2D_Q8_0) return fail(nullptr, L2D_EINVAL, "gemv: bad dtype");
+    if (rows <= 0 || cols <= 0 || rows % 2 || cols % 4 || !W || !x || !out)
+        return fail(nullptr, L2D_EINVAL, "gemv: need rows even > 0, cols % 4 == 0, non-null pointers");
+    if (dtype == L2D_Q8_0) {
+        if (gs < 16 || gs > 1024 || (gs & (gs - 1)) || cols % gs || !W_s)
+            return fail(nullptr, L2D_EINVAL, "gemv: Q8_0 needs a power-of-two gs in [16,1024] dividing cols");
+        if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
+    } else if (cols > 16384) {
+        return fail(nullptr, L2D_EINVAL, "gemv: fp32 cols > 16384");
+    }
+    GemvParams p;
+    memset(&p, 0, sizeof(p));
+    p.W = W;
+    p.Ws = W_s;
+    p.M = rows;
+    p.K = cols;
+    p.gs = dtype == L2D_Q8_0 ? gs : 1;
+    p.x = x;
+    p.out = out;
+    p.group_dots = dtype == L2D_Q8_0 ? group_dots : nullptr;
+    int dev = 0, cus = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipError_t e = launch_gemv(dtype == L2D_F32 ? DT_F32 : DT_Q8, PRO_PLAIN, EPI_STORE, p,
+                               cus > 0 ? 2 * cus : 512, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("gemv: ") + hipGetErrorString(e));
+    return L2D_OK;
+}
+
+int l2d_trace_layer(l2d_ctx* ctx, int32_t layer)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "trace_layer: null context");
+    if (layer >= ctx->L) return fail(ctx, L2D_EINVAL, "trace_layer: layer out of range");
+    ctx->trace_layer = layer < 0 ? -1 : layer;
+    return L2D_OK;
+}
+
+int l2d_trace_read(l2d_ctx* ctx, int32_t slot, int8_t* host_q, float* host_s)
+{
+    if (!ctx || slot < 0 || slot > 3 || !host_q || !host_s) return fail(ctx, L2D_EINVAL, "trace_read: bad argument");
+    if (ctx->dt != DT_Q8) return fail(ctx, L2D_EINVAL, "trace_read: tracing records Q8_0 codes only");
+    const int64_t n = slot == 3 ? ctx->h : ctx->d;
+    HIP_TRY(ctx, hipMemcpyAsync(host_q, ctx->trace_q[slot], (size_t)n, hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(ctx, hipMemcpyAsync(host_s, ctx->trace_s[slot], (size_t)(n / ctx->gs) * 4,
+                                hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return L2D_OK;
+}
+
+void* l2d_stream(l2d_ctx* ctx) { return ctx ? (void*)ctx->stream : nullptr; }
+
+int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, double* avg_seconds)
+{
+    if (!ctx || !avg_seconds || reps <= 0) return fail(ctx, L2D_EINVAL, "profile_step: bad argument");
+    if (pos < 0 || pos >= ctx->S || token < 0 || token >= ctx->V)
+        return fail(ctx, L2D_EINVAL, "profile_step: token or pos out of range");
+    KernelTimer kt;
+    kt.s = ctx->stream;
+    for (int r = 0; r < reps; r++) {
+        HIP_TRY(ctx, kt.mark(KC_BEGIN));
+        HIP_TRY(ctx, begin(ctx, token, pos, false));
+        HIP_TRY(ctx, kt.done());
+        int rc = enqueue_layers(ctx, false, &kt);
+        if (rc != L2D_OK) return rc;
+    }
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    double sum[KC_COUNT] = {0};
+    int cnt[KC_COUNT] = {0};
+    for (size_t i = 0; i < kt.used / 2; i++) {
+        float ms = 0.f;
+        HIP_TRY(ctx, hipEventElapsedTime(&ms, kt.ev[2 * i], kt.ev[2 * i + 1]));
+        sum[kt.cls[i]] += ms * 1e-3;
+        cnt[kt.cls[i]] += 1;
+    }
+    for (int c = 0; c < KC_COUNT; c++) avg_seconds[c] = cnt[c] ? sum[c] / cnt[c] : 0.0;
+    ctx->last_pos = pos;
+    return L2D_OK;
+}
+
+int l2d_use_graph(l2d_ctx* ctx, int32_t enable)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "use_graph: null context");
+    ctx->use_graph = enable != 0;
+    return L2D_OK;
+}
+
+}  // extern "C"

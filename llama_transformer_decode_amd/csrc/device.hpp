@@ -1,0 +1,120 @@
+// device.hpp - wavefront-level helpers for gfx950 (64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace l2d {
+
+constexpr int kWave = 64;
+
+// native clang vectors: 16-byte global loads (plain and nontemporal)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// fp64 sum over the 64 lanes of a wavefront; every lane gets the total.
+// The xor-butterfly order is fixed, so the result is deterministic.
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_max(double v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmax(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_maxf(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+// sum of an int over aligned groups of `width` lanes (width a power of two <= 64)
+__device__ __forceinline__ int group_sum_i32(int v, int width)
+{
+    for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// dot of 4 int8 pairs packed in two 32-bit words, accumulated into c (v_dot4_i32_i8)
+__device__ __forceinline__ int dot4_i8(int a, int b, int c)
+{
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+__device__ __forceinline__ int dot16_i8(i32x4 a, i32x4 b)
+{
+    int p = dot4_i8(a.x, b.x, 0);
+    p = dot4_i8(a.y, b.y, p);
+    p = dot4_i8(a.z, b.z, p);
+    p = dot4_i8(a.w, b.w, p);
+    return p;
+}
+
+// Order-preserving map of a float onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// argmax candidate packed for a 64-bit atomicMax: high word the float key,
+// low word the complement of the index, so equal values favour the lower index.
+__device__ __forceinline__ unsigned long long argmax_pack(float v, uint32_t idx)
+{
+    return ((unsigned long long)float_key(v) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+
+// Q8_0 quantisation of one group value: the group's scale is wmax / 127
+// (IEEE fp32 division), the code is the fp32 quotient rounded half away from
+// zero; a zero scale gives code 0.
+__device__ __forceinline__ float q80_scale(float wmax) { return wmax / 127.0f; }
+
+__device__ __forceinline__ int q80_code(float x, float scale)
+{
+    if (scale == 0.0f) return 0;
+    return (int)roundf(x / scale);
+}
+
+}  // namespace l2d
+
+namespace l2d {
+
+// Wave-cooperative Q8_0 quantisation of groups of gs values (gs a power of
+// two in [16, 1024]). A wave handles 64/min(gs,64) groups per iteration;
+// iterations first_iter, first_iter + iter_stride, ... cover all ng groups.
+// val(i) yields the fp32 value of element i. Codes go to q[i], scales to s[g].
+template <class Val>
+__device__ __forceinline__ void q80_groups_wave(Val val, int64_t ng, int gs, int64_t first_iter,
+                                                int64_t iter_stride, int8_t* q, float* s,
+                                                int lane)
+{
+    const int sw = gs < kWave ? gs : kWave;  // lanes per group
+    const int gpw = kWave / sw;               // groups per wave iteration
+    const int epl = gs / sw;                  // values per lane
+    const int sub = lane % sw;
+    for (int64_t it = first_iter; it * gpw < ng; it += iter_stride) {
+        const int64_t g = it * gpw + lane / sw;
+        const bool ok = g < ng;
+        float m = 0.0f;
+        if (ok)
+            for (int k = 0; k < epl; k++) m = fmaxf(m, fabsf(val(g * gs + sub + k * sw)));
+        for (int w = 1; w < sw; w <<= 1) m = fmaxf(m, __shfl_xor(m, w, kWave));
+        const float sc = q80_scale(m);
+        if (ok) {
+            for (int k = 0; k < epl; k++) {
+                const int64_t i = g * gs + sub + k * sw;
+                q[i] = (int8_t)q80_code(val(i), sc);
+            }
+            if (sub == 0) s[g] = sc;
+        }
+    }
+}
+
+}  // namespace l2d

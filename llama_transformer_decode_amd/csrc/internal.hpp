@@ -1,0 +1,84 @@
+// internal.hpp - kernel parameter blocks and launchers shared by the runtime
+// (ctx.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace l2d {
+
+enum Dt { DT_F32 = 0, DT_Q8 = 1 };
+
+// GEMV input-vector preparation (the "prologue", run by every workgroup into
+// its LDS): PRO_PLAIN takes x as is; PRO_NORM applies RMSNorm with gain.
+enum Pro { PRO_PLAIN = 0, PRO_NORM = 1 };
+
+// What happens to each finished output row (the "epilogue").
+enum Epi {
+    EPI_STORE = 0,   // out[row] = y
+    EPI_RESID = 1,   // out[row] += y (residual stream)
+    EPI_QKV = 2,     // RoPE on q/k pairs, q -> out, k/v -> cache slot pos
+    EPI_SWIGLU = 3,  // rows (2i, 2i+1) = (w1, w3): out[i] = silu(y0) * y1
+    EPI_LOGITS = 4,  // out[row] = y and a packed 64-bit argmax
+};
+
+struct GemvParams {
+    const void* W;     // fp32 [M][K] or int8 codes [M][K]
+    const float* Ws;   // Q8_0 scales [M][K/gs]
+    int64_t M, K;
+    int32_t gs;
+    const float* x;     // input vector [K], fp32
+    const float* gain;  // RMSNorm gain [K] (PRO_NORM)
+    double eps;
+    float* out;
+    // EPI_QKV
+    float* kcache;  // this layer's [seq_len][kv_dim]
+    float* vcache;
+    int32_t d, kvd, hs;
+    const float* freqs;   // [hs/2] RoPE frequencies
+    const int32_t* step;  // device {token, pos}
+    // EPI_LOGITS
+    unsigned long long* argmax;  // two slots, written at [pos & 1]
+    // diagnostics
+    int32_t* group_dots;  // [M][K/gs] exact int32 group dots (Q8_0, test hook)
+    int8_t* trace_q;      // workgroup 0 copies its quantised input here
+    float* trace_s;
+};
+
+hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_blocks,
+                       hipStream_t s);
+
+// dynamic LDS bytes the GEMV needs for an input of K values
+size_t gemv_lds_bytes(int dt, int64_t K, int gs);
+
+struct AttnParams {
+    const float* q;    // [n_heads * hs]
+    const float* kc;   // this layer's [S][kvd]
+    const float* vc;
+    float* o;          // [n_heads * hs]
+    double* part_o;    // [nkv][nsplit][G][hs]
+    double* part_ml;   // [nkv][nsplit][G][2]
+    int32_t* counters; // [nkv], zero between steps
+    const int32_t* step;
+    int32_t S, nkv, hs, kvd, G, nsplit, chunk;
+};
+
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+size_t attention_lds_bytes(int G, int hs, int chunk);
+
+struct BeginParams {
+    const void* emb;
+    const float* emb_s;
+    int32_t dtype, gs, d, vocab;
+    float* x;
+    int32_t* step;
+    unsigned long long* argmax;
+    int32_t token, pos, greedy;
+};
+
+hipError_t launch_begin(const BeginParams& p, hipStream_t s);
+
+hipError_t launch_quantize(const float* x, int64_t n, int32_t gs, int8_t* q, float* s,
+                           hipStream_t st);
+
+}  // namespace l2d

@@ -1,0 +1,77 @@
+// runtime.hpp - the decode context and host-side helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "l2d.h"
+
+namespace l2d {
+
+// record an error message (for ctx, or the calling thread when ctx is null)
+// and return code
+int fail(l2d_ctx* ctx, int code, const std::string& msg);
+
+// check a config against what the kernels support; returns L2D_OK or L2D_EINVAL
+int validate_config(const l2d_config* c);
+
+}  // namespace l2d
+
+struct l2d_ctx {
+    l2d_config cfg;
+    int dt;
+    int64_t d, h, L, V, S, nh, nkv, hs, kvd, G;
+    int gs;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    int device = 0;
+    int max_blocks = 0;  // GEMV workgroup cap (CUs x workgroups per CU)
+
+    // device weights, in the library's layout
+    void* emb = nullptr;      // [V][d]
+    float* emb_s = nullptr;
+    void* wqkv = nullptr;     // [L][d + 2 kvd][d]: q rows, then k rows, then v rows
+    float* wqkv_s = nullptr;
+    void* wo = nullptr;       // [L][d][d]
+    float* wo_s = nullptr;
+    void* w13 = nullptr;      // [L][2h][d]: row 2i = w1 row i, row 2i+1 = w3 row i
+    float* w13_s = nullptr;
+    void* w2 = nullptr;       // [L][d][h]
+    float* w2_s = nullptr;
+    void* wcls = nullptr;     // [V][d], aliases emb when the classifier is shared
+    float* wcls_s = nullptr;
+    float* rms_att = nullptr;
+    float* rms_ffn = nullptr;
+    float* rms_final = nullptr;
+    float* freqs = nullptr;   // [hs/2]
+
+    // state
+    float* kc = nullptr;      // [L][S][kvd]
+    float* vc = nullptr;
+    float* x = nullptr;       // residual stream [d]
+    float* q = nullptr;       // [d]
+    float* o = nullptr;       // attention output [d]
+    float* hb = nullptr;      // [h]
+    float* logits = nullptr;  // [V]
+    int32_t* step = nullptr;  // {token, pos}
+    unsigned long long* argmax = nullptr;  // [2]
+    double* part_o = nullptr;
+    double* part_ml = nullptr;
+    int32_t* counters = nullptr;
+    int nsplit = 0, chunk = 0;
+
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    bool use_graph = true;
+
+    int trace_layer = -1;
+    int8_t* trace_q[4] = {nullptr, nullptr, nullptr, nullptr};
+    float* trace_s[4] = {nullptr, nullptr, nullptr, nullptr};
+
+    int32_t last_pos = -1;
+    std::string err;
+    std::vector<void*> allocs;
+};

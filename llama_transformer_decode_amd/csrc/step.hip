@@ -1,0 +1,71 @@
+// step.hip - the first kernel of a decode step, and the standalone Q8_0
+// quantiser.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace l2d {
+
+// Step start: record (token, pos) for the captured kernels, clear this
+// step's argmax slot, and write the embedding row of token into the residual
+// stream x (the first step of the toy forward pass, mht18 essay section
+// 2.3). Q8_0 rows are dequantised: x_i = code_i * scale of its group (fp32
+// product, exact before the one rounding). In greedy mode the token is the
+// argmax of the previous step, read from the other argmax slot.
+__global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int32_t token = p.token;
+    if (p.greedy) {
+        const unsigned long long prev = p.argmax[(p.pos - 1) & 1];
+        token = (int32_t)(0xFFFFFFFFu - (uint32_t)(prev & 0xFFFFFFFFull));
+        if (token < 0 || token >= p.vocab) token = 0;
+    }
+    if (i < p.d) {
+        const int64_t off = (int64_t)token * p.d + i;
+        if (p.dtype == DT_F32) {
+            p.x[i] = ((const float*)p.emb)[off];
+        } else {
+            const int8_t c = ((const int8_t*)p.emb)[off];
+            p.x[i] = (float)((double)c * (double)p.emb_s[off / p.gs]);
+        }
+    }
+    if (i == 0) {
+        p.step[0] = token;
+        p.step[1] = p.pos;
+        p.argmax[p.pos & 1] = 0ull;
+    }
+}
+
+hipError_t launch_begin(const BeginParams& p, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)((p.d + 255) / 256);
+    hipLaunchKernelGGL(begin_step_kernel, dim3(blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// Standalone quantiser: the same wave-cooperative group code the GEMV
+// prologue uses, over a vector in device memory.
+__global__ __launch_bounds__(256) void quantize_kernel(const float* x, int64_t n, int32_t gs,
+                                                      int8_t* q, float* s)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    auto val = [&](int64_t i) -> float { return x[i]; };
+    q80_groups_wave(val, n / gs, gs, wave, nwaves, q, s, lane);
+}
+
+hipError_t launch_quantize(const float* x, int64_t n, int32_t gs, int8_t* q, float* s,
+                           hipStream_t st)
+{
+    const int64_t ng = n / gs;
+    const int64_t gpw = 64 / (gs < 64 ? gs : 64);
+    int64_t iters = (ng + gpw - 1) / gpw;
+    int64_t blocks = (iters + 3) / 4;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, gs, q, s);
+    return hipGetLastError();
+}
+
+}  // namespace l2d

@@ -59,6 +59,9 @@ def bind(path: str):
         "or_trace_scales": (_vp, [_vp, ctypes.c_int]),
         "or_trace_input": (_vp, [_vp, ctypes.c_int]),
         "or_forward": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int]),
+        "or_matvec_f32": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
+        "or_matvec_q80": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -106,6 +109,30 @@ def group_dots(wq: np.ndarray, xq: np.ndarray, gs: int = 64) -> np.ndarray:
     rc = _load().or_group_dots(_ptr(wq), _ptr(xq), wq.size, gs, _ptr(out))
     if rc != 0:
         raise ValueError("or_group_dots: invalid size/group")
+    return out
+
+
+def matvec_f32(W: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """out = W x for fp32 W [rows][cols] (fp64 dot, stored fp32)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = W.shape
+    out = np.empty(rows, dtype=np.float32)
+    if _load().or_matvec_f32(_ptr(W), _ptr(x), rows, cols, _ptr(out)) != 0:
+        raise ValueError("or_matvec_f32")
+    return out
+
+
+def matvec_q80(Q: np.ndarray, S: np.ndarray, x: np.ndarray, gs: int = 64) -> np.ndarray:
+    """out = W x for Q8_0 W (codes [rows][cols], scales [rows][cols/gs]); x
+    (fp32) is quantised first."""
+    Q = np.ascontiguousarray(Q, dtype=np.int8)
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = Q.shape
+    out = np.empty(rows, dtype=np.float32)
+    if _load().or_matvec_q80(_ptr(Q), _ptr(S), _ptr(x), rows, cols, gs, _ptr(out)) != 0:
+        raise ValueError("or_matvec_q80")
     return out
 
 

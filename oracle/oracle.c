@@ -304,31 +304,20 @@ static void rmsnorm(float* out, const float* x, const float* g, int64_t n)
  * in integers, then scaled by the weight and activation scales and summed
  * in fp64.
  */
-static void matvec(or_model* m, float* out, const float* x, const or_mat* w, int64_t woff,
-                   int64_t rows, int64_t cols, int trace_slot)
+static void matvec_f32_rows(float* out, const float* x, const float* W, int64_t rows, int64_t cols)
 {
-    if (m->dtype == OR_F32) {
-        const float* W = w->f + woff;
-        #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < rows; i++) {
-            const float* wr = W + i * cols;
-            double acc = 0.0;
-            for (int64_t j = 0; j < cols; j++) acc += (double)wr[j] * (double)x[j];
-            out[i] = (float)acc;
-        }
-        return;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; i++) {
+        const float* wr = W + i * cols;
+        double acc = 0.0;
+        for (int64_t j = 0; j < cols; j++) acc += (double)wr[j] * (double)x[j];
+        out[i] = (float)acc;
     }
-    int gs = m->gs;
-    or_quantize(x, cols, gs, m->aq, m->as);
-    if (trace_slot >= 0) {
-        memcpy(m->tq[trace_slot], m->aq, (size_t)cols);
-        memcpy(m->ts[trace_slot], m->as, (size_t)(cols / gs) * 4);
-        memcpy(m->tf[trace_slot], x, (size_t)cols * 4);
-    }
-    const int8_t* Q = w->q + woff;
-    const float* S = w->s + woff / gs;
-    const int8_t* aq = m->aq;
-    const float* as = m->as;
+}
+
+static void matvec_q80_rows(float* out, const int8_t* aq, const float* as, const int8_t* Q,
+                            const float* S, int64_t rows, int64_t cols, int gs)
+{
     int64_t ng = cols / gs;
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; i++) {
@@ -342,6 +331,46 @@ static void matvec(or_model* m, float* out, const float* x, const or_mat* w, int
         }
         out[i] = (float)acc;
     }
+}
+
+static void matvec(or_model* m, float* out, const float* x, const or_mat* w, int64_t woff,
+                   int64_t rows, int64_t cols, int trace_slot)
+{
+    if (m->dtype == OR_F32) {
+        matvec_f32_rows(out, x, w->f + woff, rows, cols);
+        return;
+    }
+    int gs = m->gs;
+    or_quantize(x, cols, gs, m->aq, m->as);
+    if (trace_slot >= 0) {
+        memcpy(m->tq[trace_slot], m->aq, (size_t)cols);
+        memcpy(m->ts[trace_slot], m->as, (size_t)(cols / gs) * 4);
+        memcpy(m->tf[trace_slot], x, (size_t)cols * 4);
+    }
+    matvec_q80_rows(out, m->aq, m->as, w->q + woff, w->s + woff / gs, rows, cols, gs);
+}
+
+/* standalone fp32 matvec out = W x (the same loop the model uses) */
+int or_matvec_f32(const float* W, const float* x, int64_t rows, int64_t cols, float* out)
+{
+    if (rows < 0 || cols < 0) return OR_EINVAL;
+    matvec_f32_rows(out, x, W, rows, cols);
+    return OR_OK;
+}
+
+/* standalone Q8_0 matvec: x is quantised first, as in the model */
+int or_matvec_q80(const int8_t* Q, const float* S, const float* x, int64_t rows, int64_t cols,
+                  int gs, float* out)
+{
+    if (gs <= 0 || cols % gs || rows < 0) return OR_EINVAL;
+    int8_t* aq = (int8_t*)malloc((size_t)cols);
+    float* as = (float*)malloc((size_t)(cols / gs + 1) * 4);
+    if (!aq || !as) { free(aq); free(as); return OR_ENOMEM; }
+    or_quantize(x, cols, gs, aq, as);
+    matvec_q80_rows(out, aq, as, Q, S, rows, cols, gs);
+    free(aq);
+    free(as);
+    return OR_OK;
 }
 
 /* the int32 group dot products of one Q8_0 matvec row: out[g] for g < cols/gs */

@@ -1,0 +1,139 @@
+"""GPU parity of the individual kernels against the oracle, through the C ABI:
+the Q8_0 quantiser (bit-exact codes and scales), the fp32 GEMV (fp64
+accumulation: at most one fp32 ulp from the oracle), and the Q8_0 GEMV
+(exact int32 group dots; outputs at most one ulp away)."""
+import numpy as np
+import pytest
+
+import llama_transformer_decode_amd as l2d
+import oracle
+import synth
+from gpu_util import log, need_gpu, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+
+def _adversarial(n, gs, rng):
+    """Values whose quotient x/scale sits exactly on k + 1/2, zero groups,
+    +-max, tiny and huge magnitudes."""
+    x = rng.standard_normal(n).astype(np.float32)
+    g = x.reshape(-1, gs)
+    ng = g.shape[0]
+    for i in range(0, ng, 7):      # exact ties: wmax 127 -> scale 1, values k + 0.5
+        g[i] = (rng.integers(-127, 127, gs) + 0.5).astype(np.float32)
+        g[i, 0] = 127.0
+    for i in range(1, ng, 11):     # all-zero group
+        g[i] = 0.0
+    for i in range(2, ng, 13):     # +-max only
+        g[i] = 0.0
+        g[i, 3] = -3.0
+    for i in range(3, ng, 17):     # tiny magnitudes
+        g[i] *= np.float32(1e-30)
+    for i in range(4, ng, 19):     # huge magnitudes
+        g[i] *= np.float32(1e30)
+    return g.reshape(-1)
+
+
+@pytest.mark.parametrize("gs", [16, 32, 64, 128, 256])
+def test_quantize_q80_bitexact(gs):
+    torch = need_gpu()
+    rng = np.random.default_rng(gs)
+    for n in (gs, gs * 3, 1_000_000 // gs * gs, 4096):
+        for kind in ("normal", "adversarial"):
+            x = (rng.standard_normal(n).astype(np.float32) if kind == "normal"
+                 else _adversarial(n, gs, rng))
+            q, s = l2d.quantize_q80(torch.from_numpy(x).cuda(), gs)
+            torch.cuda.synchronize()
+            rq, rs = oracle.quantize(x, gs)
+            np.testing.assert_array_equal(s.cpu().numpy(), rs)
+            np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+def test_quantize_q80_errors():
+    need_gpu()
+    with pytest.raises(l2d.L2DError):
+        l2d.lib() and l2d._check(l2d.lib().l2d_quantize_q80(None, 100, 64, None, None, None))
+    with pytest.raises(l2d.L2DError):
+        l2d._check(l2d.lib().l2d_quantize_q80(None, 64, 0, None, None, None))
+    assert l2d.lib().l2d_quantize_q80(None, 0, 64, None, None, None) == 0
+
+
+F32_SHAPES = [(2, 4), (6, 172), (34, 288), (770, 768), (4096, 4096), (12288, 4096),
+              (4096, 11008), (32000, 4096)]
+Q8_SHAPES = [(2, 64), (6, 192), (34, 768), (130, 2048), (4096, 4096), (12288, 4096),
+             (4096, 11008), (32000, 4096), (1280, 8192), (8192, 3584)]
+
+
+def _report(name, g, r):
+    u = ulp_diff(g, r)
+    log(f"  {name}: exact {np.mean(u == 0):.5f}, max ulp {int(u.max())}")
+    return u
+
+
+@pytest.mark.parametrize("rows,cols", F32_SHAPES)
+def test_gemv_f32_vs_oracle(rows, cols):
+    torch = need_gpu()
+    W = synth.normal_f32(rows * 7 + cols, 1, rows * cols, 0.02).reshape(rows, cols)
+    x = synth.normal_f32(rows * 7 + cols, 2, cols, 1.0)
+    out = l2d.gemv(l2d.F32, torch.from_numpy(W).cuda(), None, torch.from_numpy(x).cuda(),
+                   rows, cols)
+    g = out.cpu().numpy()
+    r = oracle.matvec_f32(W, x)
+    u = _report(f"f32 {rows}x{cols}", g, r)
+    assert u.max() <= 1
+    assert np.mean(u == 0) > 0.99
+
+
+@pytest.mark.parametrize("rows,cols", Q8_SHAPES)
+def test_gemv_q80_vs_oracle(rows, cols):
+    torch = need_gpu()
+    gs = 64
+    rng = np.random.default_rng(rows + cols)
+    Q = rng.integers(-127, 128, (rows, cols)).astype(np.int8)
+    S = (rng.uniform(0.5, 1.5, (rows, cols // gs)) * 3e-4).astype(np.float32)
+    x = synth.normal_f32(rows + 3 * cols, 3, cols, 1.0)
+    gd = torch.zeros(rows * (cols // gs), dtype=torch.int32, device="cuda")
+    out = l2d.gemv(l2d.Q8_0, torch.from_numpy(Q).cuda(), torch.from_numpy(S).cuda(),
+                   torch.from_numpy(x).cuda(), rows, cols, gs, group_dots=gd)
+    g = out.cpu().numpy()
+    r = oracle.matvec_q80(Q, S, x, gs)
+    # exact int32 group dots against the oracle's, for the activation codes
+    # the oracle computes (the kernel quantises x itself; codes are bit-exact)
+    xq, _ = oracle.quantize(x, gs)
+    dots = gd.cpu().numpy().reshape(rows, cols // gs)
+    for i in range(0, rows, max(1, rows // 64)):
+        np.testing.assert_array_equal(dots[i], oracle.group_dots(Q[i], xq, gs))
+    u = _report(f"q8 {rows}x{cols}", g, r)
+    assert u.max() <= 1
+    assert np.mean(u == 0) > 0.99
+
+
+def test_gemv_q80_extreme_codes():
+    """All codes +-127 (largest group dots, 64*127^2) and a zero input."""
+    torch = need_gpu()
+    rows, cols, gs = 64, 4096, 64
+    Q = np.where(np.arange(rows * cols).reshape(rows, cols) % 3 == 0, -127, 127).astype(np.int8)
+    S = np.full((rows, cols // gs), 1e-3, np.float32)
+    x = np.full(cols, 2.5, np.float32)
+    gd = torch.zeros(rows * (cols // gs), dtype=torch.int32, device="cuda")
+    out = l2d.gemv(l2d.Q8_0, torch.from_numpy(Q).cuda(), torch.from_numpy(S).cuda(),
+                   torch.from_numpy(x).cuda(), rows, cols, gs, group_dots=gd)
+    xq, _ = oracle.quantize(x, gs)
+    assert (xq == 127).all()
+    dots = gd.cpu().numpy().reshape(rows, cols // gs)
+    for i in range(rows):
+        np.testing.assert_array_equal(dots[i], oracle.group_dots(Q[i], xq, gs))
+    np.testing.assert_array_equal(out.cpu().numpy(), oracle.matvec_q80(Q, S, x, gs))
+    z = l2d.gemv(l2d.Q8_0, torch.from_numpy(Q).cuda(), torch.from_numpy(S).cuda(),
+                 torch.zeros(cols, device="cuda"), rows, cols, gs)
+    assert (z.cpu().numpy() == 0).all()
+
+
+def test_gemv_rejects_bad_shapes():
+    torch = need_gpu()
+    W = torch.zeros(12, device="cuda")
+    x = torch.zeros(4, device="cuda")
+    with pytest.raises(l2d.L2DError):
+        l2d.gemv(l2d.F32, W, None, x, 3, 4)  # odd rows
+    with pytest.raises(l2d.L2DError):
+        l2d.gemv(l2d.Q8_0, W, W, x, 2, 48, 64)  # gs does not divide cols
