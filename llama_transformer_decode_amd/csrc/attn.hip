@@ -6,157 +6,243 @@
 // t * kv_dim in the layer's cache):
 //     s_t = q_h . k_t / sqrt(hs),  a = softmax(s),  o_h = sum_t a_t v_t.
 //
-// Grid (n_kv_heads, nsplit): workgroup (g, c) takes positions
-// [c*chunk, (c+1)*chunk) of kv head g for all G query heads of g, so each K/V
-// row is read from HBM once per step whatever G is. Within a workgroup:
-//   1. scores: LPP lanes per position (16-byte loads of a K row, interleaved
-//      so LPP lanes read LPP*16 contiguous bytes), G fp64 dots, LPP-lane
-//      butterfly; scores kept in LDS as fp64;
-//   2. per head: max, exp, sum over the chunk (fp64, one wave per head);
-//   3. values: thread = (float4 column f, position slot), G fp64 double4
-//      accumulators, slots reduced through LDS in a fixed order;
-//   4. one chunk: write o = acc / l. Several: write (m, l, acc) partials; the
-//      last workgroup of kv head g to finish (device-scope counter) merges
-//      them, o = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c, and resets
-//      the counter for the next step.
-// Workgroups with no positions (c*chunk > pos) exit at once: the grid is
-// sized for seq_len once, and pos is read from device memory, so the same
-// launch serves every position of a captured graph.
+// Grid (n_kv_heads, NS): workgroup (g, c) owns a contiguous range of about
+// (pos+1)/NS positions of kv head g and serves all G query heads of g, so
+// every K/V row is read from HBM once per step whatever G is. The range is
+// walked in sub-chunks of SC positions whose K and V rows are loaded two
+// sub-chunks ahead (double buffer), so a range of up to 2*SC positions costs
+// one HBM round trip. Per sub-chunk:
+//   scores  LPK lanes per position (16-byte loads, interleaved so the LPK
+//           lanes read LPK*16 contiguous bytes), G fp64 dots, DPP lane sums;
+//   softmax per head, online in fp64: running max m and sum l, rescale
+//           factor e^{m_old - m_new} for what was accumulated before;
+//   values  thread = (float4 column f, position slot), G fp64 double4
+//           accumulators.
+// The slots are reduced through LDS in a fixed order. One active range: o is
+// written directly. Several: each publishes (m, l, acc) with agent-scope
+// atomic stores; the last workgroup of kv head g to arrive (device-scope
+// counter) merges them, o = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c,
+// and resets the counter.
+// Workgroups beyond the active ranges exit at once: the grid is sized once,
+// pos is read from device memory, and the same launch serves every position
+// of a captured graph.
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace l2d {
 
 constexpr int kAThreads = 256;
+constexpr int kMaxG = 8;    // query heads per kv head held in registers
+constexpr int kMaxKPT = 4;  // K float4 per lane per sub-chunk
+constexpr int kMaxVPT = 4;  // V float4 per thread per sub-chunk
+constexpr int kMaxSplits = 512;  // NS * G <= this (merge weights in LDS)
 
-static __host__ __device__ inline int attn_lpp(int F)
+struct AttnShape {
+    int F;      // float4 per head row
+    int lpk;    // lanes per position in the score phase
+    int sc;     // positions per sub-chunk
+    int kpt;    // K float4 per lane
+    int slots;  // position slots in the value phase
+    int vpt;    // V float4 per thread
+};
+
+__host__ __device__ inline AttnShape attn_shape(int hs)
 {
-    // lanes per position for the score phase: up to 4, a power of two dividing F
-    return (F % 4 == 0) ? 4 : ((F % 2 == 0) ? 2 : 1);
+    AttnShape a;
+    a.F = hs / 4;
+    a.lpk = (a.F % 8 == 0) ? 8 : (a.F % 4 == 0) ? 4 : (a.F % 2 == 0) ? 2 : 1;
+    a.sc = kAThreads / a.lpk;
+    if (a.sc > 128) a.sc = 128;
+    a.kpt = a.F / a.lpk;
+    a.slots = kAThreads / a.F;
+    a.vpt = (a.sc + a.slots - 1) / a.slots;
+    return a;
 }
 
-static __host__ __device__ inline int attn_slots(int F, int G, int hs)
+int attention_positions_per_subchunk(int hs) { return attn_shape(hs).sc; }
+
+bool attention_supported(int G, int hs)
 {
-    // position slots of the value phase, bounded so the fp64 reduction
-    // buffer (slots * G * hs doubles) stays within 48 KiB
-    int s = kAThreads / F;
-    const int cap = (48 * 1024) / (G * hs * 8);
-    if (s > cap) s = cap;
-    return s < 1 ? 1 : s;
+    const AttnShape a = attn_shape(hs);
+    return (G == 1 || G == 2 || G == 4 || G == 8) && hs % 4 == 0 && a.F <= 64 && a.kpt <= kMaxKPT &&
+           a.vpt <= kMaxVPT && attention_lds_bytes(G, hs, 0) <= 64 * 1024;
 }
 
-size_t attention_lds_bytes(int G, int hs, int chunk)
+size_t attention_lds_bytes(int G, int hs, int)
 {
-    const int F = hs / 4;
-    const size_t q = (size_t)G * hs * 4;
-    const size_t sc = (size_t)G * chunk * 8;
-    const size_t red = (size_t)attn_slots(F, G, hs) * G * hs * 8;
-    return q + sc + red + 64;
+    const AttnShape a = attn_shape(hs);
+    const size_t q = (((size_t)G * hs * 4) + 15) & ~(size_t)15;
+    const size_t sc = (size_t)G * a.sc * 8;
+    const size_t stats = (size_t)3 * kMaxG * 8;
+    const bool wave_red = (64 % a.F) == 0;
+    size_t red = (size_t)(wave_red ? 4 : a.slots) * G * hs * 8;
+    if (red < (size_t)kMaxSplits * 8) red = (size_t)kMaxSplits * 8;  // merge weights [NS][G]
+    return q + sc + stats + red;
 }
 
+__device__ __forceinline__ double lanes_sum_f64(double v, int width)
+{
+    if (width >= 2) {
+        const int lo = dpp_xor1(__double2loint(v)), hi = dpp_xor1(__double2hiint(v));
+        v += __hiloint2double(hi, lo);
+    }
+    if (width >= 4) {
+        const int lo = dpp_xor2(__double2loint(v)), hi = dpp_xor2(__double2hiint(v));
+        v += __hiloint2double(hi, lo);
+    }
+    for (int m = 4; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+struct KVBuf {
+    f32x4 k[kMaxKPT];
+    f32x4 v[kMaxVPT];
+};
+
+__device__ __forceinline__ void load_kv(KVBuf& b, const AttnParams& p, const AttnShape& a, int g,
+                                        int t0, int n)
+{
+    const int tid = threadIdx.x;
+    // K: position tid / lpk, float4 columns sub + lpk*k
+    {
+        const int tl = tid / a.lpk, sub = tid % a.lpk;
+        const bool ok = tl < n;
+        const f32x4* row = (const f32x4*)(p.kc + (size_t)(t0 + (ok ? tl : 0)) * p.kvd + (size_t)g * p.hs);
+#pragma unroll
+        for (int k = 0; k < kMaxKPT; k++)
+            b.k[k] = (ok && k < a.kpt) ? row[sub + a.lpk * k] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // V: column tid % F, positions slot + slots*j
+    {
+        const int f = tid % a.F, slot = tid / a.F;
+#pragma unroll
+        for (int j = 0; j < kMaxVPT; j++) {
+            const int tl = slot + a.slots * j;
+            const bool ok = slot < a.slots && j < a.vpt && tl < n;
+            b.v[j] = ok ? *((const f32x4*)(p.vc + (size_t)(t0 + tl) * p.kvd + (size_t)g * p.hs) + f)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+template <int KG>
 __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int g = blockIdx.x, split = blockIdx.y;
-    const int pos = p.step[1];
-    const int T = pos + 1;
-    const int chunk = p.chunk;
-    const int nact = (T + chunk - 1) / chunk;
+    const int T = p.step[1] + 1;
+    const int NS = p.nsplit;
+    const int per = (T + NS - 1) / NS;
+    const int nact = (T + per - 1) / per;
     if (split >= nact) return;
-    const int t0 = split * chunk;
-    const int n = min(T - t0, chunk);
-    const int G = p.G, hs = p.hs, F = hs / 4, kvd = p.kvd;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = split * per;
+    const int n = min(T - r0, per);
 
-    float* qs = (float*)smem;                                   // [G][hs]
-    double* sc = (double*)(smem + (((size_t)G * hs * 4 + 7) & ~(size_t)7));  // [G][chunk]
-    double* red = sc + (size_t)G * chunk;                       // [slots][G][hs]
+    constexpr int G = KG;
+    const int hs = p.hs;
+    const AttnShape a = attn_shape(hs);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nsub = (n + a.sc - 1) / a.sc;
+
+    float* qs = (float*)smem;
+    double* sc = (double*)(smem + ((((size_t)G * hs * 4) + 15) & ~(size_t)15));
+    double* m_run = sc + (size_t)G * a.sc;
+    double* l_run = m_run + kMaxG;
+    double* alpha = l_run + kMaxG;
+    double* red = alpha + kMaxG;
     __shared__ int last_flag;
 
-    // q of the G query heads of kv head g (contiguous: heads g*G .. g*G+G-1)
+    // issue the first two sub-chunks' K/V loads, then q
+    KVBuf A, B;
+    load_kv(A, p, a, g, r0, min(a.sc, n));
+    if (nsub > 1) load_kv(B, p, a, g, r0 + a.sc, min(a.sc, n - a.sc));
     for (int i = tid; i < G * hs; i += kAThreads) qs[i] = p.q[(size_t)g * G * hs + i];
+    if (tid < G) {
+        m_run[tid] = -INFINITY;
+        l_run[tid] = 0.0;
+    }
     __syncthreads();
 
-    // ---- 1. scores
     const double scale = 1.0 / sqrt((double)hs);
-    {
-        const int lpp = attn_lpp(F);
-        const int ppp = kAThreads / lpp;  // positions per pass
-        const int sub = tid % lpp;
-        const f32x4* q4 = (const f32x4*)qs;
-        for (int base = 0; base < n; base += ppp) {
-            const int tl = base + tid / lpp;
-            const bool ok = tl < n;
-            double s[8];
-            for (int h0 = 0; h0 < G; h0 += 8) {
-                const int hn = min(8, G - h0);
+    const int vf = tid % a.F, vslot = tid / a.F;
+    double ax[KG], ay[KG], az[KG], aw[KG];
 #pragma unroll
-                for (int h = 0; h < 8; h++) s[h] = 0.0;
-                if (ok) {
-                    const f32x4* k4 = (const f32x4*)(p.kc + (size_t)(t0 + tl) * kvd + (size_t)g * hs);
-                    for (int f = sub; f < F; f += lpp) {
-                        const f32x4 kv = k4[f];
+    for (int h = 0; h < KG; h++) ax[h] = ay[h] = az[h] = aw[h] = 0.0;
+
+    auto step = [&](KVBuf& cur, int s) {
+        const int t0 = r0 + s * a.sc;
+        const int m = min(a.sc, n - s * a.sc);
+        // scores
+        {
+            const int tl = tid / a.lpk, sub = tid % a.lpk;
+            const f32x4* q4 = (const f32x4*)qs;
+            double sv[KG];
 #pragma unroll
-                        for (int h = 0; h < 8; h++) {
-                            if (h < hn) {
-                                const f32x4 qv = q4[(size_t)(h0 + h) * F + f];
-                                s[h] += (double)qv.x * (double)kv.x;
-                                s[h] += (double)qv.y * (double)kv.y;
-                                s[h] += (double)qv.z * (double)kv.z;
-                                s[h] += (double)qv.w * (double)kv.w;
-                            }
+            for (int h = 0; h < KG; h++) {
+                double acc = 0.0;
+                if (h < G) {
+#pragma unroll
+                    for (int k = 0; k < kMaxKPT; k++) {
+                        if (k < a.kpt) {
+                            const f32x4 qv = q4[(size_t)h * a.F + sub + a.lpk * k];
+                            const f32x4 kv = cur.k[k];
+                            acc += (double)qv.x * (double)kv.x;
+                            acc += (double)qv.y * (double)kv.y;
+                            acc += (double)qv.z * (double)kv.z;
+                            acc += (double)qv.w * (double)kv.w;
                         }
                     }
                 }
+                sv[h] = lanes_sum_f64(acc, a.lpk);
+            }
+            if (sub == 0 && tl < m)
 #pragma unroll
-                for (int h = 0; h < 8; h++) {
-                    double v = s[h];
-                    for (int m = 1; m < lpp; m <<= 1) v += __shfl_xor(v, m, kWave);
-                    if (ok && sub == 0 && h < hn) sc[(size_t)(h0 + h) * chunk + tl] = v * scale;
-                }
+                for (int h = 0; h < KG; h++)
+                    if (h < G) sc[(size_t)h * a.sc + tl] = sv[h] * scale;
+        }
+        __syncthreads();
+        for (int h = wave; h < G; h += kAThreads / kWave) {
+            double mx = -INFINITY;
+            for (int t = lane; t < m; t += kWave) mx = fmax(mx, sc[(size_t)h * a.sc + t]);
+            mx = wave_max(mx);
+            const double mo = m_run[h];
+            const double mn = fmax(mo, mx);
+            double l = 0.0;
+            for (int t = lane; t < m; t += kWave) {
+                const double e = exp(sc[(size_t)h * a.sc + t] - mn);
+                sc[(size_t)h * a.sc + t] = e;
+                l += e;
+            }
+            l = wave_sum(l);
+            if (lane == 0) {
+                const double al = exp(mo - mn);  // 0 when mo is -inf
+                alpha[h] = al;
+                l_run[h] = l_run[h] * al + l;
+                m_run[h] = mn;
             }
         }
-    }
-    __syncthreads();
-
-    // ---- 2. softmax statistics per head (one wave per head)
-    __shared__ double mh[64], lh[64];  // G <= 64
-    for (int h = wave; h < G; h += kAThreads / kWave) {
-        double m = -INFINITY;
-        for (int t = lane; t < n; t += kWave) m = fmax(m, sc[(size_t)h * chunk + t]);
-        m = wave_max(m);
-        double l = 0.0;
-        for (int t = lane; t < n; t += kWave) {
-            const double e = exp(sc[(size_t)h * chunk + t] - m);
-            sc[(size_t)h * chunk + t] = e;
-            l += e;
-        }
-        l = wave_sum(l);
-        if (lane == 0) {
-            mh[h] = m;
-            lh[h] = l;
-        }
-    }
-    __syncthreads();
-
-    // ---- 3. values: acc_h = sum_t e_t v_t
-    const int slots = attn_slots(F, G, hs);
-    {
-        const int f = tid % F, slot = tid / F;
-        const bool active = slot < slots;
-        for (int h0 = 0; h0 < G; h0 += 8) {
-            const int hn = min(8, G - h0);
-            double ax[8], ay[8], az[8], aw[8];
+        __syncthreads();
+        // values
+        if (vslot < a.slots) {
 #pragma unroll
-            for (int h = 0; h < 8; h++) ax[h] = ay[h] = az[h] = aw[h] = 0.0;
-            if (active) {
-                for (int tl = slot; tl < n; tl += slots) {
-                    const f32x4 vv =
-                        *((const f32x4*)(p.vc + (size_t)(t0 + tl) * kvd + (size_t)g * hs) + f);
+            for (int h = 0; h < KG; h++) {
+                if (h < G) {
+                    const double al = alpha[h];
+                    ax[h] *= al;
+                    ay[h] *= al;
+                    az[h] *= al;
+                    aw[h] *= al;
+                }
+            }
 #pragma unroll
-                    for (int h = 0; h < 8; h++) {
-                        if (h < hn) {
-                            const double e = sc[(size_t)(h0 + h) * chunk + tl];
+            for (int j = 0; j < kMaxVPT; j++) {
+                const int tl = vslot + a.slots * j;
+                if (j < a.vpt && tl < m) {
+                    const f32x4 vv = cur.v[j];
+#pragma unroll
+                    for (int h = 0; h < KG; h++) {
+                        if (h < G) {
+                            const double e = sc[(size_t)h * a.sc + tl];
                             ax[h] += e * (double)vv.x;
                             ay[h] += e * (double)vv.y;
                             az[h] += e * (double)vv.z;
@@ -164,72 +250,141 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
                         }
                     }
                 }
-                for (int h = 0; h < hn; h++) {
-                    double* rr = red + ((size_t)slot * G + h0 + h) * hs + f * 4;
-                    rr[0] = ax[h];
-                    rr[1] = ay[h];
-                    rr[2] = az[h];
-                    rr[3] = aw[h];
-                }
             }
+        }
+        __syncthreads();
+        // refill the buffer just consumed with the sub-chunk after next
+        if (s + 2 < nsub) load_kv(cur, p, a, g, t0 + 2 * a.sc, min(a.sc, n - (s + 2) * a.sc));
+    };
+    for (int s = 0; s < nsub; s += 2) {
+        step(A, s);
+        if (s + 1 < nsub) step(B, s + 1);
+    }
+
+    // reduce the value accumulators over position slots, in a fixed order
+    const bool wave_red = (64 % a.F) == 0;
+    if (wave_red) {
+        // slots within a wave: butterfly over lane bits >= log2(F)
+        for (int msk = a.F; msk < kWave; msk <<= 1) {
+#pragma unroll
+            for (int h = 0; h < KG; h++) {
+                ax[h] += __shfl_xor(ax[h], msk, kWave);
+                ay[h] += __shfl_xor(ay[h], msk, kWave);
+                az[h] += __shfl_xor(az[h], msk, kWave);
+                aw[h] += __shfl_xor(aw[h], msk, kWave);
+            }
+        }
+        if (lane < a.F) {
+            for (int h = 0; h < G; h++) {
+                double* rr = red + ((size_t)wave * G + h) * hs + vf * 4;
+                rr[0] = ax[h];
+                rr[1] = ay[h];
+                rr[2] = az[h];
+                rr[3] = aw[h];
+            }
+        }
+    } else if (vslot < a.slots) {
+        for (int h = 0; h < G; h++) {
+            double* rr = red + ((size_t)vslot * G + h) * hs + vf * 4;
+            rr[0] = ax[h];
+            rr[1] = ay[h];
+            rr[2] = az[h];
+            rr[3] = aw[h];
         }
     }
     __syncthreads();
+    const int nred = wave_red ? 4 : a.slots;
 
-    // reduce slots in index order; e = h*hs + i
     if (nact == 1) {
         for (int e = tid; e < G * hs; e += kAThreads) {
-            double a = 0.0;
-            for (int sl = 0; sl < slots; sl++) a += red[(size_t)sl * G * hs + e];
-            const int h = e / hs;
-            p.o[(size_t)g * G * hs + e] = (float)(a / lh[h]);
+            double acc = 0.0;
+            for (int sl = 0; sl < nred; sl++) acc += red[(size_t)sl * G * hs + e];
+            p.o[(size_t)g * G * hs + e] = (float)(acc / l_run[e / hs]);
         }
         return;
     }
-    const size_t pbase = ((size_t)g * p.nsplit + split) * G;
+    // Several ranges: publish (acc, m, l) with agent-scope atomic stores
+    // (they reach the device coherence point, so no L2 write-back is needed),
+    // wait until every lane's stores are acknowledged, then count arrivals.
+    const size_t pbase = ((size_t)g * NS + split) * G;
     for (int e = tid; e < G * hs; e += kAThreads) {
-        double a = 0.0;
-        for (int sl = 0; sl < slots; sl++) a += red[(size_t)sl * G * hs + e];
-        p.part_o[pbase * hs + e] = a;
+        double acc = 0.0;
+        for (int sl = 0; sl < nred; sl++) acc += red[(size_t)sl * G * hs + e];
+        __hip_atomic_store(p.part_o + pbase * hs + e, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid < G) {
-        p.part_ml[(pbase + tid) * 2 + 0] = mh[tid];
-        p.part_ml[(pbase + tid) * 2 + 1] = lh[tid];
+        __hip_atomic_store(p.part_ml + (pbase + tid) * 2 + 0, m_run[tid], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.part_ml + (pbase + tid) * 2 + 1, l_run[tid], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const int prev = atomicAdd(p.counters + g, 1);
+        const int prev = __hip_atomic_fetch_add(p.counters + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (prev == nact - 1);
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
 
-    // ---- 4. merge the nact partials of kv head g
+    // Merge the nact ranges of kv head g: per head, M = max m_c, weights
+    // w_c = e^{m_c - M} and L = sum w_c l_c (one wave per head), then every
+    // output element sums w_c acc_c with its loads issued together.
+    double* wts = red;  // [nact][G], the slot buffer is free now
+    double* Linv = sc;  // [G]
+    for (int h = wave; h < G; h += kAThreads / kWave) {
+        double mx = -INFINITY;
+        for (int c = lane; c < nact; c += kWave) {
+            const size_t b = ((size_t)g * NS + c) * G + h;
+            mx = fmax(mx, __hip_atomic_load(p.part_ml + b * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        mx = wave_max(mx);
+        double L = 0.0;
+        for (int c = lane; c < nact; c += kWave) {
+            const size_t b = ((size_t)g * NS + c) * G + h;
+            const double mc = __hip_atomic_load(p.part_ml + b * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const double lc = __hip_atomic_load(p.part_ml + b * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const double w = exp(mc - mx);
+            wts[(size_t)c * G + h] = w;
+            L += w * lc;
+        }
+        L = wave_sum(L);
+        if (lane == 0) Linv[h] = L;
+    }
+    __syncthreads();
     for (int e = tid; e < G * hs; e += kAThreads) {
         const int h = e / hs;
-        double M = -INFINITY;
-        for (int c = 0; c < nact; c++) {
-            const size_t b = ((size_t)g * p.nsplit + c) * G + h;
-            M = fmax(M, __builtin_nontemporal_load(p.part_ml + b * 2));
+        double O = 0.0;
+        int c = 0;
+        for (; c + 8 <= nact; c += 8) {
+            double v[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                v[k] = __hip_atomic_load(p.part_o + (((size_t)g * NS + c + k) * G) * hs + e, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < 8; k++) O += wts[(size_t)(c + k) * G + h] * v[k];
         }
-        double O = 0.0, L = 0.0;
-        for (int c = 0; c < nact; c++) {
-            const size_t b = ((size_t)g * p.nsplit + c) * G;
-            const double w = exp(__builtin_nontemporal_load(p.part_ml + (b + h) * 2) - M);
-            L += w * __builtin_nontemporal_load(p.part_ml + (b + h) * 2 + 1);
-            O += w * __builtin_nontemporal_load(p.part_o + b * hs + e);
-        }
-        p.o[(size_t)g * G * hs + e] = (float)(O / L);
+        for (; c < nact; c++)
+            O += wts[(size_t)c * G + h] *
+                 __hip_atomic_load(p.part_o + (((size_t)g * NS + c) * G) * hs + e, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        p.o[(size_t)g * G * hs + e] = (float)(O / Linv[h]);
     }
-    if (tid == 0) p.counters[g] = 0;
+    if (tid == 0) __hip_atomic_store(p.counters + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s)
 {
-    const size_t lds = attention_lds_bytes(p.G, p.hs, p.chunk);
-    hipLaunchKernelGGL(attention_kernel, dim3(p.nkv, p.nsplit), dim3(kAThreads), lds, s, p);
+    const size_t lds = attention_lds_bytes(p.G, p.hs, 0);
+    const dim3 grid(p.nkv, p.nsplit);
+    switch (p.G) {
+    case 1: hipLaunchKernelGGL(attention_kernel<1>, grid, dim3(kAThreads), lds, s, p); break;
+    case 2: hipLaunchKernelGGL(attention_kernel<2>, grid, dim3(kAThreads), lds, s, p); break;
+    case 4: hipLaunchKernelGGL(attention_kernel<4>, grid, dim3(kAThreads), lds, s, p); break;
+    case 8: hipLaunchKernelGGL(attention_kernel<8>, grid, dim3(kAThreads), lds, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

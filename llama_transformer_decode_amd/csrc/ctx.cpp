@@ -60,13 +60,12 @@ static int check_supported(l2d_ctx* ctx, const l2d_config* c)
     if (c->dim % 4 || c->hidden_dim % 4)
         return fail(ctx, L2D_EINVAL, "init: dim and hidden_dim must be multiples of 4");
     if (hs % 4 || hs > 256) return fail(ctx, L2D_EINVAL, "init: head_size must be a multiple of 4 and <= 256");
-    if (c->n_heads / c->n_kv_heads > 64) return fail(ctx, L2D_EINVAL, "init: at most 64 query heads per kv head");
     if (c->dtype == L2D_F32 && (c->dim > 16384 || c->hidden_dim > 16384))
         return fail(ctx, L2D_EINVAL, "init: fp32 matvec inputs are limited to 16384 values (64 KiB of LDS)");
     if (c->dim > 65536 || c->hidden_dim > 65536)
         return fail(ctx, L2D_EINVAL, "init: matvec inputs are limited to 65536 values");
-    if (attention_lds_bytes(c->n_heads / c->n_kv_heads, hs, 64) > 64 * 1024)
-        return fail(ctx, L2D_EINVAL, "init: attention working set exceeds 64 KiB of LDS");
+    if (!attention_supported(c->n_heads / c->n_kv_heads, hs))
+        return fail(ctx, L2D_EINVAL, "init: attention supports at most 8 query heads per kv head");
     return L2D_OK;
 }
 
@@ -224,7 +223,6 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         a.kvd = (int32_t)kvd;
         a.G = (int32_t)ctx->G;
         a.nsplit = ctx->nsplit;
-        a.chunk = ctx->chunk;
         if (kt) HIP_TRY(ctx, kt->mark(KC_ATTN));
         HIP_TRY(ctx, launch_attention(a, s));
         if (kt) HIP_TRY(ctx, kt->done());
@@ -382,8 +380,16 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ALLOC(ctx->logits, (size_t)V * 4);
     ALLOC(ctx->step, 64);
     ALLOC(ctx->argmax, 64);
-    ctx->chunk = 64;
-    ctx->nsplit = (int)((ctx->S + ctx->chunk - 1) / ctx->chunk);
+    // attention position splits: about 1024 workgroups over the kv heads
+    // (fewer when G query heads share a kv head: their merge grows with G),
+    // never more than one split per sub-chunk of the full context
+    {
+        const int64_t sc = attention_positions_per_subchunk((int)ctx->hs);
+        int64_t ns = 1024 / ctx->nkv;
+        if (ns > 512 / ctx->G) ns = 512 / ctx->G;
+        if (ns > (ctx->S + sc - 1) / sc) ns = (ctx->S + sc - 1) / sc;
+        ctx->nsplit = (int)(ns < 1 ? 1 : ns);
+    }
     const size_t nparts = (size_t)ctx->nkv * ctx->nsplit * ctx->G;
     ALLOC(ctx->part_o, nparts * ctx->hs * 8);
     ALLOC(ctx->part_ml, nparts * 2 * 8);

@@ -118,3 +118,63 @@ __device__ __forceinline__ void q80_groups_wave(Val val, int64_t ng, int gs, int
 }
 
 }  // namespace l2d
+
+namespace l2d {
+
+// Cross-lane moves with DPP quad permutations (VALU, no LDS traffic).
+// quad_perm [1,0,3,2]: lane ^ 1; quad_perm [2,3,0,1]: lane ^ 2.
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
+
+__device__ __forceinline__ float dpp_xor1f(float v) { return __int_as_float(dpp_xor1(__float_as_int(v))); }
+__device__ __forceinline__ float dpp_xor2f(float v) { return __int_as_float(dpp_xor2(__float_as_int(v))); }
+
+// sum of an int over aligned groups of `width` lanes (power of two <= 64)
+__device__ __forceinline__ int lanes_sum_i32(int v, int width)
+{
+    if (width >= 2) v += dpp_xor1(v);
+    if (width >= 4) v += dpp_xor2(v);
+    for (int m = 4; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// max of a float over aligned groups of `width` lanes (power of two <= 64)
+__device__ __forceinline__ float lanes_max_f32(float v, int width)
+{
+    if (width >= 2) v = fmaxf(v, dpp_xor1f(v));
+    if (width >= 4) v = fmaxf(v, dpp_xor2f(v));
+    for (int m = 4; m < width; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int ilog2(int v) { return 31 - __builtin_clz(v); }
+
+}  // namespace l2d
+
+namespace l2d {
+
+// DPP move of a double (two 32-bit halves); lanes of rows disabled by
+// ROW_MASK receive 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+// fp64 sum over the 64 lanes with DPP only (fixed order); the total lands in
+// lane 63: quad xor 1, quad xor 2, half-row mirror, row mirror, then
+// row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3.
+__device__ __forceinline__ double wave_sum_to_last(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    v += dpp_f64<0x142, 0xA>(v);
+    v += dpp_f64<0x143, 0xC>(v);
+    return v;
+}
+
+}  // namespace l2d

@@ -60,11 +60,13 @@ struct AttnParams {
     double* part_ml;   // [nkv][nsplit][G][2]
     int32_t* counters; // [nkv], zero between steps
     const int32_t* step;
-    int32_t S, nkv, hs, kvd, G, nsplit, chunk;
+    int32_t S, nkv, hs, kvd, G, nsplit;
 };
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
-size_t attention_lds_bytes(int G, int hs, int chunk);
+size_t attention_lds_bytes(int G, int hs, int unused);
+bool attention_supported(int G, int hs);
+int attention_positions_per_subchunk(int hs);
 
 struct BeginParams {
     const void* emb;

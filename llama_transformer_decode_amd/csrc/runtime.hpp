@@ -61,7 +61,7 @@ struct l2d_ctx {
     double* part_o = nullptr;
     double* part_ml = nullptr;
     int32_t* counters = nullptr;
-    int nsplit = 0, chunk = 0;
+    int nsplit = 0;
 
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
