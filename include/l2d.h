@@ -101,8 +101,9 @@ int l2d_blob_parse(const void* blob, uint64_t nbytes, int32_t dtype, int32_t gro
  * and scratch; copy the weights host->device; capture one decode step as a
  * HIP graph. stream: a hipStream_t to run on, or NULL for a stream the
  * context creates and owns. The host weights may be freed after return.
- * Supported: dim and hidden_dim multiples of 4; head_size even and <= 256;
- * Q8_0 group size a power of two in [16, 1024] dividing dim and hidden_dim.
+ * Supported: dim and hidden_dim multiples of 4 (fp32: at most 16000);
+ * head_size a multiple of 4 and <= 256; n_heads / n_kv_heads in {1, 2, 4, 8};
+ * Q8_0 group size a power of two in [16, 256] dividing dim and hidden_dim.
  * Errors: L2D_EINVAL, L2D_ENOMEM (device memory), L2D_EHIP.
  */
 int l2d_init(const l2d_config* cfg, const l2d_weights* w, void* stream, l2d_ctx** out);
@@ -176,7 +177,9 @@ int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache);
  * W_s [rows][cols/gs]; x is fp32 [cols] (quantised inside the kernel for
  * Q8_0, as in the decode step); out is fp32 [rows]. group_dots, when not NULL
  * (Q8_0 only), receives the exact int32 dot of every (row, group):
- * [rows][cols/gs]. rows must be even. Asynchronous on stream.
+ * [rows][cols/gs]. rows must be even; Q8_0 gs a power of two in [16, 256].
+ * Asynchronous on stream (Q8_0 codes are first re-laid-out into a
+ * stream-ordered temporary buffer).
  */
 int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
              int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream);

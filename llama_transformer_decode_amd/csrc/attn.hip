@@ -7,7 +7,7 @@
 //     s_t = q_h . k_t / sqrt(hs),  a = softmax(s),  o_h = sum_t a_t v_t.
 //
 // Grid (n_kv_heads, NS): workgroup (g, c) owns a contiguous range of about
-// (pos+1)/NS positions of kv head g and serves all G query heads of g, so
+// (pos+1)/NS positions (rounded up to whole sub-chunks) of kv head g and serves all G query heads of g, so
 // every K/V row is read from HBM once per step whatever G is. The range is
 // walked in sub-chunks of SC positions whose K and V rows are loaded two
 // sub-chunks ahead (double buffer), so a range of up to 2*SC positions costs
@@ -19,10 +19,9 @@
 //   values  thread = (float4 column f, position slot), G fp64 double4
 //           accumulators.
 // The slots are reduced through LDS in a fixed order. One active range: o is
-// written directly. Several: each publishes (m, l, acc) with agent-scope
-// atomic stores; the last workgroup of kv head g to arrive (device-scope
-// counter) merges them, o = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c,
-// and resets the counter.
+// written directly. Several: each writes (m, l, acc) and a small merge kernel
+// launched right after combines them, o = sum_c e^{m_c - M} acc_c /
+// sum_c e^{m_c - M} l_c (no atomics or device-scope fences needed).
 // Workgroups beyond the active ranges exit at once: the grid is sized once,
 // pos is read from device memory, and the same launch serves every position
 // of a captured graph.
@@ -35,7 +34,6 @@ constexpr int kAThreads = 256;
 constexpr int kMaxG = 8;    // query heads per kv head held in registers
 constexpr int kMaxKPT = 4;  // K float4 per lane per sub-chunk
 constexpr int kMaxVPT = 4;  // V float4 per thread per sub-chunk
-constexpr int kMaxSplits = 512;  // NS * G <= this (merge weights in LDS)
 
 struct AttnShape {
     int F;      // float4 per head row
@@ -61,6 +59,18 @@ __host__ __device__ inline AttnShape attn_shape(int hs)
 
 int attention_positions_per_subchunk(int hs) { return attn_shape(hs).sc; }
 
+// Positions per split for T = pos + 1 cached positions and NS splits: the
+// even share rounded up to whole sub-chunks, so a split is one or more full
+// sub-chunks (the last split may be short). Returns the number of active
+// splits through nact.
+__host__ __device__ inline int attn_split(int T, int NS, int sc, int* nact)
+{
+    int per = (T + NS - 1) / NS;
+    per = ((per + sc - 1) / sc) * sc;
+    *nact = (T + per - 1) / per;
+    return per;
+}
+
 bool attention_supported(int G, int hs)
 {
     const AttnShape a = attn_shape(hs);
@@ -75,8 +85,7 @@ size_t attention_lds_bytes(int G, int hs, int)
     const size_t sc = (size_t)G * a.sc * 8;
     const size_t stats = (size_t)3 * kMaxG * 8;
     const bool wave_red = (64 % a.F) == 0;
-    size_t red = (size_t)(wave_red ? 4 : a.slots) * G * hs * 8;
-    if (red < (size_t)kMaxSplits * 8) red = (size_t)kMaxSplits * 8;  // merge weights [NS][G]
+    const size_t red = (size_t)(wave_red ? 4 : a.slots) * G * hs * 8;
     return q + sc + stats + red;
 }
 
@@ -132,8 +141,8 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     const int g = blockIdx.x, split = blockIdx.y;
     const int T = p.step[1] + 1;
     const int NS = p.nsplit;
-    const int per = (T + NS - 1) / NS;
-    const int nact = (T + per - 1) / per;
+    int nact;
+    const int per = attn_split(T, NS, attn_shape(p.hs).sc, &nact);
     if (split >= nact) return;
     const int r0 = split * per;
     const int n = min(T - r0, per);
@@ -150,7 +159,6 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     double* l_run = m_run + kMaxG;
     double* alpha = l_run + kMaxG;
     double* red = alpha + kMaxG;
-    __shared__ int last_flag;
 
     // issue the first two sub-chunks' K/V loads, then q
     KVBuf A, B;
@@ -303,75 +311,70 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
         }
         return;
     }
-    // Several ranges: publish (acc, m, l) with agent-scope atomic stores
-    // (they reach the device coherence point, so no L2 write-back is needed),
-    // wait until every lane's stores are acknowledged, then count arrivals.
+    // Several ranges: write (acc, m, l); the merge kernel that follows in
+    // the stream combines them (the kernel boundary orders the stores)
     const size_t pbase = ((size_t)g * NS + split) * G;
     for (int e = tid; e < G * hs; e += kAThreads) {
         double acc = 0.0;
         for (int sl = 0; sl < nred; sl++) acc += red[(size_t)sl * G * hs + e];
-        __hip_atomic_store(p.part_o + pbase * hs + e, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        p.part_o[pbase * hs + e] = acc;
     }
     if (tid < G) {
-        __hip_atomic_store(p.part_ml + (pbase + tid) * 2 + 0, m_run[tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.part_ml + (pbase + tid) * 2 + 1, l_run[tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        p.part_ml[(pbase + tid) * 2 + 0] = m_run[tid];
+        p.part_ml[(pbase + tid) * 2 + 1] = l_run[tid];
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(p.counters + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (prev == nact - 1);
-    }
-    __syncthreads();
-    if (!last_flag) return;
+}
 
-    // Merge the nact ranges of kv head g: per head, M = max m_c, weights
-    // w_c = e^{m_c - M} and L = sum w_c l_c (one wave per head), then every
-    // output element sums w_c acc_c with its loads issued together.
-    double* wts = red;  // [nact][G], the slot buffer is free now
-    double* Linv = sc;  // [G]
-    for (int h = wave; h < G; h += kAThreads / kWave) {
-        double mx = -INFINITY;
-        for (int c = lane; c < nact; c += kWave) {
-            const size_t b = ((size_t)g * NS + c) * G + h;
-            mx = fmax(mx, __hip_atomic_load(p.part_ml + b * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-        mx = wave_max(mx);
-        double L = 0.0;
-        for (int c = lane; c < nact; c += kWave) {
-            const size_t b = ((size_t)g * NS + c) * G + h;
-            const double mc = __hip_atomic_load(p.part_ml + b * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const double lc = __hip_atomic_load(p.part_ml + b * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const double w = exp(mc - mx);
-            wts[(size_t)c * G + h] = w;
-            L += w * lc;
-        }
-        L = wave_sum(L);
-        if (lane == 0) Linv[h] = L;
-    }
-    __syncthreads();
-    for (int e = tid; e < G * hs; e += kAThreads) {
-        const int h = e / hs;
-        double O = 0.0;
-        int c = 0;
-        for (; c + 8 <= nact; c += 8) {
-            double v[8];
+// Merge of the split results, o = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c
+// with M = max_c m_c, in fp64. Four adjacent lanes share an output element
+// and take every fourth split; their partial maxima and sums combine by DPP
+// in a fixed order. Does nothing when one split covered all positions (the
+// attention kernel then wrote o itself).
+__global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p)
+{
+    const int T = p.step[1] + 1;
+    int nact;
+    attn_split(T, p.nsplit, attn_shape(p.hs).sc, &nact);
+    if (nact == 1) return;
+    const int G = p.G, hs = p.hs;
+    const int64_t n_out = (int64_t)p.nkv * G * hs;
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2;
+    const int sub = threadIdx.x & 3;
+    const int64_t ec = e < n_out ? e : n_out - 1;  // clamped: all lanes join the DPP sums
+    const int64_t g = ec / (G * hs);
+    const int64_t within = ec % (G * hs);
+    const int64_t h = within / hs;
+    const size_t base = (size_t)g * p.nsplit;
+    // this lane's splits c = sub + 4k (k < 16, NS <= 64), loads issued together
+    constexpr int KMAX = 16;
+    double m[KMAX], l[KMAX], o[KMAX];
 #pragma unroll
-            for (int k = 0; k < 8; k++)
-                v[k] = __hip_atomic_load(p.part_o + (((size_t)g * NS + c + k) * G) * hs + e, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int k = 0; k < 8; k++) O += wts[(size_t)(c + k) * G + h] * v[k];
-        }
-        for (; c < nact; c++)
-            O += wts[(size_t)c * G + h] *
-                 __hip_atomic_load(p.part_o + (((size_t)g * NS + c) * G) * hs + e, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        p.o[(size_t)g * G * hs + e] = (float)(O / Linv[h]);
+    for (int k = 0; k < KMAX; k++) {
+        const int c = min(sub + 4 * k, nact - 1);
+        m[k] = p.part_ml[((base + c) * G + h) * 2];
+        l[k] = p.part_ml[((base + c) * G + h) * 2 + 1];
+        o[k] = p.part_o[((base + c) * G) * hs + within];
     }
-    if (tid == 0) __hip_atomic_store(p.counters + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    double M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KMAX; k++)
+        if (sub + 4 * k < nact) M = fmax(M, m[k]);
+    M = fmax(M, __hiloint2double(dpp_xor1(__double2hiint(M)), dpp_xor1(__double2loint(M))));
+    M = fmax(M, __hiloint2double(dpp_xor2(__double2hiint(M)), dpp_xor2(__double2loint(M))));
+    double O = 0.0, L = 0.0;
+#pragma unroll
+    for (int k = 0; k < KMAX; k++) {
+        if (sub + 4 * k < nact) {
+            const double w = exp(m[k] - M);
+            L += w * l[k];
+            O += w * o[k];
+        }
+    }
+    O += __hiloint2double(dpp_xor1(__double2hiint(O)), dpp_xor1(__double2loint(O)));
+    O += __hiloint2double(dpp_xor2(__double2hiint(O)), dpp_xor2(__double2loint(O)));
+    L += __hiloint2double(dpp_xor1(__double2hiint(L)), dpp_xor1(__double2loint(L)));
+    L += __hiloint2double(dpp_xor2(__double2hiint(L)), dpp_xor2(__double2loint(L)));
+    if (sub == 0 && e < n_out) p.o[e] = (float)(O / L);
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s)
@@ -385,6 +388,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s)
     case 8: hipLaunchKernelGGL(attention_kernel<8>, grid, dim3(kAThreads), lds, s, p); break;
     default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)p.nkv * p.G * p.hs * 4;
+    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

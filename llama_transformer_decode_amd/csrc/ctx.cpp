@@ -45,8 +45,8 @@ int validate_config(const l2d_config* c)
     if (c->dtype != L2D_F32 && c->dtype != L2D_Q8_0) return bad("config: unknown dtype");
     if (c->dtype == L2D_Q8_0) {
         const int gs = c->group_size;
-        if (!pow2(gs) || gs < 16 || gs > 1024)
-            return bad("config: Q8_0 group size must be a power of two in [16, 1024]");
+        if (!pow2(gs) || gs < 16 || gs > 256)
+            return bad("config: Q8_0 group size must be a power of two in [16, 256]");
         if (c->dim % gs || c->hidden_dim % gs)
             return bad("config: Q8_0 group size must divide dim and hidden_dim");
     }
@@ -60,8 +60,8 @@ static int check_supported(l2d_ctx* ctx, const l2d_config* c)
     if (c->dim % 4 || c->hidden_dim % 4)
         return fail(ctx, L2D_EINVAL, "init: dim and hidden_dim must be multiples of 4");
     if (hs % 4 || hs > 256) return fail(ctx, L2D_EINVAL, "init: head_size must be a multiple of 4 and <= 256");
-    if (c->dtype == L2D_F32 && (c->dim > 16384 || c->hidden_dim > 16384))
-        return fail(ctx, L2D_EINVAL, "init: fp32 matvec inputs are limited to 16384 values (64 KiB of LDS)");
+    if (c->dtype == L2D_F32 && (c->dim > 16000 || c->hidden_dim > 16000))
+        return fail(ctx, L2D_EINVAL, "init: fp32 matvec inputs are limited to 16000 values (64 KiB of LDS)");
     if (c->dim > 65536 || c->hidden_dim > 65536)
         return fail(ctx, L2D_EINVAL, "init: matvec inputs are limited to 65536 values");
     if (!attention_supported(c->n_heads / c->n_kv_heads, hs))
@@ -115,6 +115,19 @@ int upload_rows(l2d_ctx* ctx, void* dst, size_t dpitch, const void* src, size_t 
     HIP_TRY(ctx, hipMemcpyAsync(staging, src, width * rows, hipMemcpyHostToDevice, ctx->stream));
     HIP_TRY(ctx, hipMemcpy2DAsync(dst, dpitch, staging, width, width, rows,
                                   hipMemcpyDeviceToDevice, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return L2D_OK;
+}
+
+// host -> device copy of Q8_0 codes [rows][K] through the staging buffer,
+// re-laid-out on the device (group-interleaved rows; source row r lands at
+// destination row (r / blk) * stride + off + r % blk)
+int upload_q8(l2d_ctx* ctx, void* dst, const void* src, int64_t rows, int64_t K, int64_t blk,
+              int64_t stride, int64_t off, void* staging)
+{
+    HIP_TRY(ctx, hipMemcpyAsync(staging, src, (size_t)(rows * K), hipMemcpyHostToDevice, ctx->stream));
+    HIP_TRY(ctx, launch_permute_q8((const int8_t*)staging, (int8_t*)dst, rows, K, ctx->gs, blk, stride,
+                                   off, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     return L2D_OK;
 }
@@ -215,7 +228,6 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         a.o = ctx->o;
         a.part_o = ctx->part_o;
         a.part_ml = ctx->part_ml;
-        a.counters = ctx->counters;
         a.step = ctx->step;
         a.S = (int32_t)ctx->S;
         a.nkv = (int32_t)ctx->nkv;
@@ -379,21 +391,20 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ALLOC(ctx->hb, (size_t)h * 4);
     ALLOC(ctx->logits, (size_t)V * 4);
     ALLOC(ctx->step, 64);
-    ALLOC(ctx->argmax, 64);
-    // attention position splits: about 1024 workgroups over the kv heads
-    // (fewer when G query heads share a kv head: their merge grows with G),
-    // never more than one split per sub-chunk of the full context
+    ALLOC(ctx->argmax, (size_t)kArgmaxWords * 8);
+    // attention position splits: about 2048 workgroups over the kv heads at
+    // full context (splits of at least one sub-chunk; the grid is sized
+    // once, inactive splits exit), at most 64 splits to merge per head
     {
         const int64_t sc = attention_positions_per_subchunk((int)ctx->hs);
-        int64_t ns = 1024 / ctx->nkv;
-        if (ns > 512 / ctx->G) ns = 512 / ctx->G;
+        int64_t ns = 2048 / ctx->nkv;
+        if (ns > 64) ns = 64;
         if (ns > (ctx->S + sc - 1) / sc) ns = (ctx->S + sc - 1) / sc;
         ctx->nsplit = (int)(ns < 1 ? 1 : ns);
     }
     const size_t nparts = (size_t)ctx->nkv * ctx->nsplit * ctx->G;
     ALLOC(ctx->part_o, nparts * ctx->hs * 8);
     ALLOC(ctx->part_ml, nparts * 2 * 8);
-    ALLOC(ctx->counters, (size_t)ctx->nkv * 4);
     for (int i = 0; i < 4; i++) {
         const int64_t n = i == 3 ? h : d;
         ALLOC(ctx->trace_q[i], (size_t)n);
@@ -403,7 +414,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     // staging buffer for the strided (re-laid-out) uploads: the largest of
     // the arrays that go through it
     size_t stage = 0;
-    for (int64_t n : {L * d * d, L * kvd * d, L * h * d}) {
+    for (int64_t n : {L * d * d, L * kvd * d, L * h * d, V * d}) {
         if ((size_t)n * es > stage) stage = (size_t)n * es;
         if (sbytes(n) > stage) stage = sbytes(n);
     }
@@ -417,40 +428,48 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     }
     auto up_all = [&]() -> int {
         int r;
-        // embedding (and its scales)
-        if ((r = upload(ctx, ctx->emb, w->emb, (size_t)(V * d) * es))) return r;
-        if (q8 && (r = upload(ctx, ctx->emb_s, w->emb_s, sbytes(V * d)))) return r;
-        // q, k, v rows of each layer side by side: [L][d + 2kvd][d]
         const size_t lpitch = (size_t)(nqkv * d) * es;
-        if ((r = upload_rows(ctx, ctx->wqkv, lpitch, w->wq, (size_t)(d * d) * es, L, staging))) return r;
-        if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)(d * d) * es, lpitch, w->wk,
-                             (size_t)(kvd * d) * es, L, staging))) return r;
-        if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)((d + kvd) * d) * es, lpitch, w->wv,
-                             (size_t)(kvd * d) * es, L, staging))) return r;
+        const size_t rb = (size_t)d * es;
         if (q8) {
+            // codes: group-interleaved rows, placed by the permute kernel
+            const int64_t all = 1ll << 62;
+            if ((r = upload_q8(ctx, ctx->emb, w->emb, V, d, all, 0, 0, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->wqkv, w->wq, L * d, d, d, nqkv, 0, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->wqkv, w->wk, L * kvd, d, kvd, nqkv, d, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->wqkv, w->wv, L * kvd, d, kvd, nqkv, d + kvd, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->wo, w->wo, L * d, d, all, 0, 0, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->w13, w->w1, L * h, d, 1, 2, 0, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->w13, w->w3, L * h, d, 1, 2, 1, staging))) return r;
+            if ((r = upload_q8(ctx, ctx->w2, w->w2, L * d, h, all, 0, 0, staging))) return r;
+            if (!shared && (r = upload_q8(ctx, ctx->wcls, w->wcls, V, d, all, 0, 0, staging))) return r;
+            // scales: plain [row][K/gs], rows placed like the codes
+            if ((r = upload(ctx, ctx->emb_s, w->emb_s, sbytes(V * d)))) return r;
             const size_t sp = sbytes(nqkv * d);
             if ((r = upload_rows(ctx, ctx->wqkv_s, sp, w->wq_s, sbytes(d * d), L, staging))) return r;
             if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv_s + sbytes(d * d), sp, w->wk_s,
                                  sbytes(kvd * d), L, staging))) return r;
             if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv_s + sbytes((d + kvd) * d), sp, w->wv_s,
                                  sbytes(kvd * d), L, staging))) return r;
-        }
-        if ((r = upload(ctx, ctx->wo, w->wo, (size_t)(L * d * d) * es))) return r;
-        if (q8 && (r = upload(ctx, ctx->wo_s, w->wo_s, sbytes(L * d * d)))) return r;
-        // w1 / w3 rows interleaved: [L][h][2][d]
-        const size_t rb = (size_t)d * es;
-        if ((r = upload_rows(ctx, ctx->w13, 2 * rb, w->w1, rb, L * h, staging))) return r;
-        if ((r = upload_rows(ctx, (uint8_t*)ctx->w13 + rb, 2 * rb, w->w3, rb, L * h, staging))) return r;
-        if (q8) {
+            if ((r = upload(ctx, ctx->wo_s, w->wo_s, sbytes(L * d * d)))) return r;
             const size_t sb = sbytes(d);
             if ((r = upload_rows(ctx, ctx->w13_s, 2 * sb, w->w1_s, sb, L * h, staging))) return r;
             if ((r = upload_rows(ctx, (uint8_t*)ctx->w13_s + sb, 2 * sb, w->w3_s, sb, L * h, staging))) return r;
-        }
-        if ((r = upload(ctx, ctx->w2, w->w2, (size_t)(L * d * h) * es))) return r;
-        if (q8 && (r = upload(ctx, ctx->w2_s, w->w2_s, sbytes(L * d * h)))) return r;
-        if (!shared) {
-            if ((r = upload(ctx, ctx->wcls, w->wcls, (size_t)(V * d) * es))) return r;
-            if (q8 && (r = upload(ctx, ctx->wcls_s, w->wcls_s, sbytes(V * d)))) return r;
+            if ((r = upload(ctx, ctx->w2_s, w->w2_s, sbytes(L * d * h)))) return r;
+            if (!shared && (r = upload(ctx, ctx->wcls_s, w->wcls_s, sbytes(V * d)))) return r;
+        } else {
+            if ((r = upload(ctx, ctx->emb, w->emb, (size_t)(V * d) * es))) return r;
+            // q, k, v rows of each layer side by side: [L][d + 2kvd][d]
+            if ((r = upload_rows(ctx, ctx->wqkv, lpitch, w->wq, (size_t)(d * d) * es, L, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)(d * d) * es, lpitch, w->wk,
+                                 (size_t)(kvd * d) * es, L, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)((d + kvd) * d) * es, lpitch, w->wv,
+                                 (size_t)(kvd * d) * es, L, staging))) return r;
+            if ((r = upload(ctx, ctx->wo, w->wo, (size_t)(L * d * d) * es))) return r;
+            // w1 / w3 rows interleaved: [L][h][2][d]
+            if ((r = upload_rows(ctx, ctx->w13, 2 * rb, w->w1, rb, L * h, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->w13 + rb, 2 * rb, w->w3, rb, L * h, staging))) return r;
+            if ((r = upload(ctx, ctx->w2, w->w2, (size_t)(L * d * h) * es))) return r;
+            if (!shared && (r = upload(ctx, ctx->wcls, w->wcls, (size_t)(V * d) * es))) return r;
         }
         if ((r = upload(ctx, ctx->rms_att, w->rms_att, (size_t)(L * d) * 4))) return r;
         if ((r = upload(ctx, ctx->rms_ffn, w->rms_ffn, (size_t)(L * d) * 4))) return r;
@@ -476,8 +495,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     }
     HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->counters, 0, (size_t)ctx->nkv * 4, ctx->stream));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, 64, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, (size_t)kArgmaxWords * 8, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     return capture(ctx);
@@ -580,10 +598,13 @@ int l2d_last_token(l2d_ctx* ctx, int32_t* token)
 {
     if (!ctx || !token) return fail(ctx, L2D_EINVAL, "last_token: null argument");
     if (ctx->last_pos < 0) return fail(ctx, L2D_EINVAL, "last_token: no forward yet");
-    unsigned long long v = 0;
-    HIP_TRY(ctx, hipMemcpyAsync(&v, ctx->argmax + (ctx->last_pos & 1), 8, hipMemcpyDeviceToHost,
-                                ctx->stream));
+    unsigned long long slots[kArgmaxSlots * kArgmaxStride];
+    HIP_TRY(ctx, hipMemcpyAsync(slots, ctx->argmax + (size_t)(ctx->last_pos & 1) * kArgmaxSlots * kArgmaxStride,
+                                sizeof(slots), hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    unsigned long long v = 0;
+    for (int i = 0; i < kArgmaxSlots; i++)
+        if (slots[i * kArgmaxStride] > v) v = slots[i * kArgmaxStride];
     *token = (int32_t)(0xFFFFFFFFu - (uint32_t)(v & 0xFFFFFFFFull));
     return L2D_OK;
 }
@@ -646,15 +667,27 @@ int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int
     if (rows <= 0 || cols <= 0 || rows % 2 || cols % 4 || !W || !x || !out)
         return fail(nullptr, L2D_EINVAL, "gemv: need rows even > 0, cols % 4 == 0, non-null pointers");
     if (dtype == L2D_Q8_0) {
-        if (gs < 16 || gs > 1024 || (gs & (gs - 1)) || cols % gs || !W_s)
-            return fail(nullptr, L2D_EINVAL, "gemv: Q8_0 needs a power-of-two gs in [16,1024] dividing cols");
+        if (gs < 16 || gs > 256 || (gs & (gs - 1)) || cols % gs || !W_s)
+            return fail(nullptr, L2D_EINVAL, "gemv: Q8_0 needs a power-of-two gs in [16,256] dividing cols");
         if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
-    } else if (cols > 16384) {
-        return fail(nullptr, L2D_EINVAL, "gemv: fp32 cols > 16384");
+    } else if (cols > 16000) {
+        return fail(nullptr, L2D_EINVAL, "gemv: fp32 cols > 16000");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    void* perm = nullptr;
+    if (dtype == L2D_Q8_0) {
+        // the kernel reads the device layout: group-interleaved rows
+        hipError_t e = hipMallocAsync(&perm, (size_t)(rows * cols), st);
+        if (e != hipSuccess) return fail(nullptr, L2D_ENOMEM, "gemv: no device memory for the re-laid-out codes");
+        e = launch_permute_q8((const int8_t*)W, (int8_t*)perm, rows, cols, gs, 1ll << 62, 0, 0, st);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(perm, st);
+            return fail(nullptr, L2D_EHIP, std::string("gemv: ") + hipGetErrorString(e));
+        }
     }
     GemvParams p;
     memset(&p, 0, sizeof(p));
-    p.W = W;
+    p.W = perm ? perm : W;
     p.Ws = W_s;
     p.M = rows;
     p.K = cols;
@@ -666,7 +699,8 @@ int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int
     hipGetDevice(&dev);
     hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     hipError_t e = launch_gemv(dtype == L2D_F32 ? DT_F32 : DT_Q8, PRO_PLAIN, EPI_STORE, p,
-                               cus > 0 ? 2 * cus : 512, (hipStream_t)stream);
+                               cus > 0 ? 2 * cus : 512, st);
+    if (perm) (void)hipFreeAsync(perm, st);
     if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("gemv: ") + hipGetErrorString(e));
     return L2D_OK;
 }

@@ -178,3 +178,24 @@ __device__ __forceinline__ double wave_sum_to_last(double v)
 }
 
 }  // namespace l2d
+
+namespace l2d {
+
+// Device layout of a Q8_0 row of K codes (group size gs, ng = K/gs groups):
+// groups are taken 64 at a time ("blocks"; the last block may hold fewer,
+// nb); within a block the 16-byte quarters of its groups are stored quarter
+// by quarter: quarter q of group j of the block sits at
+//     block_start + 16*nb*q + 16*j,   block_start = 64*gs*block.
+// A wavefront reading quarter q of a block with lane j = group j loads 16*nb
+// contiguous bytes, and each lane ends up with whole groups.
+__host__ __device__ __forceinline__ int64_t q8_perm_offset(int64_t i, int64_t K, int gs)
+{
+    const int64_t ng = K / gs;
+    const int64_t g = i / gs, w = i % gs;
+    const int64_t blk = g / 64, j = g % 64;
+    const int64_t nb = (ng - blk * 64) < 64 ? (ng - blk * 64) : 64;
+    const int64_t q = w / 16, b = w % 16;
+    return blk * 64 * gs + 16 * nb * q + 16 * j + b;
+}
+
+}  // namespace l2d

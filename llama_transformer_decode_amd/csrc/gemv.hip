@@ -2,23 +2,29 @@
 //
 // One kernel template serves every matvec of the step (q/k/v, output
 // projection, w1/w3, w2, classifier: the hand-written row-by-row matmul of
-// the ainews article's technical section, over HBM-resident weights):
+// the ainews article's technical section, over HBM-resident weights).
 //
-//   prologue  every workgroup builds the input vector in LDS in one parallel
-//             pass (16 values per thread): x as is, or RMSNorm(x) (pomoai.com
-//             hub page, architecture list), and for Q8_0 the int8 codes and
-//             group scales of that vector (gitcode porting guide, INT8
-//             quantisation section; the group max is a DPP lane reduction);
-//   main loop each wavefront owns a contiguous, balanced range of row tiles
-//             (RPW rows each) and streams them in chunks of U 16-byte loads
-//             per row, double-buffered: the next chunk is in flight while the
-//             current one is consumed, and the first chunk is issued before
-//             the prologue so its HBM latency overlaps the prologue. Lanes
-//             cover 64 x 16 B = 1 KiB contiguous per load instruction. fp32
-//             rows multiply-add into fp64 (a product of two fp32 values is
-//             exact in fp64); Q8_0 rows use v_dot4_i32_i8 for exact int32
-//             group dots (DPP quad sums), combined in fp64 with the weight
-//             and activation scales;
+// Order of work in a workgroup, arranged so that the HBM latency of the
+// weights overlaps everything else:
+//   1. every thread issues the loads of its share of the input vector (and
+//      of the RMSNorm gain);
+//   2. every wavefront issues the loads of its first NBUF weight chunks;
+//   3. prologue: the input vector is prepared in LDS while those loads are in
+//      flight: x as is, or RMSNorm(x) (pomoai.com hub page, architecture
+//      list), and for Q8_0 the int8 codes and group scales of that vector
+//      (gitcode porting guide, INT8 quantisation section; group max by DPP);
+//   4. main loop over a contiguous, balanced range of row tiles (RPW rows
+//      each), as a ring of NBUF chunk buffers: consume a chunk, refill its
+//      buffer with the chunk NBUF ahead. Every load is unconditional (indices
+//      past the end are clamped onto valid memory and their contribution is
+//      masked), so each iteration issues the same loads and the compiler's
+//      wait counts stay exact: NBUF-1 chunks remain in flight while one is
+//      consumed.
+// Lanes cover 64 x 16 B = 1 KiB contiguous per load instruction. fp32 rows
+// multiply-add into fp64 (a product of two fp32 values is exact in fp64).
+// Q8_0 rows are stored group-interleaved (q8_perm_offset) so that each lane
+// holds whole groups: v_dot4_i32_i8 gives the exact int32 group dot in one
+// lane, combined in fp64 with the weight and activation scales.
 //   epilogue  a DPP wave sum leaves each row's total in lane 63, which
 //             finishes the tile: store, residual add, RoPE + KV-cache write,
 //             SwiGLU, or classifier + packed argmax.
@@ -31,6 +37,13 @@ namespace l2d {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+
+// LDS bytes of the prepared input vector (16-byte aligned end)
+__host__ __device__ inline size_t gemv_input_bytes(int dt, int64_t K, int gs)
+{
+    const size_t b = dt == DT_F32 ? (size_t)K * 4 : (size_t)K + (size_t)(K / gs) * 4;
+    return (b + 15) & ~(size_t)15;
+}
 
 // ---------------------------------------------------------------- prologue
 
@@ -46,63 +59,59 @@ __device__ __forceinline__ double block_sum(double v, double* red)
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
 
-// fp32 input vector -> LDS as float4 chunks (thread t takes chunks t, t+256,
-// ...). NC: float4 chunks per thread kept in registers for RMSNorm.
+__device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// fp32 input: thread t holds float4 chunks t, t+256, ... (NC of them)
 template <int PRO, int NC>
-__device__ __forceinline__ void prologue_f32(const GemvParams& p, unsigned char* smem)
-{
-    const int tid = threadIdx.x;
-    const int64_t K4 = p.K / 4;
-    f32x4* xl = (f32x4*)smem;
-    __shared__ double red[kWaves];
-    if (PRO == PRO_NORM) {
-        f32x4 xv[NC], gv[NC];
+struct InputF32 {
+    f32x4 x[NC], g[NC];
+
+    __device__ __forceinline__ void issue(const GemvParams& p)
+    {
+        const int64_t K4 = p.K / 4;
 #pragma unroll
         for (int j = 0; j < NC; j++) {
-            const int64_t c = (int64_t)j * kThreads + tid;
-            xv[j] = c < K4 ? ld4(p.x + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
-            gv[j] = c < K4 ? ld4(p.gain + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int64_t c = imin((int64_t)j * kThreads + threadIdx.x, K4 - 1);
+            x[j] = ld4(p.x + 4 * c);
+            if (PRO == PRO_NORM) g[j] = ld4(p.gain + 4 * c);
         }
-        double ss = 0.0;
+    }
+
+    __device__ __forceinline__ void finish(const GemvParams& p, unsigned char* smem, double* red)
+    {
+        const int64_t K4 = p.K / 4;
+        f32x4* xl = (f32x4*)smem;
+        double r = 1.0;
+        if (PRO == PRO_NORM) {
+            double ss = 0.0;
 #pragma unroll
-        for (int j = 0; j < NC; j++) {
-            ss += (double)xv[j].x * (double)xv[j].x;
-            ss += (double)xv[j].y * (double)xv[j].y;
-            ss += (double)xv[j].z * (double)xv[j].z;
-            ss += (double)xv[j].w * (double)xv[j].w;
+            for (int j = 0; j < NC; j++) {
+                const bool ok = (int64_t)j * kThreads + threadIdx.x < K4;
+                const f32x4 v = x[j];
+                const double s4 = (double)v.x * (double)v.x + (double)v.y * (double)v.y +
+                                  (double)v.z * (double)v.z + (double)v.w * (double)v.w;
+                ss += ok ? s4 : 0.0;
+            }
+            ss = block_sum(ss, red);
+            r = 1.0 / sqrt(ss / (double)p.K + p.eps);
         }
-        ss = block_sum(ss, red);
-        const double r = 1.0 / sqrt(ss / (double)p.K + p.eps);
 #pragma unroll
         for (int j = 0; j < NC; j++) {
-            const int64_t c = (int64_t)j * kThreads + tid;
+            const int64_t c = (int64_t)j * kThreads + threadIdx.x;
             if (c < K4) {
-                f32x4 o;
-                o.x = (float)((double)gv[j].x * ((double)xv[j].x * r));
-                o.y = (float)((double)gv[j].y * ((double)xv[j].y * r));
-                o.z = (float)((double)gv[j].z * ((double)xv[j].z * r));
-                o.w = (float)((double)gv[j].w * ((double)xv[j].w * r));
+                f32x4 o = x[j];
+                if (PRO == PRO_NORM) {
+                    o.x = (float)((double)g[j].x * ((double)x[j].x * r));
+                    o.y = (float)((double)g[j].y * ((double)x[j].y * r));
+                    o.z = (float)((double)g[j].z * ((double)x[j].z * r));
+                    o.w = (float)((double)g[j].w * ((double)x[j].w * r));
+                }
                 xl[c] = o;
             }
         }
-    } else {
-        constexpr int B = 8;  // loads in flight per thread
-        for (int64_t base = 0; base < K4; base += (int64_t)B * kThreads) {
-            f32x4 v[B];
-#pragma unroll
-            for (int j = 0; j < B; j++) {
-                const int64_t c = base + (int64_t)j * kThreads + tid;
-                v[j] = c < K4 ? ld4(p.x + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int j = 0; j < B; j++) {
-                const int64_t c = base + (int64_t)j * kThreads + tid;
-                if (c < K4) xl[c] = v[j];
-            }
-        }
+        __syncthreads();
     }
-    __syncthreads();
-}
+};
 
 // quantise one 16-value chunk (this lane's part of a group of lpg lanes)
 __device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_out)
@@ -127,91 +136,134 @@ __device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_o
     return i32x4{w[0], w[1], w[2], w[3]};
 }
 
-__device__ __forceinline__ void load16(float* v, const float* src, bool ok)
+__device__ __forceinline__ void unpack16(float* v, const f32x4* a)
 {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-        const f32x4 a = ok ? ld4(src + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
-        v[4 * k] = a.x;
-        v[4 * k + 1] = a.y;
-        v[4 * k + 2] = a.z;
-        v[4 * k + 3] = a.w;
+        v[4 * k] = a[k].x;
+        v[4 * k + 1] = a[k].y;
+        v[4 * k + 2] = a[k].z;
+        v[4 * k + 3] = a[k].w;
     }
 }
 
-// Q8_0 input vector -> LDS codes [K] + scales [K/gs] (thread t takes 16-value
-// chunks t, t+256, ...; the lpg = gs/16 lanes of a group are adjacent).
-// NC: 16-value chunks per thread kept in registers for RMSNorm.
+// Q8_0 input: thread t holds 16-value chunks t, t+256, ... (NC of them);
+// lanes of one group (lpg = gs/16) are adjacent. Codes go to LDS in the
+// group-interleaved order of the weights, scales in plain order after them.
+// NC == 0: the input is too long to hold; it is loaded in batches after the
+// weight prefetch instead.
 template <int PRO, int NC>
-__device__ __forceinline__ void prologue_q8(const GemvParams& p, unsigned char* smem)
-{
-    const int tid = threadIdx.x;
-    const int64_t nq = p.K / 16;
-    const int lpg = p.gs / 16;
-    i32x4* xq = (i32x4*)smem;
-    float* xs = (float*)(smem + p.K);
-    __shared__ double red[kWaves];
-    if (PRO == PRO_NORM) {
-        float xv[NC][16], gv[NC][16];
+struct InputQ8 {
+    static constexpr int N = NC > 0 ? NC : 1;
+    f32x4 x[N][4], g[N][4];
+
+    __device__ __forceinline__ void issue(const GemvParams& p)
+    {
+        if (NC == 0) return;
+        const int64_t nq = p.K / 16;
 #pragma unroll
-        for (int j = 0; j < NC; j++) {
-            const int64_t c = (int64_t)j * kThreads + tid;
-            load16(xv[j], p.x + 16 * c, c < nq);
-            load16(gv[j], p.gain + 16 * c, c < nq);
-        }
-        double ss = 0.0;
+        for (int j = 0; j < N; j++) {
+            const int64_t c = imin((int64_t)j * kThreads + threadIdx.x, nq - 1);
 #pragma unroll
-        for (int j = 0; j < NC; j++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) ss += (double)xv[j][i] * (double)xv[j][i];
-        ss = block_sum(ss, red);
-        const double r = 1.0 / sqrt(ss / (double)p.K + p.eps);
-#pragma unroll
-        for (int j = 0; j < NC; j++) {
-            const int64_t c = (int64_t)j * kThreads + tid;
-            float v[16];
-#pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = (float)((double)gv[j][i] * ((double)xv[j][i] * r));
-            float sc;
-            const i32x4 codes = quant16(v, lpg, &sc);
-            if (c < nq) {
-                xq[c] = codes;
-                if ((c & (lpg - 1)) == 0) xs[c / lpg] = sc;
+            for (int k = 0; k < 4; k++) {
+                x[j][k] = ld4(p.x + 16 * c + 4 * k);
+                if (PRO == PRO_NORM) g[j][k] = ld4(p.gain + 16 * c + 4 * k);
             }
         }
-    } else {
-        constexpr int B = 4;  // 16-value chunks in flight per thread
-        for (int64_t base = 0; base < nq; base += (int64_t)B * kThreads) {
-            float v[B][16];
+    }
+
+    __device__ __forceinline__ void store(const GemvParams& p, unsigned char* smem, int64_t c,
+                                          const float* v, int lpg)
+    {
+        float sc;
+        const i32x4 codes = quant16(v, lpg, &sc);
+        if (c < p.K / 16) {
+            ((i32x4*)smem)[q8_perm_offset(16 * c, p.K, p.gs) / 16] = codes;
+            if ((c & (lpg - 1)) == 0) ((float*)(smem + p.K))[c / lpg] = sc;
+        }
+    }
+
+    __device__ __forceinline__ void finish(const GemvParams& p, unsigned char* smem, double* red)
+    {
+        const int64_t nq = p.K / 16;
+        const int lpg = p.gs / 16;
+        if (NC > 0) {
+            double r = 1.0;
+            if (PRO == PRO_NORM) {
+                double ss = 0.0;
 #pragma unroll
-            for (int j = 0; j < B; j++) {
-                const int64_t c = base + (int64_t)j * kThreads + tid;
-                load16(v[j], p.x + 16 * c, c < nq);
+                for (int j = 0; j < N; j++) {
+                    const bool ok = (int64_t)j * kThreads + threadIdx.x < nq;
+                    double s = 0.0;
+#pragma unroll
+                    for (int k = 0; k < 4; k++)
+                        s += (double)x[j][k].x * (double)x[j][k].x + (double)x[j][k].y * (double)x[j][k].y +
+                             (double)x[j][k].z * (double)x[j][k].z + (double)x[j][k].w * (double)x[j][k].w;
+                    ss += ok ? s : 0.0;
+                }
+                ss = block_sum(ss, red);
+                r = 1.0 / sqrt(ss / (double)p.K + p.eps);
             }
 #pragma unroll
-            for (int j = 0; j < B; j++) {
-                const int64_t c = base + (int64_t)j * kThreads + tid;
-                float sc;
-                const i32x4 codes = quant16(v[j], lpg, &sc);
-                if (c < nq) {
-                    xq[c] = codes;
-                    if ((c & (lpg - 1)) == 0) xs[c / lpg] = sc;
+            for (int j = 0; j < N; j++) {
+                if ((int64_t)j * kThreads >= nq) break;  // uniform
+                float v[16];
+                unpack16(v, x[j]);
+                if (PRO == PRO_NORM) {
+                    float gg[16];
+                    unpack16(gg, g[j]);
+#pragma unroll
+                    for (int i = 0; i < 16; i++) v[i] = (float)((double)gg[i] * ((double)v[i] * r));
+                }
+                store(p, smem, (int64_t)j * kThreads + threadIdx.x, v, lpg);
+            }
+        } else {
+            // long plain inputs: batches of 4 chunks per thread
+            for (int64_t base = 0; base < nq; base += 4 * kThreads) {
+                f32x4 a[4][4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int64_t c = imin(base + (int64_t)j * kThreads + threadIdx.x, nq - 1);
+#pragma unroll
+                    for (int k = 0; k < 4; k++) a[j][k] = ld4(p.x + 16 * c + 4 * k);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    if (base + (int64_t)j * kThreads >= nq) break;  // uniform
+                    float v[16];
+                    unpack16(v, a[j]);
+                    store(p, smem, base + (int64_t)j * kThreads + threadIdx.x, v, lpg);
                 }
             }
         }
+        __syncthreads();
+        if (p.trace_q != nullptr && blockIdx.x == 0) {
+            // back to plain element order for the trace
+            for (int64_t c = threadIdx.x; c < nq; c += kThreads)
+                ((i32x4*)p.trace_q)[c] = ((const i32x4*)smem)[q8_perm_offset(16 * c, p.K, p.gs) / 16];
+            for (int64_t g = threadIdx.x; g < p.K / p.gs; g += kThreads)
+                p.trace_s[g] = ((const float*)(smem + p.K))[g];
+        }
     }
-    __syncthreads();
-    if (p.trace_q != nullptr && blockIdx.x == 0) {
-        for (int64_t c = tid; c < nq; c += kThreads) ((i32x4*)p.trace_q)[c] = xq[c];
-        for (int64_t g = tid; g < p.K / p.gs; g += kThreads) p.trace_s[g] = xs[g];
-    }
-}
+};
 
 // ---------------------------------------------------------------- epilogue
 
+// What the epilogue needs besides the row sums, gathered without global
+// loads on the critical path: pos (read once per kernel), the residual values
+// of the tile's rows (loaded with the tile's weight chunks) and the RoPE
+// cos/sin table of this pos (built in LDS by the prologue).
+struct EpiIn {
+    int pos;
+    const float* res;    // [rpw] residual stream values of the tile's rows
+    const float* rcos;   // [hs/2] fp32 cosines of pos * freq_j
+    const float* rsin;   // [hs/2] fp32 sines
+};
+
 template <int EPI>
 __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0, int rpw,
-                                              const double* acc, unsigned long long& best)
+                                              const double* acc, unsigned long long& best,
+                                              const EpiIn& in)
 {
     if (EPI == EPI_STORE) {
         for (int r = 0; r < rpw; r++)
@@ -221,7 +273,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
             const int64_t row = row0 + r;
             if (row < p.M) {
                 const float y = (float)acc[r];
-                p.out[row] = (float)((double)p.out[row] + (double)y);
+                p.out[row] = (float)((double)in.res[r] + (double)y);
             }
         }
     } else if (EPI == EPI_LOGITS) {
@@ -248,7 +300,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
     } else if (EPI == EPI_QKV) {
         // rows [0, d) q, [d, d+kvd) k, [d+kvd, d+2kvd) v; pairs (2j, 2j+1)
         // of each q/k head rotate by pos * freq_j (RoPE, computed on the fly)
-        const int pos = p.step[1];
+        const int pos = in.pos;
         for (int r = 0; r + 1 < rpw; r += 2) {
             const int64_t row = row0 + r;
             if (row + 1 >= p.M) continue;
@@ -256,9 +308,8 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
             if (row < p.d + p.kvd) {
                 const int64_t within = row < p.d ? row : row - p.d;
                 const int j = (int)((within % p.hs) / 2);
-                const float ang = (float)pos * p.freqs[j];
-                const double c = (double)(float)cos((double)ang);
-                const double s = (double)(float)sin((double)ang);
+                const double c = (double)in.rcos[j];
+                const double s = (double)in.rsin[j];
                 const float ra = (float)((double)a * c - (double)b * s);
                 const float rb = (float)((double)a * s + (double)b * c);
                 if (row < p.d) {
@@ -280,33 +331,58 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
 
 // ---------------------------------------------------------------- main loop
 
-// One chunk of a tile: U loads of 16 bytes per lane for each of RPW rows.
+// One chunk of a tile.
+//   fp32: U loads of 16 bytes per lane for each of RPW rows (64*U float4
+//         columns of each row).
+//   Q8_0: one block of 64 groups of each of RPW rows in the permuted layout:
+//         lane j holds group j of the block, U = gs/16 loads of 16 bytes,
+//         plus that group's weight scale.
 template <int DT, int RPW, int U>
 struct Chunk {
     using V = typename std::conditional<DT == DT_F32, f32x4, i32x4>::type;
     V w[RPW][U];
-    float s[RPW][U];  // Q8_0: the weight scale of this lane's group
+    float s[RPW];
+    float res[RPW];  // residual values of the rows (EPI_RESID)
 };
 
-template <int DT, int RPW, int U>
+// Loads of one chunk; rows, columns and lanes past the end are clamped onto
+// valid addresses (use_chunk masks them), so the sequence never branches.
+// A "dummy" chunk (past the wave's last tile: the ring's refills at the end)
+// reads the first 16 bytes of the input vector instead, a cache-resident
+// address, so it costs no HBM traffic and returns quickly.
+template <int DT, int EPI, int RPW, int U>
 __device__ __forceinline__ void load_chunk(Chunk<DT, RPW, U>& ch, const GemvParams& p, int64_t row0,
-                                           int64_t c0, int64_t Kv, int lane, int gshift)
+                                           int64_t chunk, int lane, bool dummy)
 {
+    const int64_t keep = dummy ? 0 : 1;  // multiplies every offset
+    if (EPI == EPI_RESID) {
 #pragma unroll
-    for (int uu = 0; uu < U; uu++) {
-        const int64_t c = c0 + uu * kWave + lane;
+        for (int r = 0; r < RPW; r++) ch.res[r] = p.out[imin(row0 + r, p.M - 1) * keep];
+    }
+    if constexpr (DT == DT_F32) {
+        const int64_t Kv = p.K / 4;
+        const f32x4* base = dummy ? (const f32x4*)p.x : (const f32x4*)p.W;
+#pragma unroll
+        for (int uu = 0; uu < U; uu++) {
+            const int64_t c = imin(chunk * kWave * U + uu * kWave + lane, Kv - 1);
+#pragma unroll
+            for (int r = 0; r < RPW; r++)
+                ch.w[r][uu] = __builtin_nontemporal_load(base + (imin(row0 + r, p.M - 1) * Kv + c) * keep);
+        }
+    } else {
+        const int64_t ng = p.K / p.gs;
+        const int64_t g0 = chunk * 64;
+        const int64_t nb = imin(ng - g0, 64);
+        const int64_t j = imin(lane, nb - 1);
+        const int8_t* base = dummy ? (const int8_t*)p.x : (const int8_t*)p.W;
+        const float* sbase = dummy ? p.x : p.Ws;
 #pragma unroll
         for (int r = 0; r < RPW; r++) {
-            const bool ok = c < Kv && row0 + r < p.M;
-            if constexpr (DT == DT_F32) {
-                const f32x4* W = (const f32x4*)p.W + (row0 + r) * Kv;
-                ch.w[r][uu] = ok ? __builtin_nontemporal_load(W + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                const i32x4* W = (const i32x4*)p.W + (row0 + r) * Kv;
-                ch.w[r][uu] = ok ? __builtin_nontemporal_load(W + c) : i32x4{0, 0, 0, 0};
-                const int64_t ngr = (Kv * 16) >> (gshift + 4);
-                ch.s[r][uu] = ok ? p.Ws[(row0 + r) * ngr + (c >> gshift)] : 0.0f;
-            }
+            const int64_t row = imin(row0 + r, p.M - 1);
+            const i32x4* W = (const i32x4*)(base + (row * p.K + g0 * p.gs) * keep);
+#pragma unroll
+            for (int q = 0; q < U; q++) ch.w[r][q] = __builtin_nontemporal_load(W + (nb * q + j) * keep);
+            ch.s[r] = sbase[(row * ng + g0 + j) * keep];
         }
     }
 }
@@ -314,15 +390,16 @@ __device__ __forceinline__ void load_chunk(Chunk<DT, RPW, U>& ch, const GemvPara
 template <int DT, int RPW, int U, bool DBG>
 __device__ __forceinline__ void use_chunk(const Chunk<DT, RPW, U>& ch, double* acc,
                                           const GemvParams& p, const unsigned char* smem,
-                                          int64_t row0, int64_t c0, int64_t Kv, int lane,
-                                          int gshift, int lpg)
+                                          int64_t row0, int64_t chunk, int lane, bool valid)
 {
+    if constexpr (DT == DT_F32) {
+        const int64_t Kv = p.K / 4;
 #pragma unroll
-    for (int uu = 0; uu < U; uu++) {
-        const int64_t c = c0 + uu * kWave + lane;
-        const bool ok = c < Kv;
-        if constexpr (DT == DT_F32) {
-            const f32x4 xv = ok ? ((const f32x4*)smem)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int uu = 0; uu < U; uu++) {
+            const int64_t c = chunk * kWave * U + uu * kWave + lane;
+            const f32x4 xl = ((const f32x4*)smem)[imin(c, Kv - 1)];
+            const bool ok = valid && c < Kv;
+            const f32x4 xv = ok ? xl : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < RPW; r++) {
                 const f32x4 w = ch.w[r][uu];
@@ -331,136 +408,191 @@ __device__ __forceinline__ void use_chunk(const Chunk<DT, RPW, U>& ch, double* a
                 acc[r] += (double)w.z * (double)xv.z;
                 acc[r] += (double)w.w * (double)xv.w;
             }
-        } else {
-            const i32x4 xv = ok ? ((const i32x4*)smem)[c] : i32x4{0, 0, 0, 0};
-            const float* xs = (const float*)(smem + Kv * 16);
-            const int64_t g = c >> gshift;
-            const double xsg = ok ? (double)xs[g] : 0.0;
-            const bool lead = (lane & (lpg - 1)) == 0;
+        }
+    } else {
+        const int64_t ng = p.K / p.gs;
+        const int64_t g0 = chunk * 64;
+        const int64_t nb = imin(ng - g0, 64);
+        const int64_t j = imin(lane, nb - 1);
+        const bool ok = valid && lane < nb;
+        const i32x4* xq = (const i32x4*)(smem + g0 * p.gs);
+        i32x4 xv[U];
 #pragma unroll
-            for (int r = 0; r < RPW; r++) {
-                int d = dot16_i8(ch.w[r][uu], xv);
-                d = lanes_sum_i32(d, lpg);
-                const double t = ((double)d * (double)ch.s[r][uu]) * xsg;
-                acc[r] += (ok && lead) ? t : 0.0;
-                if (DBG && ok && lead && row0 + r < p.M) {
-                    const int64_t ngr = (Kv * 16) >> (gshift + 4);
-                    p.group_dots[(row0 + r) * ngr + g] = d;
-                }
+        for (int q = 0; q < U; q++) xv[q] = xq[nb * q + j];
+        const double xsg = (double)((const float*)(smem + p.K))[g0 + j];
+#pragma unroll
+        for (int r = 0; r < RPW; r++) {
+            int d = 0;
+#pragma unroll
+            for (int q = 0; q < U; q++) {
+                d = dot4_i8(ch.w[r][q].x, xv[q].x, d);
+                d = dot4_i8(ch.w[r][q].y, xv[q].y, d);
+                d = dot4_i8(ch.w[r][q].z, xv[q].z, d);
+                d = dot4_i8(ch.w[r][q].w, xv[q].w, d);
             }
+            const double t = ((double)d * (double)ch.s[r]) * xsg;
+            acc[r] += ok ? t : 0.0;
+            if (DBG && ok && row0 + r < p.M) p.group_dots[(row0 + r) * ng + g0 + lane] = d;
         }
     }
 }
 
-template <int DT, int PRO, int EPI, int RPW, int U, int NC, bool DBG>
+template <int DT, int PRO, int EPI, int RPW, int U, int NC, int NBUF, bool DBG>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ double red[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t Kv = DT == DT_F32 ? p.K / 4 : p.K / 16;  // 16-byte vectors per row
-    const int gshift = DT == DT_F32 ? 0 : ilog2(p.gs) - 4;  // vector index -> group
-    const int lpg = DT == DT_F32 ? 1 : p.gs / 16;            // lanes per group
-    const int64_t CH = (int64_t)kWave * U;                  // vectors per row per chunk
-    const int64_t nch = (Kv + CH - 1) / CH;                  // chunks per tile
-
+    // chunks per tile: 64*U float4 columns (fp32) or 64 groups (Q8_0)
+    const int64_t nch = DT == DT_F32 ? (p.K / 4 + kWave * U - 1) / (kWave * U)
+                                     : (p.K / p.gs + 63) / 64;
     // balanced contiguous range of tiles for this wave
     const int64_t tiles = (p.M + RPW - 1) / RPW;
     const int64_t nw = (int64_t)gridDim.x * kWaves;
     const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
     const int64_t t_beg = tiles * gw / nw, t_end = tiles * (gw + 1) / nw;
     const int64_t iters = (t_end - t_beg) * nch;
+    const int pos = (EPI == EPI_QKV || EPI == EPI_LOGITS) ? p.step[1] : 0;
 
-    Chunk<DT, RPW, U> A, B;
-    if (iters > 0) load_chunk<DT, RPW, U>(A, p, t_beg * RPW, 0, Kv, lane, gshift);
+    // 1. input loads
+    typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<PRO, NC>>::type in;
+    in.issue(p);
 
-    if constexpr (DT == DT_F32)
-        prologue_f32<PRO, NC>(p, smem);
-    else
-        prologue_q8<PRO, NC>(p, smem);
+    // 2. the first NBUF chunks (dummy loads for a wave with fewer chunks)
+    Chunk<DT, RPW, U> buf[NBUF];
+    int64_t ltile = t_beg, lch = 0;
+    auto load_next = [&](Chunk<DT, RPW, U>& b) {
+        load_chunk<DT, EPI, RPW, U>(b, p, imin(ltile, tiles - 1) * RPW, lch, lane, ltile >= t_end);
+        if (++lch == nch) {
+            lch = 0;
+            ++ltile;
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < NBUF; k++) load_next(buf[k]);
 
+    // 3. prologue. RoPE table of this pos first: fp32 cosine / sine of the
+    //    fp32 angle pos*freq_j, correctly rounded (fp64 value rounded once)
+    float* rcos = (float*)(smem + gemv_input_bytes(DT, p.K, p.gs));
+    float* rsin = rcos + p.hs / 2;
+    if (EPI == EPI_QKV && (int)threadIdx.x < p.hs / 2) {
+        const float ang = (float)pos * p.freqs[threadIdx.x];
+        rcos[threadIdx.x] = (float)cos((double)ang);
+        rsin[threadIdx.x] = (float)sin((double)ang);
+    }
+    in.finish(p, smem, red);
+
+    // 4. main loop: every iteration consumes one buffer and refills it
     double acc[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; r++) acc[r] = 0.0;
     unsigned long long best = 0;
-    int64_t tile = t_beg, ch = 0;  // position of the chunk in A
-    int64_t ntile = t_beg, nchk = 0;
-
-    auto advance = [&](int64_t& t, int64_t& c) {
-        if (++c == nch) {
-            c = 0;
-            ++t;
+    int64_t tile = t_beg, ch = 0;
+    for (int64_t it = 0; it < iters; it += NBUF) {
+#pragma unroll
+        for (int k = 0; k < NBUF; k++) {
+            const bool valid = it + k < iters;
+            use_chunk<DT, RPW, U, DBG>(buf[k], acc, p, smem, tile * RPW, ch, lane, valid);
+            if (valid && ch == nch - 1) {
+#pragma unroll
+                for (int r = 0; r < RPW; r++) acc[r] = wave_sum_to_last(acc[r]);
+                if (lane == kWave - 1) {
+                    const EpiIn ein{pos, buf[k].res, rcos, rsin};
+                    gemv_epilogue<EPI>(p, tile * RPW, RPW, acc, best, ein);
+                }
+#pragma unroll
+                for (int r = 0; r < RPW; r++) acc[r] = 0.0;
+            }
+            load_next(buf[k]);
+            if (++ch == nch) {
+                ch = 0;
+                ++tile;
+            }
         }
-    };
-    auto finish_tile = [&]() {
-#pragma unroll
-        for (int r = 0; r < RPW; r++) acc[r] = wave_sum_to_last(acc[r]);
-        if (lane == kWave - 1) gemv_epilogue<EPI>(p, tile * RPW, RPW, acc, best);
-#pragma unroll
-        for (int r = 0; r < RPW; r++) acc[r] = 0.0;
-    };
-
-    for (int64_t it = 0; it < iters; it += 2) {
-        // A holds chunk `it`; fetch it+1 into B, then consume A
-        ntile = tile;
-        nchk = ch;
-        advance(ntile, nchk);
-        if (it + 1 < iters) load_chunk<DT, RPW, U>(B, p, ntile * RPW, nchk * CH, Kv, lane, gshift);
-        use_chunk<DT, RPW, U, DBG>(A, acc, p, smem, tile * RPW, ch * CH, Kv, lane, gshift, lpg);
-        if (ch == nch - 1) finish_tile();
-        tile = ntile;
-        ch = nchk;
-        if (it + 1 >= iters) break;
-        // B holds chunk it+1; fetch it+2 into A, then consume B
-        ntile = tile;
-        nchk = ch;
-        advance(ntile, nchk);
-        if (it + 2 < iters) load_chunk<DT, RPW, U>(A, p, ntile * RPW, nchk * CH, Kv, lane, gshift);
-        use_chunk<DT, RPW, U, DBG>(B, acc, p, smem, tile * RPW, ch * CH, Kv, lane, gshift, lpg);
-        if (ch == nch - 1) finish_tile();
-        tile = ntile;
-        ch = nchk;
     }
-    if (EPI == EPI_LOGITS && lane == kWave - 1 && best != 0)
-        atomicMax(p.argmax + (p.step[1] & 1), best);
+    if (EPI == EPI_LOGITS) {
+        // workgroup maximum, then one atomic into a slot chosen by workgroup
+        __shared__ unsigned long long wbest[kWaves];
+        if (lane == kWave - 1) wbest[wave] = best;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long b = wbest[0];
+            for (int w = 1; w < kWaves; w++) b = wbest[w] > b ? wbest[w] : b;
+            if (b != 0)
+                atomicMax(p.argmax + ((size_t)(pos & 1) * kArgmaxSlots + blockIdx.x % kArgmaxSlots) *
+                                         kArgmaxStride,
+                          b);
+        }
+    }
 }
 
-size_t gemv_lds_bytes(int dt, int64_t K, int gs)
+size_t gemv_lds_bytes(int dt, int64_t K, int gs, int hs)
 {
-    if (dt == DT_F32) return (size_t)K * 4;
-    return (size_t)K + (size_t)(K / gs) * 4;
+    return gemv_input_bytes(dt, K, gs) + (size_t)hs * 4;
 }
 
 template <int DT, int PRO, int EPI, int RPW, int U, int NC, bool DBG>
 static hipError_t launch_t(const GemvParams& p, int blocks, hipStream_t s)
 {
-    const size_t lds = gemv_lds_bytes(DT, p.K, p.gs);
-    hipLaunchKernelGGL((gemv_kernel<DT, PRO, EPI, RPW, U, NC, DBG>), dim3((unsigned)blocks),
+    constexpr int NBUF = 2;
+    const size_t lds = gemv_lds_bytes(DT, p.K, p.gs, EPI == EPI_QKV ? p.hs : 0);
+    hipLaunchKernelGGL((gemv_kernel<DT, PRO, EPI, RPW, U, NC, NBUF, DBG>), dim3((unsigned)blocks),
                        dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }
 
-// Launch shape: RPW rows per tile, U loads per row per chunk, and the grid.
-// Every wave gets a contiguous 1/nw share of the tiles; the grid is capped at
-// max_blocks workgroups and never exceeds one tile per wave. NC (RMSNorm
-// prologues only) is the smallest register budget that holds the input.
-template <int DT, int PRO, int EPI, bool DBG>
-static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t s)
+// NC: the smallest register budget holding this thread's share of the input
+// (fp32: float4 chunks; Q8_0: 16-value chunks; 0 = batched late loads)
+template <int DT, int PRO, int EPI, int RPW, int U, bool DBG>
+static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s)
 {
-    constexpr int RPW = DT == DT_F32 ? 2 : 4;
-    constexpr int U = DT == DT_F32 ? 4 : 2;
     const int64_t tiles = (p.M + RPW - 1) / RPW;
     int64_t blocks = (tiles + kWaves - 1) / kWaves;
     if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
     if (blocks < 1) blocks = 1;
     const int64_t per_thread = DT == DT_F32 ? (p.K / 4 + kThreads - 1) / kThreads
                                             : (p.K / 16 + kThreads - 1) / kThreads;
-    if (PRO == PRO_PLAIN || per_thread <= 1)
-        return launch_t<DT, PRO, EPI, RPW, U, 1, DBG>(p, (int)blocks, s);
-    if (per_thread <= 2) return launch_t<DT, PRO, EPI, RPW, U, 2, DBG>(p, (int)blocks, s);
-    if (per_thread <= 4) return launch_t<DT, PRO, EPI, RPW, U, 4, DBG>(p, (int)blocks, s);
-    if (DT == DT_F32 && per_thread <= 16)
-        return launch_t<DT, PRO, EPI, RPW, U, 16, DBG>(p, (int)blocks, s);
-    return hipErrorInvalidValue;
+    const int b = (int)blocks;
+    if (per_thread <= 1) return launch_t<DT, PRO, EPI, RPW, U, 1, DBG>(p, b, s);
+    if (per_thread <= 2) return launch_t<DT, PRO, EPI, RPW, U, 2, DBG>(p, b, s);
+    if (per_thread <= 4) return launch_t<DT, PRO, EPI, RPW, U, 4, DBG>(p, b, s);
+    if constexpr (DT == DT_F32) {
+        if (per_thread <= 16) return launch_t<DT, PRO, EPI, RPW, U, 16, DBG>(p, b, s);
+        return hipErrorInvalidValue;
+    } else {
+        if (PRO == PRO_PLAIN) return launch_t<DT, PRO, EPI, RPW, U, 0, DBG>(p, b, s);
+        return hipErrorInvalidValue;  // RMSNorm inputs longer than 16384
+    }
+}
+
+// Launch shape: RPW rows per tile and U 16-byte loads per row per chunk
+// (fp32), or U = gs/16 loads per group (Q8_0); every wave gets a contiguous
+// share of the tiles; the grid is capped at max_blocks workgroups.
+// Measured on MI355X (7B shapes, back-to-back launches): two chunks in the
+// ring beat three or four (fewer registers, more waves); Q8_0 rows are best
+// one per tile when the matrix gives a wave fewer than three two-row tiles
+// (output projection, w2), two per tile otherwise. Epilogues that combine a
+// row pair (RoPE, SwiGLU) always get an even number of rows per tile.
+template <int DT, int PRO, int EPI, bool DBG>
+static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t s)
+{
+    if constexpr (DT == DT_F32) {
+        return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s);
+    } else {
+        const int64_t waves = (int64_t)(max_blocks > 0 ? max_blocks : 512) * kWaves;
+        switch (p.gs) {
+        case 16: return launch_nc<DT, PRO, EPI, 8, 1, DBG>(p, max_blocks, s);
+        case 32: return launch_nc<DT, PRO, EPI, 4, 2, DBG>(p, max_blocks, s);
+        case 64:
+            // the q/k/v and w1/w3 epilogues work on row pairs: RPW stays even
+            if constexpr (EPI != EPI_QKV && EPI != EPI_SWIGLU)
+                if (p.M < 6 * waves) return launch_nc<DT, PRO, EPI, 1, 4, DBG>(p, max_blocks, s);
+            return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s);
+        case 128: return launch_nc<DT, PRO, EPI, 1, 8, DBG>(p, max_blocks, s);
+        case 256: return launch_nc<DT, PRO, EPI, 1, 16, DBG>(p, max_blocks, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
 }
 
 hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_blocks,

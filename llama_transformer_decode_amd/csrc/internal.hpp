@@ -9,6 +9,14 @@ namespace l2d {
 
 enum Dt { DT_F32 = 0, DT_Q8 = 1 };
 
+// The classifier's argmax is kept in kArgmaxSlots packed 64-bit slots per
+// step parity (pos & 1), each on its own 128-byte line, so that workgroups
+// finishing together do not serialise on one atomic; the step's argmax is
+// the maximum over the slots.
+constexpr int kArgmaxSlots = 64;
+constexpr int kArgmaxStride = 16;  // u64 per slot
+constexpr int kArgmaxWords = 2 * kArgmaxSlots * kArgmaxStride;
+
 // GEMV input-vector preparation (the "prologue", run by every workgroup into
 // its LDS): PRO_PLAIN takes x as is; PRO_NORM applies RMSNorm with gain.
 enum Pro { PRO_PLAIN = 0, PRO_NORM = 1 };
@@ -38,7 +46,7 @@ struct GemvParams {
     const float* freqs;   // [hs/2] RoPE frequencies
     const int32_t* step;  // device {token, pos}
     // EPI_LOGITS
-    unsigned long long* argmax;  // two slots, written at [pos & 1]
+    unsigned long long* argmax;  // [2][kArgmaxSlots][kArgmaxStride], parity pos & 1
     // diagnostics
     int32_t* group_dots;  // [M][K/gs] exact int32 group dots (Q8_0, test hook)
     int8_t* trace_q;      // workgroup 0 copies its quantised input here
@@ -48,8 +56,9 @@ struct GemvParams {
 hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_blocks,
                        hipStream_t s);
 
-// dynamic LDS bytes the GEMV needs for an input of K values
-size_t gemv_lds_bytes(int dt, int64_t K, int gs);
+// dynamic LDS bytes the GEMV needs for an input of K values (+ the RoPE
+// table of a head of hs values for the q/k/v epilogue, else hs = 0)
+size_t gemv_lds_bytes(int dt, int64_t K, int gs, int hs);
 
 struct AttnParams {
     const float* q;    // [n_heads * hs]
@@ -58,7 +67,6 @@ struct AttnParams {
     float* o;          // [n_heads * hs]
     double* part_o;    // [nkv][nsplit][G][hs]
     double* part_ml;   // [nkv][nsplit][G][2]
-    int32_t* counters; // [nkv], zero between steps
     const int32_t* step;
     int32_t S, nkv, hs, kvd, G, nsplit;
 };
@@ -79,6 +87,9 @@ struct BeginParams {
 };
 
 hipError_t launch_begin(const BeginParams& p, hipStream_t s);
+
+hipError_t launch_permute_q8(const int8_t* src, int8_t* dst, int64_t rows, int64_t K, int32_t gs,
+                             int64_t blk, int64_t stride, int64_t off, hipStream_t st);
 
 hipError_t launch_quantize(const float* x, int64_t n, int32_t gs, int8_t* q, float* s,
                            hipStream_t st);

@@ -57,10 +57,9 @@ struct l2d_ctx {
     float* hb = nullptr;      // [h]
     float* logits = nullptr;  // [V]
     int32_t* step = nullptr;  // {token, pos}
-    unsigned long long* argmax = nullptr;  // [2]
+    unsigned long long* argmax = nullptr;  // [2][kArgmaxSlots][kArgmaxStride]
     double* part_o = nullptr;
     double* part_ml = nullptr;
-    int32_t* counters = nullptr;
     int nsplit = 0;
 
     hipGraph_t graph = nullptr;

@@ -16,7 +16,20 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     int32_t token = p.token;
     if (p.greedy) {
-        const unsigned long long prev = p.argmax[(p.pos - 1) & 1];
+        // maximum over the previous step's argmax slots (wave 0), broadcast
+        __shared__ unsigned long long prev;
+        if (threadIdx.x < 64) {
+            const int q = ((p.pos - 1) & 1) * kArgmaxSlots;
+            unsigned long long v = threadIdx.x < kArgmaxSlots
+                                       ? p.argmax[(size_t)(q + threadIdx.x) * kArgmaxStride]
+                                       : 0ull;
+            for (int m = 32; m >= 1; m >>= 1) {
+                const unsigned long long o = __shfl_xor(v, m, 64);
+                v = o > v ? o : v;
+            }
+            if (threadIdx.x == 0) prev = v;
+        }
+        __syncthreads();
         token = (int32_t)(0xFFFFFFFFu - (uint32_t)(prev & 0xFFFFFFFFull));
         if (token < 0 || token >= p.vocab) token = 0;
     }
@@ -25,21 +38,52 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
         if (p.dtype == DT_F32) {
             p.x[i] = ((const float*)p.emb)[off];
         } else {
-            const int8_t c = ((const int8_t*)p.emb)[off];
+            // codes are stored group-interleaved within the row
+            const int8_t c = ((const int8_t*)p.emb)[(int64_t)token * p.d + q8_perm_offset(i, p.d, p.gs)];
             p.x[i] = (float)((double)c * (double)p.emb_s[off / p.gs]);
         }
     }
     if (i == 0) {
         p.step[0] = token;
         p.step[1] = p.pos;
-        p.argmax[p.pos & 1] = 0ull;
     }
+    if (blockIdx.x == 0 && threadIdx.x < kArgmaxSlots)
+        p.argmax[((size_t)(p.pos & 1) * kArgmaxSlots + threadIdx.x) * kArgmaxStride] = 0ull;
 }
 
 hipError_t launch_begin(const BeginParams& p, hipStream_t s)
 {
     const unsigned blocks = (unsigned)((p.d + 255) / 256);
     hipLaunchKernelGGL(begin_step_kernel, dim3(blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// Q8_0 codes from the plain row-major layout into the device layout: every
+// row's codes are group-interleaved (q8_perm_offset), and source row r lands
+// at destination row (r / blk) * stride + off + r % blk, which places q, k, v
+// rows of a layer side by side and interleaves w1 / w3 rows.
+__global__ __launch_bounds__(256) void permute_q8_kernel(const int8_t* src, int8_t* dst, int64_t rows,
+                                                        int64_t K, int32_t gs, int64_t blk,
+                                                        int64_t stride, int64_t off)
+{
+    const int64_t nq = K / 16;
+    const int64_t total = rows * nq;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / nq, c = i % nq;
+        const int64_t drow = (r / blk) * stride + off + r % blk;
+        *(i32x4*)(dst + drow * K + q8_perm_offset(16 * c, K, gs)) = *(const i32x4*)(src + r * K + 16 * c);
+    }
+}
+
+hipError_t launch_permute_q8(const int8_t* src, int8_t* dst, int64_t rows, int64_t K, int32_t gs,
+                             int64_t blk, int64_t stride, int64_t off, hipStream_t st)
+{
+    int64_t blocks = (rows * (K / 16) + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(permute_q8_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, dst, rows, K,
+                       gs, blk, stride, off);
     return hipGetLastError();
 }
 
