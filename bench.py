@@ -18,6 +18,7 @@ position; per-position and fp32 figures ride along under "detail".
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+GEMV_SRC = os.path.join(ROOT, "llama_transformer_decode_amd", "csrc", "gemv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_w13_7B_q8_0.txt")
 
 
 def log(*a):
@@ -72,14 +75,34 @@ def time_replays(ctx, token: int, pos: int, steps: int, warmup: int, torch) -> f
 
 def kernel_times(ctx, token: int, pos: int, reps: int) -> dict:
     """Average duration (s) of each kernel class of the step, from HIP events
-    recorded around every launch on the context's stream (kernel-by-kernel
-    launches, same kernels and grids as the graph)."""
+    stamped at every kernel's own start and end on the context's stream
+    (kernel-by-kernel launches, same kernels and grids as the graph)."""
     return ctx.kernel_profile(token, pos, reps)
 
 
-def decode_to(ctx, positions, torch):
+def measured_traffic():
+    """HBM bytes per launch of the w1/w3 GEMV from the committed rocprofv3
+    counter summary, or None when the kernel source changed since then."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        digest = hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()
+        if fields.get("gemv_source_sha256") != digest:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def decode_to(ctx, positions, torch, fill=True):
     """Greedy decode from pos 0 through max(positions); returns the token fed
-    at each requested position."""
+    at each requested position. Without fill the cache stays zero and the
+    replays run at the requested positions directly (same bytes moved)."""
+    if not fill:
+        return {p: 1 for p in positions}
     last = max(positions)
     fed = {}
     ctx.forward(1, 0)
@@ -96,7 +119,7 @@ def decode_to(ctx, positions, torch):
     return fed
 
 
-def bench_dtype(cfg, dtype, positions, steps, warmup, torch, l2d, synth):
+def bench_dtype(cfg, dtype, positions, steps, warmup, torch, l2d, synth, fill=True):
     t = time.time()
     blob = synth.make_blob(cfg, dtype)
     log(f"[bench] {cfg.name} dtype={'q8_0' if dtype else 'fp32'}: blob {blob.size / 1e9:.2f} GB "
@@ -106,8 +129,9 @@ def bench_dtype(cfg, dtype, positions, steps, warmup, torch, l2d, synth):
     del blob
     log(f"[bench] upload + graph capture {time.time() - t:.1f}s")
     t = time.time()
-    fed = decode_to(ctx, positions, torch)
-    log(f"[bench] greedy decode 0..{max(positions)} in {time.time() - t:.1f}s")
+    fed = decode_to(ctx, positions, torch, fill)
+    if fill:
+        log(f"[bench] greedy decode 0..{max(positions)} in {time.time() - t:.1f}s")
     res = {}
     for p in positions:
         sec = time_replays(ctx, fed[p], p, steps, warmup, torch)
@@ -153,6 +177,10 @@ def main():
     ap.add_argument("--dtypes", default="q8_0,fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-fill", action="store_true",
+                    help="skip the greedy decode that fills the cache (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
@@ -165,6 +193,13 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
+        del a, b
     cfg = synth.CONFIGS[args.config]
     positions = sorted({int(p) for p in args.positions.split(",")} | {args.headline_pos})
     dtypes = [0 if d.strip() == "fp32" else 1 for d in args.dtypes.split(",")]
@@ -172,7 +207,8 @@ def main():
     head = None
     for dt in dtypes:
         name = "q8_0" if dt else "fp32"
-        ctx, fed, res = bench_dtype(cfg, dt, positions, args.steps, args.warmup, torch, l2d, synth)
+        ctx, fed, res = bench_dtype(cfg, dt, positions, args.steps, args.warmup, torch, l2d, synth,
+                                    not args.no_fill)
         # per-kernel HIP-event timing at the headline position
         kt = kernel_times(ctx, fed[args.headline_pos], args.headline_pos, 3)
         b = step_bytes(cfg, dt, args.headline_pos)
@@ -215,7 +251,8 @@ def main():
         "hbm_step_frac": r["step_gbs"] / PEAK_HBM_GBS,
         "roofline": {"bound": "hbm", "kernel": "gemv w1/w3 + SwiGLU",
                      "achieved": w13, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": w13 / PEAK_HBM_GBS, "traffic": None},
+                     "frac": w13 / PEAK_HBM_GBS,
+                     "traffic": measured_traffic() if dt == 1 and cfg.name == "7B" else None},
         "detail": detail,
     }
     if not args.no_cpu_baseline:

@@ -25,6 +25,8 @@
 // Workgroups beyond the active ranges exit at once: the grid is sized once,
 // pos is read from device memory, and the same launch serves every position
 // of a captured graph.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -377,21 +379,33 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p)
     if (sub == 0 && e < n_out) p.o[e] = (float)(O / L);
 }
 
-hipError_t launch_attention(const AttnParams& p, hipStream_t s)
+hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     const size_t lds = attention_lds_bytes(p.G, p.hs, 0);
     const dim3 grid(p.nkv, p.nsplit);
+    hipEvent_t e0 = ev ? ev->start : nullptr;
+#define L2D_ATT(GG)                                                                                \
+    if (ev)                                                                                        \
+        hipExtLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), (uint32_t)lds, s, e0,   \
+                              nullptr, 0u, p);                                                     \
+    else                                                                                           \
+        hipLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), lds, s, p);
     switch (p.G) {
-    case 1: hipLaunchKernelGGL(attention_kernel<1>, grid, dim3(kAThreads), lds, s, p); break;
-    case 2: hipLaunchKernelGGL(attention_kernel<2>, grid, dim3(kAThreads), lds, s, p); break;
-    case 4: hipLaunchKernelGGL(attention_kernel<4>, grid, dim3(kAThreads), lds, s, p); break;
-    case 8: hipLaunchKernelGGL(attention_kernel<8>, grid, dim3(kAThreads), lds, s, p); break;
+    case 1: L2D_ATT(1) break;
+    case 2: L2D_ATT(2) break;
+    case 4: L2D_ATT(4) break;
+    case 8: L2D_ATT(8) break;
     default: return hipErrorInvalidValue;
     }
+#undef L2D_ATT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)p.nkv * p.G * p.hs * 4;
-    hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+    const dim3 mgrid((unsigned)((threads + 255) / 256));
+    if (ev)
+        hipExtLaunchKernelGGL(attention_merge_kernel, mgrid, dim3(256), 0u, s, nullptr, ev->stop, 0u, p);
+    else
+        hipLaunchKernelGGL(attention_merge_kernel, mgrid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

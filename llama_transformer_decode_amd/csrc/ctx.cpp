@@ -151,14 +151,15 @@ void release(l2d_ctx* ctx)
 
 size_t elt(int dt) { return dt == DT_F32 ? 4 : 1; }
 
-// HIP events around each launch of the kernel-by-kernel step, by kernel class
+// Start/stop events of each launch of the kernel-by-kernel step, by kernel
+// class; the events are stamped at the kernel's own start and end.
 struct KernelTimer {
     std::vector<hipEvent_t> ev;
     std::vector<int> cls;
     size_t used = 0;
-    hipStream_t s = nullptr;
+    LaunchEvents cur;
 
-    hipError_t mark(int c)
+    hipError_t next(int c)
     {
         if (used + 2 > ev.size()) {
             for (int i = 0; i < 2; i++) {
@@ -170,9 +171,11 @@ struct KernelTimer {
             cls.resize(ev.size() / 2);
         }
         cls[used / 2] = c;
-        return hipEventRecord(ev[used], s);
+        cur.start = ev[used];
+        cur.stop = ev[used + 1];
+        used += 2;
+        return hipSuccess;
     }
-    hipError_t done() { hipError_t r = hipEventRecord(ev[used + 1], s); used += 2; return r; }
     ~KernelTimer()
     {
         for (hipEvent_t e : ev) hipEventDestroy(e);
@@ -216,9 +219,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.freqs = ctx->freqs;
         p.trace_q = tr ? ctx->trace_q[0] : nullptr;
         p.trace_s = tr ? ctx->trace_s[0] : nullptr;
-        if (kt) HIP_TRY(ctx, kt->mark(KC_QKV));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_QKV, p, ctx->max_blocks, s));
-        if (kt) HIP_TRY(ctx, kt->done());
+        if (kt) HIP_TRY(ctx, kt->next(KC_QKV));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_QKV, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
 
         // attention over positions 0..pos
         AttnParams a;
@@ -235,9 +237,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         a.kvd = (int32_t)kvd;
         a.G = (int32_t)ctx->G;
         a.nsplit = ctx->nsplit;
-        if (kt) HIP_TRY(ctx, kt->mark(KC_ATTN));
-        HIP_TRY(ctx, launch_attention(a, s));
-        if (kt) HIP_TRY(ctx, kt->done());
+        if (kt) HIP_TRY(ctx, kt->next(KC_ATTN));
+        HIP_TRY(ctx, launch_attention(a, s, kt ? &kt->cur : nullptr));
 
         // output projection + residual
         p.W = (const uint8_t*)ctx->wo + (size_t)(l * d * d) * es;
@@ -249,9 +250,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.out = ctx->x;
         p.trace_q = tr ? ctx->trace_q[1] : nullptr;
         p.trace_s = tr ? ctx->trace_s[1] : nullptr;
-        if (kt) HIP_TRY(ctx, kt->mark(KC_WO));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s));
-        if (kt) HIP_TRY(ctx, kt->done());
+        if (kt) HIP_TRY(ctx, kt->next(KC_WO));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
 
         // RMSNorm -> w1/w3 matvec -> SwiGLU
         p.W = (const uint8_t*)ctx->w13 + (size_t)(l * 2 * h * d) * es;
@@ -263,9 +263,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.out = ctx->hb;
         p.trace_q = tr ? ctx->trace_q[2] : nullptr;
         p.trace_s = tr ? ctx->trace_s[2] : nullptr;
-        if (kt) HIP_TRY(ctx, kt->mark(KC_W13));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s));
-        if (kt) HIP_TRY(ctx, kt->done());
+        if (kt) HIP_TRY(ctx, kt->next(KC_W13));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
 
         // w2 matvec + residual
         p.W = (const uint8_t*)ctx->w2 + (size_t)(l * d * h) * es;
@@ -277,9 +276,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.out = ctx->x;
         p.trace_q = tr ? ctx->trace_q[3] : nullptr;
         p.trace_s = tr ? ctx->trace_s[3] : nullptr;
-        if (kt) HIP_TRY(ctx, kt->mark(KC_W2));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s));
-        if (kt) HIP_TRY(ctx, kt->done());
+        if (kt) HIP_TRY(ctx, kt->next(KC_W2));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
     }
     // final RMSNorm -> classifier -> argmax
     GemvParams p;
@@ -295,9 +293,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
     p.gain = ctx->rms_final;
     p.out = ctx->logits;
     p.argmax = ctx->argmax;
-    if (kt) HIP_TRY(ctx, kt->mark(KC_CLS));
-    HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_LOGITS, p, ctx->max_blocks, s));
-    if (kt) HIP_TRY(ctx, kt->done());
+    if (kt) HIP_TRY(ctx, kt->next(KC_CLS));
+    HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_LOGITS, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
     return L2D_OK;
 }
 
@@ -501,7 +498,8 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     return capture(ctx);
 }
 
-hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
+hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy,
+                 const LaunchEvents* ev = nullptr)
 {
     BeginParams b;
     b.emb = ctx->emb;
@@ -516,7 +514,7 @@ hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
     b.token = token;
     b.pos = pos;
     b.greedy = greedy ? 1 : 0;
-    return launch_begin(b, ctx->stream);
+    return launch_begin(b, ctx->stream, ev);
 }
 
 const float* forward_impl(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
@@ -733,11 +731,9 @@ int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, dou
     if (pos < 0 || pos >= ctx->S || token < 0 || token >= ctx->V)
         return fail(ctx, L2D_EINVAL, "profile_step: token or pos out of range");
     KernelTimer kt;
-    kt.s = ctx->stream;
     for (int r = 0; r < reps; r++) {
-        HIP_TRY(ctx, kt.mark(KC_BEGIN));
-        HIP_TRY(ctx, begin(ctx, token, pos, false));
-        HIP_TRY(ctx, kt.done());
+        HIP_TRY(ctx, kt.next(KC_BEGIN));
+        HIP_TRY(ctx, begin(ctx, token, pos, false, &kt.cur));
         int rc = enqueue_layers(ctx, false, &kt);
         if (rc != L2D_OK) return rc;
     }

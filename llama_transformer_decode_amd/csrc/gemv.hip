@@ -28,6 +28,8 @@
 //   epilogue  a DPP wave sum leaves each row's total in lane 63, which
 //             finishes the tile: store, residual add, RoPE + KV-cache write,
 //             SwiGLU, or classifier + packed argmax.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device.hpp"
@@ -532,19 +534,23 @@ size_t gemv_lds_bytes(int dt, int64_t K, int gs, int hs)
 }
 
 template <int DT, int PRO, int EPI, int RPW, int U, int NC, bool DBG>
-static hipError_t launch_t(const GemvParams& p, int blocks, hipStream_t s)
+static hipError_t launch_t(const GemvParams& p, int blocks, hipStream_t s, const LaunchEvents* ev)
 {
     constexpr int NBUF = 2;
     const size_t lds = gemv_lds_bytes(DT, p.K, p.gs, EPI == EPI_QKV ? p.hs : 0);
-    hipLaunchKernelGGL((gemv_kernel<DT, PRO, EPI, RPW, U, NC, NBUF, DBG>), dim3((unsigned)blocks),
-                       dim3(kThreads), lds, s, p);
+    if (ev)
+        hipExtLaunchKernelGGL((gemv_kernel<DT, PRO, EPI, RPW, U, NC, NBUF, DBG>), dim3((unsigned)blocks),
+                              dim3(kThreads), (uint32_t)lds, s, ev->start, ev->stop, 0u, p);
+    else
+        hipLaunchKernelGGL((gemv_kernel<DT, PRO, EPI, RPW, U, NC, NBUF, DBG>), dim3((unsigned)blocks),
+                           dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }
 
 // NC: the smallest register budget holding this thread's share of the input
 // (fp32: float4 chunks; Q8_0: 16-value chunks; 0 = batched late loads)
 template <int DT, int PRO, int EPI, int RPW, int U, bool DBG>
-static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s)
+static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s, const LaunchEvents* ev)
 {
     const int64_t tiles = (p.M + RPW - 1) / RPW;
     int64_t blocks = (tiles + kWaves - 1) / kWaves;
@@ -553,14 +559,14 @@ static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s)
     const int64_t per_thread = DT == DT_F32 ? (p.K / 4 + kThreads - 1) / kThreads
                                             : (p.K / 16 + kThreads - 1) / kThreads;
     const int b = (int)blocks;
-    if (per_thread <= 1) return launch_t<DT, PRO, EPI, RPW, U, 1, DBG>(p, b, s);
-    if (per_thread <= 2) return launch_t<DT, PRO, EPI, RPW, U, 2, DBG>(p, b, s);
-    if (per_thread <= 4) return launch_t<DT, PRO, EPI, RPW, U, 4, DBG>(p, b, s);
+    if (per_thread <= 1) return launch_t<DT, PRO, EPI, RPW, U, 1, DBG>(p, b, s, ev);
+    if (per_thread <= 2) return launch_t<DT, PRO, EPI, RPW, U, 2, DBG>(p, b, s, ev);
+    if (per_thread <= 4) return launch_t<DT, PRO, EPI, RPW, U, 4, DBG>(p, b, s, ev);
     if constexpr (DT == DT_F32) {
-        if (per_thread <= 16) return launch_t<DT, PRO, EPI, RPW, U, 16, DBG>(p, b, s);
+        if (per_thread <= 16) return launch_t<DT, PRO, EPI, RPW, U, 16, DBG>(p, b, s, ev);
         return hipErrorInvalidValue;
     } else {
-        if (PRO == PRO_PLAIN) return launch_t<DT, PRO, EPI, RPW, U, 0, DBG>(p, b, s);
+        if (PRO == PRO_PLAIN) return launch_t<DT, PRO, EPI, RPW, U, 0, DBG>(p, b, s, ev);
         return hipErrorInvalidValue;  // RMSNorm inputs longer than 16384
     }
 }
@@ -574,35 +580,35 @@ static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s)
 // (output projection, w2), two per tile otherwise. Epilogues that combine a
 // row pair (RoPE, SwiGLU) always get an even number of rows per tile.
 template <int DT, int PRO, int EPI, bool DBG>
-static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t s)
+static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t s, const LaunchEvents* ev)
 {
     if constexpr (DT == DT_F32) {
-        return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s);
+        return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s, ev);
     } else {
         const int64_t waves = (int64_t)(max_blocks > 0 ? max_blocks : 512) * kWaves;
         switch (p.gs) {
-        case 16: return launch_nc<DT, PRO, EPI, 8, 1, DBG>(p, max_blocks, s);
-        case 32: return launch_nc<DT, PRO, EPI, 4, 2, DBG>(p, max_blocks, s);
+        case 16: return launch_nc<DT, PRO, EPI, 8, 1, DBG>(p, max_blocks, s, ev);
+        case 32: return launch_nc<DT, PRO, EPI, 4, 2, DBG>(p, max_blocks, s, ev);
         case 64:
             // the q/k/v and w1/w3 epilogues work on row pairs: RPW stays even
             if constexpr (EPI != EPI_QKV && EPI != EPI_SWIGLU)
-                if (p.M < 6 * waves) return launch_nc<DT, PRO, EPI, 1, 4, DBG>(p, max_blocks, s);
-            return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s);
-        case 128: return launch_nc<DT, PRO, EPI, 1, 8, DBG>(p, max_blocks, s);
-        case 256: return launch_nc<DT, PRO, EPI, 1, 16, DBG>(p, max_blocks, s);
+                if (p.M < 6 * waves) return launch_nc<DT, PRO, EPI, 1, 4, DBG>(p, max_blocks, s, ev);
+            return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s, ev);
+        case 128: return launch_nc<DT, PRO, EPI, 1, 8, DBG>(p, max_blocks, s, ev);
+        case 256: return launch_nc<DT, PRO, EPI, 1, 16, DBG>(p, max_blocks, s, ev);
         default: return hipErrorInvalidValue;
         }
     }
 }
 
 hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_blocks,
-                       hipStream_t s)
+                       hipStream_t s, const LaunchEvents* ev)
 {
 #define L2D_CASE(D, P, E)                                                  \
     if (dt == D && pro == P && epi == E) {                                 \
         if (D == DT_Q8 && p.group_dots != nullptr)                         \
-            return launch_shape<D, P, E, true>(p, max_blocks, s);          \
-        return launch_shape<D, P, E, false>(p, max_blocks, s);             \
+            return launch_shape<D, P, E, true>(p, max_blocks, s, ev);      \
+        return launch_shape<D, P, E, false>(p, max_blocks, s, ev);         \
     }
     L2D_CASE(DT_F32, PRO_NORM, EPI_QKV)
     L2D_CASE(DT_F32, PRO_PLAIN, EPI_RESID)

@@ -53,8 +53,15 @@ struct GemvParams {
     float* trace_s;
 };
 
+// Optional kernel timing: events stamped at the kernel's own start and end
+// (hipExtLaunchKernel), so durations match a hardware kernel trace.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_blocks,
-                       hipStream_t s);
+                       hipStream_t s, const LaunchEvents* ev = nullptr);
 
 // dynamic LDS bytes the GEMV needs for an input of K values (+ the RoPE
 // table of a head of hs values for the q/k/v epilogue, else hs = 0)
@@ -71,7 +78,7 @@ struct AttnParams {
     int32_t S, nkv, hs, kvd, G, nsplit;
 };
 
-hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEvents* ev = nullptr);
 size_t attention_lds_bytes(int G, int hs, int unused);
 bool attention_supported(int G, int hs);
 int attention_positions_per_subchunk(int hs);
@@ -86,7 +93,7 @@ struct BeginParams {
     int32_t token, pos, greedy;
 };
 
-hipError_t launch_begin(const BeginParams& p, hipStream_t s);
+hipError_t launch_begin(const BeginParams& p, hipStream_t s, const LaunchEvents* ev = nullptr);
 
 hipError_t launch_permute_q8(const int8_t* src, int8_t* dst, int64_t rows, int64_t K, int32_t gs,
                              int64_t blk, int64_t stride, int64_t off, hipStream_t st);

@@ -1,5 +1,7 @@
 // step.hip - the first kernel of a decode step, and the standalone Q8_0
 // quantiser.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -51,10 +53,13 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
         p.argmax[((size_t)(p.pos & 1) * kArgmaxSlots + threadIdx.x) * kArgmaxStride] = 0ull;
 }
 
-hipError_t launch_begin(const BeginParams& p, hipStream_t s)
+hipError_t launch_begin(const BeginParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     const unsigned blocks = (unsigned)((p.d + 255) / 256);
-    hipLaunchKernelGGL(begin_step_kernel, dim3(blocks), dim3(256), 0, s, p);
+    if (ev)
+        hipExtLaunchKernelGGL(begin_step_kernel, dim3(blocks), dim3(256), 0u, s, ev->start, ev->stop, 0u, p);
+    else
+        hipLaunchKernelGGL(begin_step_kernel, dim3(blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
