@@ -208,8 +208,30 @@ void* l2d_stream(l2d_ctx* ctx);
  */
 int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, double* avg_seconds);
 
-/* 1: replay the captured graph (default); 0: launch the step's kernels one by one. */
+/* 1: replay the captured graph (default); 0: launch the step's kernels one by one.
+ * Applies when the persistent step kernel is off (l2d_use_persistent). */
 int l2d_use_graph(l2d_ctx* ctx, int32_t enable);
+
+/*
+ * The same step as one persistent kernel: a single cooperative launch per
+ * l2d_forward / l2d_forward_greedy, its phases separated by grid barriers
+ * (the toy forward pass of the mht18 essay, section 2.3, computed as above;
+ * results agree with the per-phase kernels within fp64 summation order).
+ * Available only when the environment variable L2D_PERSISTENT=1 is set at
+ * l2d_init (its first run on MI355X faulted and the cause is not yet found),
+ * for Q8_0 with group size 64 or fp32, head_size <= 256, at most 8 query
+ * heads per kv head, and a device that can hold one 512-thread workgroup per
+ * CU with the step's LDS. enable = 1 where it is not available returns
+ * L2D_EINVAL. A grid barrier that waits beyond a bounded
+ * number of polls (seconds) gives up: every workgroup then ends, and the next
+ * l2d_sync, l2d_last_token or l2d_read_logits returns L2D_EHIP and resets the
+ * barrier state. Tracing (l2d_trace_layer) uses the per-phase kernels.
+ */
+int l2d_use_persistent(l2d_ctx* ctx, int32_t enable);
+
+/* 1 when l2d_forward runs the persistent step kernel, 0 when the per-phase
+ * kernels run, L2D_EINVAL for a null context. */
+int l2d_persistent(const l2d_ctx* ctx);
 
 #ifdef __cplusplus
 }

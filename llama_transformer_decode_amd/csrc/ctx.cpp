@@ -298,6 +298,8 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
     return L2D_OK;
 }
 
+int setup_mega(l2d_ctx* ctx, int cus);
+
 int capture(l2d_ctx* ctx)
 {
     HIP_TRY(ctx, hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeThreadLocal));
@@ -495,7 +497,125 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, (size_t)kArgmaxWords * 8, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    return capture(ctx);
+    rc = capture(ctx);
+    if (rc != L2D_OK) return rc;
+    return setup_mega(ctx, cus);
+}
+
+// The persistent step kernel: one workgroup per CU, all resident
+// (cooperative launch), LDS for the largest matvec input or attention
+// range. It is built but not enabled: its first run on MI355X ended in a
+// memory access fault whose cause has not been found, so the library runs
+// the captured graph of per-phase kernels unless L2D_PERSISTENT=1 is set in
+// the environment at l2d_init.
+int setup_mega(l2d_ctx* ctx, int cus)
+{
+    ctx->mega_ok = false;
+    ctx->use_mega = false;
+    const char* e = getenv("L2D_PERSISTENT");
+    if (!e || atoi(e) != 1) return L2D_OK;
+    if (!mega_supported(ctx->dt, ctx->gs, ctx->d, ctx->h, (int)ctx->G, (int)ctx->hs)) return L2D_OK;
+    int coop = 0;
+    HIP_TRY(ctx, hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, ctx->device));
+    if (!coop) return L2D_OK;
+    const size_t lds = mega_lds_bytes(ctx->dt, ctx->d, ctx->h, (int)ctx->G, (int)ctx->hs);
+    if (mega_blocks_per_cu(ctx->dt, (int)ctx->G, lds) < 1) return L2D_OK;
+    ALLOC(ctx->msync, sizeof(MegaSync));
+    ALLOC(ctx->head_ctr, (size_t)ctx->nkv * 32 * 4);
+    const size_t nparts = (size_t)ctx->nkv * kMegaSplits * ctx->G;
+    ALLOC(ctx->mpart_o, nparts * ctx->hs * 8);
+    ALLOC(ctx->mpart_ml, nparts * 2 * 8);
+    HIP_TRY(ctx, hipMemsetAsync(ctx->msync, 0, sizeof(MegaSync), ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->head_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->mega_grid = cus;
+    ctx->mega_lds = lds;
+    ctx->mega_epoch = 0;
+    ctx->mega_ok = true;
+    ctx->use_mega = true;
+    return L2D_OK;
+}
+
+// One launch of the persistent step kernel for (token, pos).
+hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
+{
+    const uint32_t nb = mega_barriers((int)ctx->L);
+    if (ctx->mega_epoch > (1u << 25) - nb) {
+        // the arrival counters count up across launches: restart them from zero
+        hipError_t e = hipMemsetAsync(ctx->msync, 0, sizeof(MegaSync), ctx->stream);
+        if (e != hipSuccess) return e;
+        ctx->mega_epoch = 0;
+    }
+    MegaParams p;
+    memset(&p, 0, sizeof(p));
+    p.dt = ctx->dt;
+    p.gs = ctx->gs;
+    p.d = (int32_t)ctx->d;
+    p.h = (int32_t)ctx->h;
+    p.L = (int32_t)ctx->L;
+    p.nkv = (int32_t)ctx->nkv;
+    p.hs = (int32_t)ctx->hs;
+    p.kvd = (int32_t)ctx->kvd;
+    p.G = (int32_t)ctx->G;
+    p.V = (int32_t)ctx->V;
+    p.S = (int32_t)ctx->S;
+    p.eps = ctx->cfg.norm_eps;
+    p.emb = ctx->emb;
+    p.emb_s = ctx->emb_s;
+    p.wqkv = ctx->wqkv;
+    p.wqkv_s = ctx->wqkv_s;
+    p.wo = ctx->wo;
+    p.wo_s = ctx->wo_s;
+    p.w13 = ctx->w13;
+    p.w13_s = ctx->w13_s;
+    p.w2 = ctx->w2;
+    p.w2_s = ctx->w2_s;
+    p.wcls = ctx->wcls;
+    p.wcls_s = ctx->wcls_s;
+    p.rms_att = ctx->rms_att;
+    p.rms_ffn = ctx->rms_ffn;
+    p.rms_final = ctx->rms_final;
+    p.freqs = ctx->freqs;
+    p.kc = ctx->kc;
+    p.vc = ctx->vc;
+    p.x = ctx->x;
+    p.q = ctx->q;
+    p.o = ctx->o;
+    p.hb = ctx->hb;
+    p.logits = ctx->logits;
+    p.step = ctx->step;
+    p.argmax = ctx->argmax;
+    p.part_o = ctx->mpart_o;
+    p.part_ml = ctx->mpart_ml;
+    p.head_ctr = ctx->head_ctr;
+    p.sync = ctx->msync;
+    p.token = token;
+    p.pos = pos;
+    p.greedy = greedy ? 1 : 0;
+    p.epoch0 = ctx->mega_epoch;
+    hipError_t e = launch_mega(p, ctx->mega_grid, ctx->mega_lds, ctx->stream);
+    if (e == hipSuccess) {
+        ctx->mega_epoch += nb;
+        ctx->mega_pending = true;
+    }
+    return e;
+}
+
+// After a synchronisation: did a grid barrier of the step kernel give up?
+// Then the barrier state is reset and the error reported.
+int mega_check(l2d_ctx* ctx)
+{
+    if (!ctx->mega_pending) return L2D_OK;
+    uint32_t err = 0;
+    HIP_TRY(ctx, hipMemcpyAsync(&err, ctx->msync->err, 4, hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->mega_pending = false;
+    if (err == 0) return L2D_OK;
+    HIP_TRY(ctx, hipMemsetAsync(ctx->msync, 0, sizeof(MegaSync), ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->head_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->mega_epoch = 0;
+    return fail(ctx, L2D_EHIP, "step kernel: a grid barrier wait gave up; the step's results are invalid");
 }
 
 hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy,
@@ -535,12 +655,21 @@ const float* forward_impl(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
         fail(ctx, L2D_EINVAL, "forward_greedy: the previous step must be at pos - 1");
         return nullptr;
     }
+    const bool tracing = ctx->trace_layer >= 0;
+    if (ctx->use_mega && ctx->mega_ok && !tracing) {
+        hipError_t e = launch_step_kernel(ctx, token, pos, greedy);
+        if (e != hipSuccess) {
+            fail(ctx, L2D_EHIP, std::string("step kernel launch: ") + hipGetErrorString(e));
+            return nullptr;
+        }
+        ctx->last_pos = pos;
+        return ctx->logits;
+    }
     hipError_t e = begin(ctx, token, pos, greedy);
     if (e != hipSuccess) {
         fail(ctx, L2D_EHIP, std::string("begin_step launch: ") + hipGetErrorString(e));
         return nullptr;
     }
-    const bool tracing = ctx->trace_layer >= 0;
     if (ctx->use_graph && !tracing) {
         e = hipGraphLaunch(ctx->exec, ctx->stream);
         if (e != hipSuccess) {
@@ -589,7 +718,7 @@ int l2d_sync(l2d_ctx* ctx)
 {
     if (!ctx) return fail(nullptr, L2D_EINVAL, "sync: null context");
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    return L2D_OK;
+    return mega_check(ctx);
 }
 
 int l2d_last_token(l2d_ctx* ctx, int32_t* token)
@@ -600,6 +729,8 @@ int l2d_last_token(l2d_ctx* ctx, int32_t* token)
     HIP_TRY(ctx, hipMemcpyAsync(slots, ctx->argmax + (size_t)(ctx->last_pos & 1) * kArgmaxSlots * kArgmaxStride,
                                 sizeof(slots), hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    int rc = mega_check(ctx);
+    if (rc != L2D_OK) return rc;
     unsigned long long v = 0;
     for (int i = 0; i < kArgmaxSlots; i++)
         if (slots[i * kArgmaxStride] > v) v = slots[i * kArgmaxStride];
@@ -613,7 +744,7 @@ int l2d_read_logits(l2d_ctx* ctx, float* host_dst)
     HIP_TRY(ctx, hipMemcpyAsync(host_dst, ctx->logits, (size_t)ctx->V * 4, hipMemcpyDeviceToHost,
                                 ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    return L2D_OK;
+    return mega_check(ctx);
 }
 
 int l2d_quantize_q80(const float* x, int64_t n, int32_t gs, int8_t* q, float* s, void* stream)
@@ -749,6 +880,21 @@ int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, dou
     for (int c = 0; c < KC_COUNT; c++) avg_seconds[c] = cnt[c] ? sum[c] / cnt[c] : 0.0;
     ctx->last_pos = pos;
     return L2D_OK;
+}
+
+int l2d_use_persistent(l2d_ctx* ctx, int32_t enable)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "use_persistent: null context");
+    if (enable && !ctx->mega_ok)
+        return fail(ctx, L2D_EINVAL, "use_persistent: the persistent step kernel is not available for this model or device");
+    ctx->use_mega = enable != 0;
+    return L2D_OK;
+}
+
+int l2d_persistent(const l2d_ctx* ctx)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "persistent: null context");
+    return ctx->use_mega && ctx->mega_ok ? 1 : 0;
 }
 
 int l2d_use_graph(l2d_ctx* ctx, int32_t enable)

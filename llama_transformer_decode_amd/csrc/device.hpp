@@ -199,3 +199,95 @@ __host__ __device__ __forceinline__ int64_t q8_perm_offset(int64_t i, int64_t K,
 }
 
 }  // namespace l2d
+
+namespace l2d {
+
+// Device-scope coherent accesses, for values that one workgroup writes and
+// another reads within the same kernel launch (the step kernel's phases):
+// relaxed atomics at agent scope, which gfx950 executes with the sc1 cache
+// policy (stores reach the device coherence point before they complete,
+// loads do not hit a stale copy in a per-XCD cache).
+__device__ __forceinline__ float ld_dev(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ double ld_dev(const double* p)
+{
+    return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p)
+{
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p)
+{
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// four consecutive floats (16-byte aligned) as two 8-byte device-scope loads
+__device__ __forceinline__ f32x4 ld_dev4(const float* p)
+{
+    unsigned long long* q = (unsigned long long*)const_cast<float*>(p);
+    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
+__device__ __forceinline__ void st_dev(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_dev(double* p, double v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_dev(unsigned long long* p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// wait until every global memory access this wave issued has completed
+// (stores acknowledged); also a compiler barrier for memory operations
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// quantise one 16-value chunk (this lane's part of a group of lpg adjacent
+// lanes): the group's scale and the 16 codes packed 4 per word
+__device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_out)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) m = fmaxf(m, fabsf(v[i]));
+    m = lanes_max_f32(m, lpg);
+    const float sc = q80_scale(m);
+    *scale_out = sc;
+    int w[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int q = q80_code(v[4 * k + i], sc);
+            b |= ((uint32_t)(q & 0xFF)) << (8 * i);
+        }
+        w[k] = (int)b;
+    }
+    return i32x4{w[0], w[1], w[2], w[3]};
+}
+
+}  // namespace l2d

@@ -115,29 +115,6 @@ struct InputF32 {
     }
 };
 
-// quantise one 16-value chunk (this lane's part of a group of lpg lanes)
-__device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_out)
-{
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) m = fmaxf(m, fabsf(v[i]));
-    m = lanes_max_f32(m, lpg);
-    const float sc = q80_scale(m);
-    *scale_out = sc;
-    int w[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        uint32_t b = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int q = q80_code(v[4 * k + i], sc);
-            b |= ((uint32_t)(q & 0xFF)) << (8 * i);
-        }
-        w[k] = (int)b;
-    }
-    return i32x4{w[0], w[1], w[2], w[3]};
-}
-
 __device__ __forceinline__ void unpack16(float* v, const f32x4* a)
 {
 #pragma unroll

@@ -101,4 +101,66 @@ hipError_t launch_permute_q8(const int8_t* src, int8_t* dst, int64_t rows, int64
 hipError_t launch_quantize(const float* x, int64_t n, int32_t gs, int8_t* q, float* s,
                            hipStream_t st);
 
+// ---------------------------------------------------------------- step kernel
+// The whole decode step as one persistent cooperative kernel (mega.hip).
+
+// Grid barrier state: arrival counters per XCD (workgroup b belongs to group
+// b % 8), each on its own 128-byte line, counting up across launches; and an
+// error word set when a wait gives up.
+struct MegaSync {
+    uint32_t arrive[8][32];
+    uint32_t err[32];
+};
+
+// largest number of position ranges per kv head in the step kernel's attention
+constexpr int kMegaSplits = 64;
+
+struct MegaParams {
+    int32_t dt, gs, d, h, L, nkv, hs, kvd, G, V, S;
+    double eps;
+    // weights, in the library's device layout
+    const void* emb;
+    const float* emb_s;
+    const void* wqkv;
+    const float* wqkv_s;
+    const void* wo;
+    const float* wo_s;
+    const void* w13;
+    const float* w13_s;
+    const void* w2;
+    const float* w2_s;
+    const void* wcls;
+    const float* wcls_s;
+    const float* rms_att;
+    const float* rms_ffn;
+    const float* rms_final;
+    const float* freqs;
+    // state
+    float* kc;
+    float* vc;
+    float* x;
+    float* q;
+    float* o;
+    float* hb;
+    float* logits;
+    int32_t* step;
+    unsigned long long* argmax;
+    double* part_o;     // [nkv][kMegaSplits][G][hs]
+    double* part_ml;    // [nkv][kMegaSplits][G][2]
+    uint32_t* head_ctr; // [nkv][32]: ranges of the kv head finished (one 128-byte line each)
+    MegaSync* sync;
+    // this launch
+    int32_t token, pos, greedy;
+    uint32_t epoch0;    // grid barriers completed by earlier launches
+};
+
+// grid barriers one launch of the step kernel performs
+inline uint32_t mega_barriers(int L) { return 1u + 5u * (uint32_t)L; }
+
+bool mega_supported(int dt, int gs, int64_t d, int64_t h, int G, int hs);
+size_t mega_lds_bytes(int dt, int64_t d, int64_t h, int G, int hs);
+// workgroups of the step kernel a CU can hold with this much LDS (0: none)
+int mega_blocks_per_cu(int dt, int G, size_t lds);
+hipError_t launch_mega(const MegaParams& p, int grid, size_t lds, hipStream_t s);
+
 }  // namespace l2d

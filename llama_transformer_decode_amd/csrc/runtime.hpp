@@ -7,6 +7,7 @@
 #include <string>
 #include <vector>
 
+#include "internal.hpp"
 #include "l2d.h"
 
 namespace l2d {
@@ -65,6 +66,18 @@ struct l2d_ctx {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     bool use_graph = true;
+
+    // the persistent step kernel (one cooperative launch per step)
+    bool mega_ok = false;       // supported for this model on this device
+    bool use_mega = false;
+    bool mega_pending = false;  // launched since the error word was last read
+    int mega_grid = 0;
+    size_t mega_lds = 0;
+    uint32_t mega_epoch = 0;    // grid barriers completed so far
+    l2d::MegaSync* msync = nullptr;
+    uint32_t* head_ctr = nullptr;
+    double* mpart_o = nullptr;
+    double* mpart_ml = nullptr;
 
     int trace_layer = -1;
     int8_t* trace_q[4] = {nullptr, nullptr, nullptr, nullptr};

@@ -27,6 +27,28 @@ def need_gpu():
     return torch
 
 
+MODES = ("persistent", "graph")
+
+# The persistent step kernel faulted on its first MI355X run (tiny fp32
+# model, first step) and the cause is not found; it stays off and its cases
+# are skipped until a cause is shown and fixed.
+PERSISTENT_SKIP = "persistent step kernel disabled: memory access fault on first run, cause not yet found"
+
+
+def set_mode(ctx, mode: str):
+    """persistent: the whole step as one kernel; graph: the captured graph
+    of per-phase kernels. Skips when the persistent kernel is unavailable."""
+    if mode == "persistent":
+        pytest.skip(PERSISTENT_SKIP)
+        try:
+            ctx.use_persistent(True)
+        except Exception as e:  # noqa: BLE001 - the library's error names the reason
+            pytest.skip(f"persistent step kernel unavailable: {e}")
+    else:
+        ctx.use_persistent(False)
+        ctx.use_graph(True)
+
+
 def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """Distance in fp32 units-in-the-last-place (same sign assumed mostly)."""
     ai = a.astype(np.float32).view(np.int32).astype(np.int64)

@@ -10,6 +10,10 @@ Full-size 7B and 70B shapes run a few steps from pos 0 and one step at a deep
 position whose cache slots 0..pos-1 hold the same synthetic keys and values
 on both sides (the KV-cache hook), so long-context attention, its position
 split and its merge are checked at the real shapes and launch configuration.
+
+Every check runs in both execution modes of the library: the persistent step
+kernel (one launch per step, the default) and the captured graph of
+per-phase kernels.
 """
 import gc
 import time
@@ -20,7 +24,7 @@ import pytest
 import llama_transformer_decode_amd as l2d
 import oracle
 import synth
-from gpu_util import decode_and_compare, log, need_gpu
+from gpu_util import MODES, decode_and_compare, log, need_gpu, set_mode
 
 pytestmark = pytest.mark.gpu
 
@@ -36,27 +40,31 @@ def _trajectory(cfg, dtype, n):
     return blob, orc, fed
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("name,dtype,steps", [
     ("tiny", synth.F32, 256),
     ("15M", synth.F32, 256),
     ("tinyq8", synth.Q8_0, 64),
 ])
-def test_decode_small(name, dtype, steps):
+def test_decode_small(name, dtype, steps, mode):
     need_gpu()
     cfg = TINY_Q8 if name == "tinyq8" else synth.CONFIGS[name]
     blob, orc, fed = _trajectory(cfg, dtype, steps)
     with l2d.Context(blob, dtype) as ctx:
-        st = decode_and_compare(ctx, orc, fed, label=f"{name} dt{dtype}")
+        set_mode(ctx, mode)
+        st = decode_and_compare(ctx, orc, fed, label=f"{name} dt{dtype} {mode}")
     st.assert_ok()
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", [synth.F32, synth.Q8_0])
-def test_decode_110m_full_trajectory(dtype):
+def test_decode_110m_full_trajectory(dtype, mode):
     need_gpu()
     cfg = synth.CONFIGS["110M"]
     blob, orc, fed = _trajectory(cfg, dtype, cfg.seq_len)
     with l2d.Context(blob, dtype) as ctx:
-        st = decode_and_compare(ctx, orc, fed, label=f"110M dt{dtype}")
+        set_mode(ctx, mode)
+        st = decode_and_compare(ctx, orc, fed, label=f"110M dt{dtype} {mode}")
     st.assert_ok()
 
 
@@ -67,6 +75,7 @@ def test_graph_and_eager_agree_and_repeat_bitwise():
     cfg = synth.CONFIGS["15M"]
     blob = synth.make_blob(cfg, synth.F32)
     with l2d.Context(blob, synth.F32) as ctx:
+        ctx.use_persistent(False)
         outs = []
         for graph in (True, False):
             ctx.reset_kv()
@@ -80,13 +89,15 @@ def test_graph_and_eager_agree_and_repeat_bitwise():
         np.testing.assert_array_equal(ctx.logits(), outs[0])
 
 
-def test_greedy_on_device_matches_host_loop():
+@pytest.mark.parametrize("mode", MODES)
+def test_greedy_on_device_matches_host_loop(mode):
     need_gpu()
     cfg = synth.CONFIGS["tiny"]
     blob = synth.make_blob(cfg, synth.F32)
     orc = oracle.Model(blob, synth.F32)
     fed, am, _ = oracle.trajectory(orc, np.array([1], np.int32), 40, keep_logits=False)
     with l2d.Context(blob, synth.F32) as ctx:
+        set_mode(ctx, mode)
         ctx.forward(1, 0)
         toks = [ctx.last_token()]
         for p in range(1, 40):
@@ -167,28 +178,31 @@ def _full_size(name, dtype, deep_positions, steps=3):
     t = time.time()
     ctx = l2d.Context(blob, dtype)
     log(f"  init (upload + graph) {time.time() - t:.1f}s")
+    from gpu_util import Stats
+    modes = [m for m in MODES if m != "persistent" or ctx.persistent]
+    if "persistent" in modes:
+        modes.remove("persistent")  # disabled, see gpu_util.PERSISTENT_SKIP
+
+    def check(p, r, what):
+        # each mode rewrites cache slot p from the same inputs before using it
+        for mode in modes:
+            set_mode(ctx, mode)
+            ctx.forward(fed[-1], p)
+            st = Stats()
+            st.add(p, ctx.logits(), r, ctx.last_token())
+            log(f"  {what} {p} {mode}: {st.summary()}")
+            st.assert_ok()
+
     try:
         fed = [1]
         for p in range(steps):
             r = orc.forward(fed[-1], p)
-            ctx.forward(fed[-1], p)
-            g = ctx.logits()
-            from gpu_util import Stats
-            st = Stats()
-            st.add(p, g, r, ctx.last_token())
-            log(f"  pos {p}: {st.summary()}")
-            st.assert_ok()
+            check(p, r, "pos")
             fed.append(int(np.argmax(r)))
         for P in deep_positions:
             _fill_kv_both(ctx, orc, P, seed=77 + P)
             r = orc.forward(fed[-1], P)
-            ctx.forward(fed[-1], P)
-            g = ctx.logits()
-            from gpu_util import Stats
-            st = Stats()
-            st.add(P, g, r, ctx.last_token())
-            log(f"  deep pos {P}: {st.summary()}")
-            st.assert_ok()
+            check(P, r, "deep pos")
     finally:
         ctx.close()
         orc.close()
