@@ -65,6 +65,9 @@ CONFIGS = {
     "110M": Config("110M", 768, 2048, 12, 12, 12, 32000, 1024, 3, (F32, Q8_0)),
     "7B": Config("7B", 4096, 11008, 32, 32, 32, -32000, 4096, 4, (F32, Q8_0)),
     "70B": Config("70B", 8192, 28672, 80, 64, 8, -32000, 4096, 5, (Q8_0,)),
+    # second full-size workload: the 13B shape (its per-tensor element counts
+    # exceed 2^31 over the layers, the range where 32-bit offsets overflow)
+    "13B": Config("13B", 5120, 13824, 40, 40, 40, -32000, 4096, 6, (F32, Q8_0)),
 }
 
 GS = 64

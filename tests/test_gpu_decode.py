@@ -219,5 +219,13 @@ def test_decode_7b_q8_full_size():
     _full_size("7B", synth.Q8_0, [512, 2048])
 
 
+def test_decode_13b_q8_full_size():
+    _full_size("13B", synth.Q8_0, [4095], steps=2)
+
+
+def test_decode_13b_fp32_full_size():
+    _full_size("13B", synth.F32, [1024], steps=2)
+
+
 def test_decode_70b_q8_full_size():
     _full_size("70B", synth.Q8_0, [4095], steps=2)
