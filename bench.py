@@ -219,6 +219,13 @@ def main():
             if kb:
                 kern[k]["gbs"] = kb / sec / 1e9
         detail[name] = {"per_pos": {str(p): res[p] for p in positions}, "kernels": kern}
+        # the same step with next-token sampling on (T = 0.8, fused into the
+        # classifier) at the headline position
+        ctx.set_sampling(0.8, 12345)
+        sec = time_replays(ctx, fed[args.headline_pos], args.headline_pos, args.steps, args.warmup, torch)
+        ctx.set_sampling(0.0, 0)
+        detail[name]["sampling_t0.8"] = {"ms": sec * 1e3, "tok_s": 1.0 / sec}
+        log(f"[bench]   pos {args.headline_pos} with sampling T=0.8: {sec * 1e3:.3f} ms/step, {1 / sec:.1f} tok/s")
         log(f"[bench] {name} kernels at pos {args.headline_pos}: " +
             ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['gbs']:.0f}GB/s" if 'gbs' in v else "")
                       for k, v in kern.items()))

@@ -121,18 +121,36 @@ int l2d_init(const l2d_config* cfg, const l2d_weights* w, void* stream, l2d_ctx*
 const float* l2d_forward(l2d_ctx* ctx, int32_t token, int32_t pos);
 
 /*
- * Like l2d_forward, with the token taken on the device from the argmax of
- * the previous step (greedy decoding without a host round trip). pos must be
- * >= 1 and the previous forward of this context must have been at pos - 1.
+ * Like l2d_forward, with the token taken on the device from the previous
+ * step's pick (its argmax, or its sampled token when sampling is on):
+ * decoding without a host round trip. pos must be >= 1 and the previous
+ * forward of this context must have been at pos - 1.
  */
 const float* l2d_forward_greedy(l2d_ctx* ctx, int32_t pos);
+
+/*
+ * Next-token selection of the following forwards (mht18 essay, section 3.2:
+ * the logits go through a softmax, the next token is a random draw from
+ * that distribution, the temperature scaling the logits first).
+ * temperature == 0 (the default): the greedy argmax. temperature > 0: the
+ * token is drawn from softmax(logits / temperature) by the Gumbel-max rule,
+ * fused into the classifier: argmax_i of fp32(logit_i / T + g_i), ties to the
+ * lowest index, g_i = -log(-log(u_i)) in fp64, u_i = ((b >> 11) + 1/2) 2^-53
+ * with b output k = pos * vocab + i + 1 of the splitmix64 stream seeded with
+ * `seed` (Steele, Lea, Flood 2014). The draws depend only on (seed, pos,
+ * token index): a run is reproducible. The logits are unchanged;
+ * l2d_last_token returns the drawn token. Returns L2D_EINVAL for a negative
+ * or non-finite temperature.
+ */
+int l2d_set_sampling(l2d_ctx* ctx, double temperature, uint64_t seed);
 
 /* Wait for the context's stream. */
 int l2d_sync(l2d_ctx* ctx);
 
 /*
- * Argmax of the last forward's logits: the lowest index among equal maxima
- * (sample_argmax of the gitcode guide's main loop). Waits for the stream.
+ * The last forward's pick: the argmax of its logits, the lowest index among
+ * equal maxima (sample_argmax of the gitcode guide's main loop), or with
+ * sampling on (l2d_set_sampling) the drawn token. Waits for the stream.
  */
 int l2d_last_token(l2d_ctx* ctx, int32_t* token);
 

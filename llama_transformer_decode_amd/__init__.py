@@ -86,6 +86,7 @@ def lib():
             "l2d_trace_read": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp]),
             "l2d_use_graph": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_use_persistent": (ctypes.c_int, [_vp, ctypes.c_int32]),
+            "l2d_set_sampling": (ctypes.c_int, [_vp, ctypes.c_double, ctypes.c_uint64]),
             "l2d_persistent": (ctypes.c_int, [_vp]),
             "l2d_stream": (_vp, [_vp]),
             "l2d_profile_step": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -103,7 +104,8 @@ def lib():
 EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l2d_sync",
            "l2d_last_token", "l2d_read_logits", "l2d_quantize_q80", "l2d_reset_kv", "l2d_free",
            "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_trace_layer", "l2d_trace_read",
-           "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent")
+           "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
+           "l2d_set_sampling")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
 
@@ -240,6 +242,11 @@ class Context:
 
     def use_graph(self, enable: bool):
         _check(lib().l2d_use_graph(self._h, 1 if enable else 0), self._h)
+
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """Next-token selection: temperature 0 = argmax, > 0 = a draw from
+        softmax(logits / temperature) with the given seed."""
+        _check(lib().l2d_set_sampling(self._h, float(temperature), int(seed) & (2**64 - 1)), self._h)
 
     def use_persistent(self, enable: bool):
         """Run each step as the one persistent kernel (True) or as the

@@ -593,6 +593,8 @@ hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool gre
     p.pos = pos;
     p.greedy = greedy ? 1 : 0;
     p.epoch0 = ctx->mega_epoch;
+    p.temperature = ctx->temperature;
+    p.seed = ctx->seed;
     hipError_t e = launch_mega(p, ctx->mega_grid, ctx->mega_lds, ctx->stream);
     if (e == hipSuccess) {
         ctx->mega_epoch += nb;
@@ -634,6 +636,8 @@ hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy,
     b.token = token;
     b.pos = pos;
     b.greedy = greedy ? 1 : 0;
+    b.temperature = ctx->temperature;
+    b.seed = ctx->seed;
     return launch_begin(b, ctx->stream, ev);
 }
 
@@ -879,6 +883,16 @@ int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, dou
     }
     for (int c = 0; c < KC_COUNT; c++) avg_seconds[c] = cnt[c] ? sum[c] / cnt[c] : 0.0;
     ctx->last_pos = pos;
+    return L2D_OK;
+}
+
+int l2d_set_sampling(l2d_ctx* ctx, double temperature, uint64_t seed)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "set_sampling: null context");
+    if (!(temperature >= 0.0) || !isfinite(temperature))
+        return fail(ctx, L2D_EINVAL, "set_sampling: temperature must be finite and >= 0");
+    ctx->temperature = temperature;
+    ctx->seed = seed;
     return L2D_OK;
 }
 

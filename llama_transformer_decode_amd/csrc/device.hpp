@@ -291,3 +291,37 @@ __device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_o
 }
 
 }  // namespace l2d
+
+namespace l2d {
+
+// Temperature sampling draws (mht18 essay, section 3.2: a random draw from
+// the softmax of the logits, the temperature scaling them): output k of the
+// splitmix64 stream seeded with seed (Steele, Lea, Flood 2014), mapped to a
+// uniform on (0, 1) as ((bits >> 11) + 1/2) * 2^-53, and its standard Gumbel
+// transform -log(-log(u)). argmax_i of logit_i / T + g_i is a draw from
+// softmax(logit / T) (Gumbel-max rule).
+__host__ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t k)
+{
+    uint64_t z = seed + k * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ double gumbel_at(uint64_t seed, uint64_t k)
+{
+    const double u = ((double)(splitmix64_at(seed, k) >> 11) + 0.5) * 0x1.0p-53;
+    return -log(-log(u));
+}
+
+// the value the classifier's argmax compares for token `row` of `n` at
+// position pos: the logit itself, or with temperature > 0 its Gumbel-max
+// score logit / T + g, rounded to fp32
+__device__ __forceinline__ float sample_key(float logit, double temperature, uint64_t seed, int pos, int64_t n,
+                                            int64_t row)
+{
+    if (!(temperature > 0.0)) return logit;
+    return (float)((double)logit / temperature + gumbel_at(seed, (uint64_t)pos * (uint64_t)n + (uint64_t)row + 1u));
+}
+
+}  // namespace l2d

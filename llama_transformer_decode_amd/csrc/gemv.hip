@@ -237,6 +237,8 @@ struct EpiIn {
     const float* res;    // [rpw] residual stream values of the tile's rows
     const float* rcos;   // [hs/2] fp32 cosines of pos * freq_j
     const float* rsin;   // [hs/2] fp32 sines
+    double temp;         // EPI_LOGITS: sampling temperature (0: argmax)
+    uint64_t seed;       // EPI_LOGITS: sampling seed
 };
 
 template <int EPI>
@@ -261,7 +263,8 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
             if (row < p.M) {
                 const float y = (float)acc[r];
                 p.out[row] = y;
-                const unsigned long long key = argmax_pack(y, (uint32_t)row);
+                const float kv = sample_key(y, in.temp, in.seed, in.pos, p.M, row);
+                const unsigned long long key = argmax_pack(kv, (uint32_t)row);
                 best = key > best ? key : best;
             }
         }
@@ -431,7 +434,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
     const int64_t t_beg = tiles * gw / nw, t_end = tiles * (gw + 1) / nw;
     const int64_t iters = (t_end - t_beg) * nch;
-    const int pos = (EPI == EPI_QKV || EPI == EPI_LOGITS) ? p.step[1] : 0;
+    const int pos = (EPI == EPI_QKV || EPI == EPI_LOGITS) ? p.step[kStepPos] : 0;
+    uint64_t seed = 0;
+    double temp = 0.0;
+    if (EPI == EPI_LOGITS) {
+        seed = *(const uint64_t*)(p.step + kStepSeed);
+        temp = *(const double*)(p.step + kStepTemp);
+    }
 
     // 1. input loads
     typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<PRO, NC>>::type in;
@@ -476,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 #pragma unroll
                 for (int r = 0; r < RPW; r++) acc[r] = wave_sum_to_last(acc[r]);
                 if (lane == kWave - 1) {
-                    const EpiIn ein{pos, buf[k].res, rcos, rsin};
+                    const EpiIn ein{pos, buf[k].res, rcos, rsin, temp, seed};
                     gemv_epilogue<EPI>(p, tile * RPW, RPW, acc, best, ein);
                 }
 #pragma unroll

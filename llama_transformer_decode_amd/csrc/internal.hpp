@@ -9,6 +9,11 @@ namespace l2d {
 
 enum Dt { DT_F32 = 0, DT_Q8 = 1 };
 
+// The device step record (int32 words), written by the step-start kernel:
+// token, pos, then the sampler's seed (uint64) and temperature (fp64; 0 =
+// greedy argmax) at 8-byte aligned word offsets.
+enum { kStepToken = 0, kStepPos = 1, kStepSeed = 2, kStepTemp = 4, kStepWords = 16 };
+
 // The classifier's argmax is kept in kArgmaxSlots packed 64-bit slots per
 // step parity (pos & 1), each on its own 128-byte line, so that workgroups
 // finishing together do not serialise on one atomic; the step's argmax is
@@ -44,7 +49,7 @@ struct GemvParams {
     float* vcache;
     int32_t d, kvd, hs;
     const float* freqs;   // [hs/2] RoPE frequencies
-    const int32_t* step;  // device {token, pos}
+    const int32_t* step;  // device step record (kStep*)
     // EPI_LOGITS
     unsigned long long* argmax;  // [2][kArgmaxSlots][kArgmaxStride], parity pos & 1
     // diagnostics
@@ -91,6 +96,8 @@ struct BeginParams {
     int32_t* step;
     unsigned long long* argmax;
     int32_t token, pos, greedy;
+    double temperature;  // 0: the classifier's argmax picks the token
+    uint64_t seed;
 };
 
 hipError_t launch_begin(const BeginParams& p, hipStream_t s, const LaunchEvents* ev = nullptr);
@@ -152,6 +159,8 @@ struct MegaParams {
     // this launch
     int32_t token, pos, greedy;
     uint32_t epoch0;    // grid barriers completed by earlier launches
+    double temperature; // 0: argmax
+    uint64_t seed;
 };
 
 // grid barriers one launch of the step kernel performs

@@ -328,13 +328,15 @@ struct MvPhase {
             if (row0 < m.M) {
                 const float v = (float)y0;
                 m.out[row0] = v;
-                const unsigned long long key = argmax_pack(v, (uint32_t)row0);
+                const float kv = sample_key(v, P.temperature, P.seed, P.pos, m.M, row0);
+                const unsigned long long key = argmax_pack(kv, (uint32_t)row0);
                 best = key > best ? key : best;
             }
             if (row0 + 1 < m.M) {
                 const float v = (float)y1;
                 m.out[row0 + 1] = v;
-                const unsigned long long key = argmax_pack(v, (uint32_t)(row0 + 1));
+                const float kv = sample_key(v, P.temperature, P.seed, P.pos, m.M, row0 + 1);
+                const unsigned long long key = argmax_pack(kv, (uint32_t)(row0 + 1));
                 best = key > best ? key : best;
             }
             break;
@@ -613,8 +615,10 @@ __global__ __launch_bounds__(kMT, 1) void step_kernel(MegaParams P)
     const int token = tok_sh;
     if (blockIdx.x == 0) {
         if (tid == 0) {
-            st_dev(P.step, token);
-            st_dev(P.step + 1, pos);
+            st_dev(P.step + kStepToken, token);
+            st_dev(P.step + kStepPos, pos);
+            st_dev((unsigned long long*)(P.step + kStepSeed), (unsigned long long)P.seed);
+            st_dev((unsigned long long*)(P.step + kStepTemp), (unsigned long long)__double_as_longlong(P.temperature));
         }
         if (tid < kArgmaxSlots) st_dev(P.argmax + ((size_t)(pos & 1) * kArgmaxSlots + tid) * kArgmaxStride, 0ull);
     }

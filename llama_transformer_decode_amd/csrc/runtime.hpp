@@ -84,6 +84,8 @@ struct l2d_ctx {
     float* trace_s[4] = {nullptr, nullptr, nullptr, nullptr};
 
     int32_t last_pos = -1;
+    double temperature = 0.0;  // next-token sampling (0: greedy argmax)
+    uint64_t seed = 0;
     std::string err;
     std::vector<void*> allocs;
 };

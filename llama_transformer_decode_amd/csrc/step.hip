@@ -46,8 +46,10 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
         }
     }
     if (i == 0) {
-        p.step[0] = token;
-        p.step[1] = p.pos;
+        p.step[kStepToken] = token;
+        p.step[kStepPos] = p.pos;
+        *(uint64_t*)(p.step + kStepSeed) = p.seed;
+        *(double*)(p.step + kStepTemp) = p.temperature;
     }
     if (blockIdx.x == 0 && threadIdx.x < kArgmaxSlots)
         p.argmax[((size_t)(p.pos & 1) * kArgmaxSlots + threadIdx.x) * kArgmaxStride] = 0ull;

@@ -54,6 +54,12 @@ def bind(path: str):
         "or_rope_freqs": (None, [ctypes.c_int64, _vp]),
         "or_rope": (None, [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
         "or_argmax": (ctypes.c_int, [_vp, ctypes.c_int64]),
+        "or_splitmix64": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_uint64]),
+        "or_uniform": (ctypes.c_double, [ctypes.c_uint64, ctypes.c_uint64]),
+        "or_sample_score": (ctypes.c_float, [ctypes.c_float, ctypes.c_double, ctypes.c_uint64,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]),
+        "or_sample": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_double, ctypes.c_uint64,
+                                     ctypes.c_int64]),
         "or_trace_layer": (None, [_vp, ctypes.c_int]),
         "or_trace_codes": (_vp, [_vp, ctypes.c_int]),
         "or_trace_scales": (_vp, [_vp, ctypes.c_int]),
@@ -151,6 +157,31 @@ def rope(vec: np.ndarray, nheads: int, hs: int, pos: int) -> np.ndarray:
 def argmax(v: np.ndarray) -> int:
     v = np.ascontiguousarray(v, dtype=np.float32)
     return int(_load().or_argmax(_ptr(v), v.size))
+
+
+def splitmix64(seed: int, k: int) -> int:
+    """Output k of the splitmix64 stream seeded with seed."""
+    return int(_load().or_splitmix64(seed & (2**64 - 1), k & (2**64 - 1)))
+
+
+def uniform(seed: int, k: int) -> float:
+    """Draw k as a uniform on (0, 1)."""
+    return float(_load().or_uniform(seed & (2**64 - 1), k & (2**64 - 1)))
+
+
+def sample_scores(logits: np.ndarray, temperature: float, seed: int, pos: int) -> np.ndarray:
+    """fp32 Gumbel-max scores logit_i / T + g_i of every token (test helper)."""
+    f = _load().or_sample_score
+    n = logits.size
+    return np.array([f(float(logits[i]), temperature, seed & (2**64 - 1), pos, n, i)
+                     for i in range(n)], np.float32)
+
+
+def sample(logits: np.ndarray, temperature: float, seed: int, pos: int) -> int:
+    """Token drawn from softmax(logits / temperature) at position pos
+    (temperature 0: argmax)."""
+    v = np.ascontiguousarray(logits, dtype=np.float32)
+    return int(_load().or_sample(_ptr(v), v.size, float(temperature), seed & (2**64 - 1), int(pos)))
 
 
 class Model:

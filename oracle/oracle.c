@@ -476,6 +476,54 @@ int or_argmax(const float* v, int64_t n)
     return (int)best;
 }
 
+/* ---- temperature sampling (mht18 essay, section 3.2: the logits go through
+   a softmax and the next token is a random draw from that distribution,
+   the temperature scaling the logits first; temperature 0 is the greedy
+   argmax above).
+   Draws: output k of the splitmix64 stream seeded with `seed` (Steele, Lea,
+   Flood 2014: state seed + k * 0x9E3779B97F4A7C15 through their finaliser),
+   as a uniform on (0, 1): ((bits >> 11) + 1/2) * 2^-53, exact in fp64.
+   The draw from softmax(logit / T) is taken by the Gumbel-max rule (Gumbel
+   1954; the argmax of logit_i / T + g_i with independent standard Gumbel
+   g_i = -log(-log(u_i)) is distributed as softmax(logit / T)): scores in
+   fp64, compared after rounding to fp32, ties to the lowest index. Token i at
+   position pos uses draw k = pos * n + i + 1. */
+uint64_t or_splitmix64(uint64_t seed, uint64_t k)
+{
+    uint64_t z = seed + k * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+double or_uniform(uint64_t seed, uint64_t k)
+{
+    return ((double)(or_splitmix64(seed, k) >> 11) + 0.5) * 0x1.0p-53;
+}
+
+/* the fp32 score of token i (for the tests' tie margins) */
+float or_sample_score(float logit, double temperature, uint64_t seed, int64_t pos, int64_t n, int64_t i)
+{
+    const double u = or_uniform(seed, (uint64_t)pos * (uint64_t)n + (uint64_t)i + 1u);
+    const double g = -log(-log(u));
+    return (float)((double)logit / temperature + g);
+}
+
+int or_sample(const float* logits, int64_t n, double temperature, uint64_t seed, int64_t pos)
+{
+    if (temperature == 0.0) return or_argmax(logits, n);
+    int64_t best = 0;
+    float bv = or_sample_score(logits[0], temperature, seed, pos, n, 0);
+    for (int64_t i = 1; i < n; i++) {
+        const float s = or_sample_score(logits[i], temperature, seed, pos, n, i);
+        if (s > bv) {
+            bv = s;
+            best = i;
+        }
+    }
+    return (int)best;
+}
+
 static void trace_alloc(or_model* m)
 {
     int64_t sizes[4] = {m->d, m->d, m->d, m->h};

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_sampling as sampling_pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
 
@@ -41,6 +42,11 @@ MUTATIONS = {
                              "float* kslot = m->kc + (pos) * kvd;"),
     "emb_dequant_scale_dropped": ("m->x[i] = (float)((double)qr[i] * (double)sr[i / m->gs]);",
                                   "m->x[i] = (float)((double)qr[i]);"),
+    "sample_temperature_multiplies": ("return (float)((double)logit / temperature + g);",
+                                      "return (float)((double)logit * temperature + g);"),
+    "sample_gumbel_sign": ("const double g = -log(-log(u));", "const double g = log(-log(u));"),
+    "sample_draw_constant": ("uint64_t z = seed + k * 0x9E3779B97F4A7C15ull;",
+                             "uint64_t z = seed + k * 0x9E3779B97F4A7C14ull;"),
 }
 
 PIN_TESTS = [
@@ -52,6 +58,8 @@ PIN_TESTS = [
     lambda: pins.test_oracle_matches_full_sequence_bruteforce(pins.TINY_Q8, 1, 8),
     pins.test_attention_pos0_is_v_and_equal_keys_give_mean_v,
     pins.test_rmsnorm_closed_form_through_embedding,
+    sampling_pins.test_splitmix64_published_outputs,
+    lambda: sampling_pins.test_draws_follow_softmax_of_scaled_logits(0.8),
 ]
 
 
