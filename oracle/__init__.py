@@ -54,6 +54,9 @@ def bind(path: str):
         "or_rope_freqs": (None, [ctypes.c_int64, _vp]),
         "or_rope": (None, [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
         "or_argmax": (ctypes.c_int, [_vp, ctypes.c_int64]),
+        "or_quantize_q40": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp]),
+        "or_group_dots_q40": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
+        "or_matvec_q40": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
         "or_splitmix64": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_uint64]),
         "or_uniform": (ctypes.c_double, [ctypes.c_uint64, ctypes.c_uint64]),
         "or_sample_score": (ctypes.c_float, [ctypes.c_float, ctypes.c_double, ctypes.c_uint64,
@@ -157,6 +160,38 @@ def rope(vec: np.ndarray, nheads: int, hs: int, pos: int) -> np.ndarray:
 def argmax(v: np.ndarray) -> int:
     v = np.ascontiguousarray(v, dtype=np.float32)
     return int(_load().or_argmax(_ptr(v), v.size))
+
+
+def quantize_q40(x: np.ndarray):
+    """4-bit group quantisation (groups of 32): (packed codes uint8[n/2], scales[n/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.empty(x.size // 2, np.uint8)
+    s = np.empty(max(x.size // 32, 1), np.float32)
+    if _load().or_quantize_q40(_ptr(x), x.size, _ptr(q), _ptr(s)) != 0:
+        raise ValueError("quantize_q40: n must be a multiple of 32")
+    return q, s[:x.size // 32]
+
+
+def group_dots_q40(wq: np.ndarray, xq: np.ndarray) -> np.ndarray:
+    """int32 dots of packed 4-bit weight groups with int8 input groups."""
+    wq = np.ascontiguousarray(wq, np.uint8)
+    xq = np.ascontiguousarray(xq, np.int8)
+    out = np.empty(xq.size // 32, np.int32)
+    if _load().or_group_dots_q40(_ptr(wq), _ptr(xq), xq.size, _ptr(out)) != 0:
+        raise ValueError("group_dots_q40: cols must be a multiple of 32")
+    return out
+
+
+def matvec_q40(Q: np.ndarray, S: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Q4_0 matvec: packed codes [rows][cols/2], scales [rows][cols/32]."""
+    Q = np.ascontiguousarray(Q, np.uint8)
+    S = np.ascontiguousarray(S, np.float32)
+    x = np.ascontiguousarray(x, np.float32)
+    rows = Q.shape[0]
+    out = np.empty(rows, np.float32)
+    if _load().or_matvec_q40(_ptr(Q), _ptr(S), _ptr(x), rows, x.size, _ptr(out)) != 0:
+        raise ValueError("matvec_q40: bad shape")
+    return out
 
 
 def splitmix64(seed: int, k: int) -> int:

@@ -373,6 +373,96 @@ int or_matvec_q80(const int8_t* Q, const float* S, const float* x, int64_t rows,
     return OR_OK;
 }
 
+/*
+ * ---- 4-bit group quantisation ("Q4_0"). The hub page's comparison table
+ * and notes name a 4-bit Q4_0 variant of the engine, a format "similar to
+ * llama.cpp's", without giving its layout. Reading, in the manner of the
+ * gitcode guide's Q8_0 listing: groups of 32 values; m is the group's value
+ * of largest magnitude (the first one among equal magnitudes); the scale is
+ * the fp32 quotient m / -8 (0 for an all-zero group); a code is the fp32
+ * quotient x / scale rounded half away from zero and clamped to [-8, 7]
+ * (the value m itself maps to -8). Storage per group: 16 bytes, byte b
+ * holding code b + 8 in its low nibble and code b + 16 + 8 in its high
+ * nibble; the fp32 scales follow as a separate array.
+ * A Q4_0 matvec quantises its input to Q8_0 with the same 32-value groups
+ * (the W8A8 scheme above with 4-bit weights): each group contributes the
+ * exact int32 dot of its codes times the weight scale times the input
+ * scale, summed over the groups in fp64.
+ */
+int or_quantize_q40(const float* x, int64_t n, uint8_t* q, float* s)
+{
+    if (n < 0 || n % 32) return OR_EINVAL;
+    for (int64_t g = 0; g < n / 32; g++) {
+        const float* xg = x + g * 32;
+        float amax = 0.0f, m = 0.0f;
+        for (int i = 0; i < 32; i++) {
+            const float a = fabsf(xg[i]);
+            if (a > amax) {
+                amax = a;
+                m = xg[i];
+            }
+        }
+        const float scale = amax == 0.0f ? 0.0f : m / -8.0f;
+        s[g] = scale;
+        int c[32];
+        for (int i = 0; i < 32; i++) {
+            int v = 0;
+            if (scale != 0.0f) {
+                const float r = roundf(xg[i] / scale);
+                v = r < -8.0f ? -8 : r > 7.0f ? 7 : (int)r;
+            }
+            c[i] = v;
+        }
+        for (int b = 0; b < 16; b++) q[g * 16 + b] = (uint8_t)((c[b] + 8) | ((c[b + 16] + 8) << 4));
+    }
+    return OR_OK;
+}
+
+/* the int32 group dot of 32 packed 4-bit weight codes with 32 int8 input codes */
+static int32_t q40_group_dot(const uint8_t* w, const int8_t* xq)
+{
+    int32_t dot = 0;
+    for (int b = 0; b < 16; b++) {
+        dot += ((int32_t)(w[b] & 15) - 8) * (int32_t)xq[b];
+        dot += ((int32_t)(w[b] >> 4) - 8) * (int32_t)xq[b + 16];
+    }
+    return dot;
+}
+
+int or_group_dots_q40(const uint8_t* wq, const int8_t* xq, int64_t cols, int32_t* out)
+{
+    if (cols % 32) return OR_EINVAL;
+    for (int64_t g = 0; g < cols / 32; g++) out[g] = q40_group_dot(wq + g * 16, xq + g * 32);
+    return OR_OK;
+}
+
+/* Q4_0 matvec: Q packed [rows][cols/2], S [rows][cols/32]; x quantised first */
+int or_matvec_q40(const uint8_t* Q, const float* S, const float* x, int64_t rows, int64_t cols, float* out)
+{
+    if (cols % 32 || rows < 0) return OR_EINVAL;
+    int8_t* aq = (int8_t*)malloc((size_t)cols + 1);
+    float* as = (float*)malloc((size_t)(cols / 32 + 1) * 4);
+    if (!aq || !as) {
+        free(aq);
+        free(as);
+        return OR_ENOMEM;
+    }
+    or_quantize(x, cols, 32, aq, as);
+    const int64_t ng = cols / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; i++) {
+        const uint8_t* qr = Q + i * (cols / 2);
+        const float* sr = S + i * ng;
+        double acc = 0.0;
+        for (int64_t g = 0; g < ng; g++)
+            acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g] * (double)as[g];
+        out[i] = (float)acc;
+    }
+    free(aq);
+    free(as);
+    return OR_OK;
+}
+
 /* the int32 group dot products of one Q8_0 matvec row: out[g] for g < cols/gs */
 int or_group_dots(const int8_t* wq, const int8_t* xq, int64_t cols, int gs, int32_t* out)
 {

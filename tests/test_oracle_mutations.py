@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_q40 as q40_pins
 import test_oracle_sampling as sampling_pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
@@ -42,6 +43,14 @@ MUTATIONS = {
                              "float* kslot = m->kc + (pos) * kvd;"),
     "emb_dequant_scale_dropped": ("m->x[i] = (float)((double)qr[i] * (double)sr[i / m->gs]);",
                                   "m->x[i] = (float)((double)qr[i]);"),
+    "q40_nibble_halves_swapped": ("dot += ((int32_t)(w[b] & 15) - 8) * (int32_t)xq[b];",
+                                  "dot += ((int32_t)(w[b] & 15) - 8) * (int32_t)xq[b + 16];"),
+    "q40_offset_7": ("dot += ((int32_t)(w[b] >> 4) - 8) * (int32_t)xq[b + 16];",
+                     "dot += ((int32_t)(w[b] >> 4) - 7) * (int32_t)xq[b + 16];"),
+    "q40_scale_positive": ("m / -8.0f;", "m / 8.0f;"),
+    "q40_clamp_8": ("v = r < -8.0f ? -8 : r > 7.0f ? 7 : (int)r;", "v = r < -8.0f ? -8 : r > 8.0f ? 8 : (int)r;"),
+    "q40_input_scale_dropped": ("acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g] * (double)as[g];",
+                                "acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g];"),
     "sample_temperature_multiplies": ("return (float)((double)logit / temperature + g);",
                                       "return (float)((double)logit * temperature + g);"),
     "sample_gumbel_sign": ("const double g = -log(-log(u));", "const double g = log(-log(u));"),
@@ -59,6 +68,8 @@ PIN_TESTS = [
     pins.test_attention_pos0_is_v_and_equal_keys_give_mean_v,
     pins.test_rmsnorm_closed_form_through_embedding,
     sampling_pins.test_splitmix64_published_outputs,
+    q40_pins.test_q40_handworked_golden,
+    q40_pins.test_q40_matvec_closed_form,
     lambda: sampling_pins.test_draws_follow_softmax_of_scaled_logits(0.8),
 ]
 
