@@ -97,6 +97,38 @@ def measured_traffic():
         return None
 
 
+def gemv_q40_rates(cfg, torch, l2d, reps: int = 20) -> dict:
+    """The Q4_0 matvec (4-bit weights, groups of 32) on the step's matrix
+    shapes: mean kernel duration (HIP events stamped at each kernel's start
+    and end) and algorithmic GB/s (packed nibbles, fp32 scales, the fp32
+    input and output once). Every shape cycles through
+    enough distinct weight copies (>= 1 GiB together) that no launch finds
+    its matrix in the 256 MB last-level cache. Weights are seeded random
+    bytes and scales (every nibble pattern is valid Q4_0 data)."""
+    d, h, V, kvd = cfg.dim, cfg.hidden_dim, cfg.vocab, cfg.kv_dim
+    shapes = {"qkv": (d + 2 * kvd, d), "wo": (d, d), "w13": (2 * h, d), "w2": (d, h), "cls": (V, d)}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4040)
+    out = {}
+    for name, (rows, cols) in shapes.items():
+        nbytes = rows * cols // 2 + rows * (cols // 32) * 4
+        copies = max(2, -(-(1 << 30) // nbytes))
+        Ws = [torch.randint(0, 256, (rows * cols // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+              for _ in range(copies)]
+        Ss = [(torch.rand(rows * (cols // 32), device="cuda", generator=gen) - 0.5) * 3e-3
+              for _ in range(copies)]
+        x = torch.randn(cols, device="cuda", generator=gen)
+        l2d.gemv_profile(l2d.Q4_0, Ws, Ss, x, rows, cols, 32, reps=copies)  # warm-up
+        sec, _ = l2d.gemv_profile(l2d.Q4_0, Ws, Ss, x, rows, cols, 32, reps=max(reps, copies))
+        alg = nbytes + cols * 4 + rows * 4
+        out[name] = {"rows": rows, "cols": cols, "avg_us": sec * 1e6, "gbs": alg / sec / 1e9,
+                     "alg_bytes": alg}
+        log(f"[bench] q4_0 gemv {name} {rows}x{cols}: {sec * 1e6:.1f} us, {alg / sec / 1e9:.0f} GB/s")
+        del Ws, Ss
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_to(ctx, positions, torch, fill=True):
     """Greedy decode from pos 0 through max(positions); returns the token fed
     at each requested position. Without fill the cache stays zero and the
@@ -179,6 +211,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-fill", action="store_true",
                     help="skip the greedy decode that fills the cache (profiling runs)")
+    ap.add_argument("--no-q4-gemv", action="store_true",
+                    help="skip the Q4_0 matvec measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -262,6 +296,8 @@ def main():
                      "traffic": measured_traffic() if dt == 1 and cfg.name == "7B" else None},
         "detail": detail,
     }
+    if not args.no_q4_gemv:
+        detail["q4_0_gemv"] = gemv_q40_rates(cfg, torch, l2d)
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
         out["cpu_baseline"] = cpu_baseline(cfg, dt, args.cpu_seconds)

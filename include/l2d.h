@@ -30,6 +30,8 @@ extern "C" {
 
 #define L2D_F32 0  /* fp32 weights and activations (run.c) */
 #define L2D_Q8_0 1 /* int8 weight/activation codes, fp32 group scales (runq.c) */
+#define L2D_Q4_0 2 /* 4-bit weight codes in groups of 32, fp32 group scales (l2d_gemv only;
+                      the 4-bit variant the pomoai.com hub page names) */
 
 #define L2D_OK 0
 #define L2D_EINVAL (-1)  /* bad argument: config, group size, token, pos, size */
@@ -191,16 +193,39 @@ int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache);
 
 /*
  * Matvec out = W x with the decode step's GEMV kernel (all device pointers):
- * W is fp32 [rows][cols] (dtype L2D_F32, W_s NULL) or Q8_0 codes with scales
- * W_s [rows][cols/gs]; x is fp32 [cols] (quantised inside the kernel for
- * Q8_0, as in the decode step); out is fp32 [rows]. group_dots, when not NULL
- * (Q8_0 only), receives the exact int32 dot of every (row, group):
- * [rows][cols/gs]. rows must be even; Q8_0 gs a power of two in [16, 256].
+ * W is fp32 [rows][cols] (dtype L2D_F32, W_s NULL), Q8_0 int8 codes
+ * [rows][cols] or Q4_0 nibbles [rows][cols/2], with fp32 scales W_s
+ * [rows][cols/gs]; x is fp32 [cols]; out is fp32 [rows].
+ * Q8_0 (gitcode porting guide, INT8 quantisation section): x is quantised
+ * inside the kernel with the weights' group size, as in the decode step;
+ * gs a power of two in [16, 256].
+ * Q4_0 (4-bit variant named on the pomoai.com hub page; read as): gs must be
+ * 32; code c of a group is stored as c + 8 in [0, 15], byte b of a group's
+ * 16 bytes holding code b in its low nibble and code b + 16 in its high
+ * nibble; the scale is the group's value of largest magnitude divided by
+ * -8. x is quantised inside the kernel to Q8_0 with groups of 32, and each
+ * output is the fp64 sum over groups of (exact int32 group dot) x weight
+ * scale x input scale, rounded to fp32.
+ * group_dots, when not NULL (Q8_0 and Q4_0), receives the exact int32 dot of
+ * every (row, group): [rows][cols/gs]. rows must be even.
  * Asynchronous on stream (Q8_0 codes are first re-laid-out into a
- * stream-ordered temporary buffer).
+ * stream-ordered temporary buffer; Q4_0 is read in place).
  */
 int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
              int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream);
+
+/*
+ * Time the matvec kernel of l2d_gemv (dtype L2D_F32 or L2D_Q4_0; Q8_0 codes
+ * need the device layout and are timed by l2d_profile_step): reps launches
+ * on stream, launch r reading weight copy r % copies (W and W_s are host
+ * arrays of `copies` device pointers; W_s may be NULL for fp32), each
+ * bracketed by HIP events stamped at the kernel's own start and end.
+ * avg_seconds receives the mean kernel duration; out holds the last
+ * launch's result. Synchronous. Same argument rules as l2d_gemv.
+ */
+int l2d_gemv_profile(int32_t dtype, const void* const* W, const float* const* W_s, int32_t copies,
+                     const float* x, int64_t rows, int64_t cols, int32_t gs, float* out,
+                     int32_t reps, double* avg_seconds, void* stream);
 
 /*
  * Trace the quantised matvec inputs of one layer (Q8_0): after l2d_trace_layer

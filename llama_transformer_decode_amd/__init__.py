@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libl2d.so")
 
 F32 = 0
 Q8_0 = 1
+Q4_0 = 2  # matvec (gemv) only
 
 OK, EINVAL, EFORMAT, ENOMEM, EHIP = 0, -1, -2, -3, -4
 
@@ -82,6 +83,9 @@ def lib():
             "l2d_kv_cache": (ctypes.c_int, [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
             "l2d_gemv": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
+            "l2d_gemv_profile": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp,
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _vp]),
             "l2d_trace_layer": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_trace_read": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp]),
             "l2d_use_graph": (ctypes.c_int, [_vp, ctypes.c_int32]),
@@ -103,7 +107,7 @@ def lib():
 # every symbol include/l2d.h declares
 EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l2d_sync",
            "l2d_last_token", "l2d_read_logits", "l2d_quantize_q80", "l2d_reset_kv", "l2d_free",
-           "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_trace_layer", "l2d_trace_read",
+           "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
            "l2d_set_sampling")
 
@@ -291,3 +295,18 @@ def gemv(dtype: int, W, W_s, x, rows: int, cols: int, gs: int = 64, group_dots=N
                           x.data_ptr(), rows, cols, gs, out.data_ptr(),
                           group_dots.data_ptr() if group_dots is not None else None, st))
     return out
+
+
+def gemv_profile(dtype: int, Ws, Ss, x, rows: int, cols: int, gs: int = 32, reps: int = 20, stream=None):
+    """Mean kernel seconds of the matvec over reps launches cycling through
+    the weight copies Ws (and scale copies Ss, or None for fp32); returns
+    (seconds, output of the last launch)."""
+    import torch
+    out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    st = _stream_handle(stream if stream is not None else torch.cuda.current_stream())
+    wp = (_vp * len(Ws))(*[w.data_ptr() for w in Ws])
+    sp = (_vp * len(Ws))(*[s.data_ptr() for s in Ss]) if Ss is not None else None
+    sec = ctypes.c_double(0.0)
+    _check(lib().l2d_gemv_profile(dtype, wp, sp, len(Ws), x.data_ptr(), rows, cols, gs,
+                                  out.data_ptr(), reps, ctypes.byref(sec), st))
+    return sec.value, out

@@ -793,19 +793,51 @@ int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache)
     return L2D_OK;
 }
 
-int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
-             int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream)
+// Argument checks shared by l2d_gemv and l2d_gemv_profile; fills p (W, Ws
+// left to the caller) and the kernel dtype.
+static int gemv_setup(int32_t dtype, const float* x, int64_t rows, int64_t cols, int32_t gs,
+                      bool have_scales, float* out, GemvParams* p, int* dt)
 {
-    if (dtype != L2D_F32 && dtype != L2D_Q8_0) return fail(nullptr, L2D_EINVAL, "gemv: bad dtype");
-    if (rows <= 0 || cols <= 0 || rows % 2 || cols % 4 || !W || !x || !out)
+    if (dtype != L2D_F32 && dtype != L2D_Q8_0 && dtype != L2D_Q4_0)
+        return fail(nullptr, L2D_EINVAL, "gemv: bad dtype");
+    if (rows <= 0 || cols <= 0 || rows % 2 || cols % 4 || !x || !out)
         return fail(nullptr, L2D_EINVAL, "gemv: need rows even > 0, cols % 4 == 0, non-null pointers");
     if (dtype == L2D_Q8_0) {
-        if (gs < 16 || gs > 256 || (gs & (gs - 1)) || cols % gs || !W_s)
+        if (gs < 16 || gs > 256 || (gs & (gs - 1)) || cols % gs || !have_scales)
             return fail(nullptr, L2D_EINVAL, "gemv: Q8_0 needs a power-of-two gs in [16,256] dividing cols");
+        if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
+    } else if (dtype == L2D_Q4_0) {
+        if (gs != 32 || cols % 32 || !have_scales) return fail(nullptr, L2D_EINVAL, "gemv: Q4_0 needs gs 32 dividing cols");
         if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
     } else if (cols > 16000) {
         return fail(nullptr, L2D_EINVAL, "gemv: fp32 cols > 16000");
     }
+    memset(p, 0, sizeof(*p));
+    p->M = rows;
+    p->K = cols;
+    p->gs = dtype == L2D_F32 ? 1 : gs;
+    p->x = x;
+    p->out = out;
+    *dt = dtype == L2D_F32 ? DT_F32 : dtype == L2D_Q8_0 ? DT_Q8 : DT_Q4;
+    return L2D_OK;
+}
+
+static int gemv_grid()
+{
+    int dev = 0, cus = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus > 0 ? 2 * cus : 512;
+}
+
+int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
+             int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream)
+{
+    GemvParams p;
+    int dt = 0;
+    int rc = gemv_setup(dtype, x, rows, cols, gs, W_s != nullptr, out, &p, &dt);
+    if (rc != L2D_OK) return rc;
+    if (!W) return fail(nullptr, L2D_EINVAL, "gemv: null weights");
     hipStream_t st = (hipStream_t)stream;
     void* perm = nullptr;
     if (dtype == L2D_Q8_0) {
@@ -818,23 +850,49 @@ int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int
             return fail(nullptr, L2D_EHIP, std::string("gemv: ") + hipGetErrorString(e));
         }
     }
-    GemvParams p;
-    memset(&p, 0, sizeof(p));
     p.W = perm ? perm : W;
     p.Ws = W_s;
-    p.M = rows;
-    p.K = cols;
-    p.gs = dtype == L2D_Q8_0 ? gs : 1;
-    p.x = x;
-    p.out = out;
-    p.group_dots = dtype == L2D_Q8_0 ? group_dots : nullptr;
-    int dev = 0, cus = 0;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    hipError_t e = launch_gemv(dtype == L2D_F32 ? DT_F32 : DT_Q8, PRO_PLAIN, EPI_STORE, p,
-                               cus > 0 ? 2 * cus : 512, st);
+    p.group_dots = dtype == L2D_F32 ? nullptr : group_dots;
+    hipError_t e = launch_gemv(dt, PRO_PLAIN, EPI_STORE, p, gemv_grid(), st);
     if (perm) (void)hipFreeAsync(perm, st);
     if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("gemv: ") + hipGetErrorString(e));
+    return L2D_OK;
+}
+
+int l2d_gemv_profile(int32_t dtype, const void* const* W, const float* const* W_s, int32_t copies,
+                     const float* x, int64_t rows, int64_t cols, int32_t gs, float* out,
+                     int32_t reps, double* avg_seconds, void* stream)
+{
+    if (!W || copies <= 0 || reps <= 0 || !avg_seconds)
+        return fail(nullptr, L2D_EINVAL, "gemv_profile: bad argument");
+    if (dtype == L2D_Q8_0)
+        return fail(nullptr, L2D_EINVAL, "gemv_profile: Q8_0 codes need the device layout (timed by l2d_profile_step)");
+    GemvParams p;
+    int dt = 0;
+    int rc = gemv_setup(dtype, x, rows, cols, gs, W_s != nullptr, out, &p, &dt);
+    if (rc != L2D_OK) return rc;
+    for (int i = 0; i < copies; i++)
+        if (!W[i] || (dtype == L2D_Q4_0 && !W_s[i])) return fail(nullptr, L2D_EINVAL, "gemv_profile: null copy");
+    hipStream_t st = (hipStream_t)stream;
+    const int grid = gemv_grid();
+    KernelTimer kt;
+    for (int r = 0; r < reps; r++) {
+        if (kt.next(0) != hipSuccess) return fail(nullptr, L2D_EHIP, "gemv_profile: no events");
+        p.W = W[r % copies];
+        p.Ws = dtype == L2D_Q4_0 ? W_s[r % copies] : nullptr;
+        hipError_t e = launch_gemv(dt, PRO_PLAIN, EPI_STORE, p, grid, st, &kt.cur);
+        if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("gemv_profile: ") + hipGetErrorString(e));
+    }
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("gemv_profile: ") + hipGetErrorString(e));
+    double sum = 0.0;
+    for (size_t i = 0; i < kt.used / 2; i++) {
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, kt.ev[2 * i], kt.ev[2 * i + 1]);
+        if (e != hipSuccess) return fail(nullptr, L2D_EHIP, std::string("gemv_profile: ") + hipGetErrorString(e));
+        sum += ms * 1e-3;
+    }
+    *avg_seconds = sum / reps;
     return L2D_OK;
 }
 

@@ -24,7 +24,11 @@
 // multiply-add into fp64 (a product of two fp32 values is exact in fp64).
 // Q8_0 rows are stored group-interleaved (q8_perm_offset) so that each lane
 // holds whole groups: v_dot4_i32_i8 gives the exact int32 group dot in one
-// lane, combined in fp64 with the weight and activation scales.
+// lane, combined in fp64 with the weight and activation scales. Q4_0 rows
+// need no re-layout: a group is 16 bytes, so one 16-byte load per lane holds
+// a whole group; its nibbles are unpacked with two masks and dotted against
+// the input's codes, the dot starting from -8 x (the group's input code sum)
+// to undo the +8 offset of the stored nibbles.
 //   epilogue  a DPP wave sum leaves each row's total in lane 63, which
 //             finishes the tile: store, residual add, RoPE + KV-cache write,
 //             SwiGLU, or classifier + packed argmax.
@@ -43,7 +47,11 @@ constexpr int kWaves = kThreads / kWave;
 // LDS bytes of the prepared input vector (16-byte aligned end)
 __host__ __device__ inline size_t gemv_input_bytes(int dt, int64_t K, int gs)
 {
-    const size_t b = dt == DT_F32 ? (size_t)K * 4 : (size_t)K + (size_t)(K / gs) * 4;
+    // fp32: the vector; Q8_0: codes and scales; Q4_0: codes, scales and
+    // the offset terms (int32)
+    const size_t b = dt == DT_F32 ? (size_t)K * 4
+                   : dt == DT_Q8  ? (size_t)K + (size_t)(K / gs) * 4
+                                  : (size_t)K + (size_t)(K / gs) * 8;
     return (b + 15) & ~(size_t)15;
 }
 
@@ -126,12 +134,23 @@ __device__ __forceinline__ void unpack16(float* v, const f32x4* a)
     }
 }
 
-// Q8_0 input: thread t holds 16-value chunks t, t+256, ... (NC of them);
-// lanes of one group (lpg = gs/16) are adjacent. Codes go to LDS in the
-// group-interleaved order of the weights, scales in plain order after them.
+// Index (in 16-byte units) of 16-value input chunk c in LDS: Q8_0 in the
+// group-interleaved order of the weights; Q4_0 (gs 32) in two planes, the
+// first 16 codes of every group, then the last 16.
+template <int DT>
+__device__ __forceinline__ int64_t input_chunk_slot(int64_t c, int64_t K, int gs)
+{
+    if (DT == DT_Q8) return q8_perm_offset(16 * c, K, gs) / 16;
+    return (c & 1) * (K / 32) + (c >> 1);
+}
+
+// Quantised input (Q8_0 codes of x for the Q8_0 and Q4_0 matvecs): thread t
+// holds 16-value chunks t, t+256, ... (NC of them); lanes of one group
+// (lpg = gs/16) are adjacent. Codes go to LDS at input_chunk_slot, scales in
+// plain order after them, and for Q4_0 then -8 x each group's code sum.
 // NC == 0: the input is too long to hold; it is loaded in batches after the
 // weight prefetch instead.
-template <int PRO, int NC>
+template <int DT, int PRO, int NC>
 struct InputQ8 {
     static constexpr int N = NC > 0 ? NC : 1;
     f32x4 x[N][4], g[N][4];
@@ -156,9 +175,15 @@ struct InputQ8 {
     {
         float sc;
         const i32x4 codes = quant16(v, lpg, &sc);
+        int csum = 0;
+        if (DT == DT_Q4) csum = lanes_sum_i32(dot16_i8(codes, i32x4{0x01010101, 0x01010101, 0x01010101,
+                                                                 0x01010101}), lpg);
         if (c < p.K / 16) {
-            ((i32x4*)smem)[q8_perm_offset(16 * c, p.K, p.gs) / 16] = codes;
-            if ((c & (lpg - 1)) == 0) ((float*)(smem + p.K))[c / lpg] = sc;
+            ((i32x4*)smem)[input_chunk_slot<DT>(c, p.K, p.gs)] = codes;
+            if ((c & (lpg - 1)) == 0) {
+                ((float*)(smem + p.K))[c / lpg] = sc;
+                if (DT == DT_Q4) ((int*)(smem + p.K))[p.K / p.gs + c / lpg] = -8 * csum;
+            }
         }
     }
 
@@ -219,7 +244,7 @@ struct InputQ8 {
         if (p.trace_q != nullptr && blockIdx.x == 0) {
             // back to plain element order for the trace
             for (int64_t c = threadIdx.x; c < nq; c += kThreads)
-                ((i32x4*)p.trace_q)[c] = ((const i32x4*)smem)[q8_perm_offset(16 * c, p.K, p.gs) / 16];
+                ((i32x4*)p.trace_q)[c] = ((const i32x4*)smem)[input_chunk_slot<DT>(c, p.K, p.gs)];
             for (int64_t g = threadIdx.x; g < p.K / p.gs; g += kThreads)
                 p.trace_s[g] = ((const float*)(smem + p.K))[g];
         }
@@ -319,11 +344,14 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
 //   Q8_0: one block of 64 groups of each of RPW rows in the permuted layout:
 //         lane j holds group j of the block, U = gs/16 loads of 16 bytes,
 //         plus that group's weight scale.
+//   Q4_0: 64*U groups of each of RPW rows: lane j holds groups j, j+64, ...
+//         (one 16-byte load each) and their weight scales.
 template <int DT, int RPW, int U>
 struct Chunk {
+    static constexpr int SU = DT == DT_Q4 ? U : 1;
     using V = typename std::conditional<DT == DT_F32, f32x4, i32x4>::type;
     V w[RPW][U];
-    float s[RPW];
+    float s[RPW][SU];
     float res[RPW];  // residual values of the rows (EPI_RESID)
 };
 
@@ -351,7 +379,7 @@ __device__ __forceinline__ void load_chunk(Chunk<DT, RPW, U>& ch, const GemvPara
             for (int r = 0; r < RPW; r++)
                 ch.w[r][uu] = __builtin_nontemporal_load(base + (imin(row0 + r, p.M - 1) * Kv + c) * keep);
         }
-    } else {
+    } else if constexpr (DT == DT_Q8) {
         const int64_t ng = p.K / p.gs;
         const int64_t g0 = chunk * 64;
         const int64_t nb = imin(ng - g0, 64);
@@ -364,7 +392,21 @@ __device__ __forceinline__ void load_chunk(Chunk<DT, RPW, U>& ch, const GemvPara
             const i32x4* W = (const i32x4*)(base + (row * p.K + g0 * p.gs) * keep);
 #pragma unroll
             for (int q = 0; q < U; q++) ch.w[r][q] = __builtin_nontemporal_load(W + (nb * q + j) * keep);
-            ch.s[r] = sbase[(row * ng + g0 + j) * keep];
+            ch.s[r][0] = sbase[(row * ng + g0 + j) * keep];
+        }
+    } else {
+        const int64_t ng = p.K / 32;
+        const i32x4* base = dummy ? (const i32x4*)p.x : (const i32x4*)p.W;
+        const float* sbase = dummy ? p.x : p.Ws;
+#pragma unroll
+        for (int r = 0; r < RPW; r++) {
+            const int64_t rg = imin(row0 + r, p.M - 1) * ng;
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t g = imin(chunk * kWave * U + u * kWave + lane, ng - 1);
+                ch.w[r][u] = __builtin_nontemporal_load(base + (rg + g) * keep);
+                ch.s[r][u] = sbase[(rg + g) * keep];
+            }
         }
     }
 }
@@ -391,7 +433,7 @@ __device__ __forceinline__ void use_chunk(const Chunk<DT, RPW, U>& ch, double* a
                 acc[r] += (double)w.w * (double)xv.w;
             }
         }
-    } else {
+    } else if constexpr (DT == DT_Q8) {
         const int64_t ng = p.K / p.gs;
         const int64_t g0 = chunk * 64;
         const int64_t nb = imin(ng - g0, 64);
@@ -412,9 +454,43 @@ __device__ __forceinline__ void use_chunk(const Chunk<DT, RPW, U>& ch, double* a
                 d = dot4_i8(ch.w[r][q].z, xv[q].z, d);
                 d = dot4_i8(ch.w[r][q].w, xv[q].w, d);
             }
-            const double t = ((double)d * (double)ch.s[r]) * xsg;
+            const double t = ((double)d * (double)ch.s[r][0]) * xsg;
             acc[r] += ok ? t : 0.0;
             if (DBG && ok && row0 + r < p.M) p.group_dots[(row0 + r) * ng + g0 + lane] = d;
+        }
+    } else {
+        // byte b of a group: code b + 8 in the low nibble, code b + 16 + 8
+        // in the high nibble
+        constexpr int kLo = 0x0F0F0F0F;
+        const int64_t ng = p.K / 32;
+        const i32x4* xlo = (const i32x4*)smem;  // codes 0-15 of every group
+        const i32x4* xhi = xlo + ng;            // codes 16-31
+        const float* xs = (const float*)(smem + p.K);
+        const int* xoff = (const int*)(xs + ng);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t g = chunk * kWave * U + u * kWave + lane;
+            const bool ok = valid && g < ng;
+            const int64_t gc = imin(g, ng - 1);
+            const i32x4 a = xlo[gc], b = xhi[gc];
+            const double xsg = (double)xs[gc];
+            const int off = xoff[gc];
+#pragma unroll
+            for (int r = 0; r < RPW; r++) {
+                const i32x4 w = ch.w[r][u];
+                int d = off;
+                d = dot4_i8(w.x & kLo, a.x, d);
+                d = dot4_i8(w.y & kLo, a.y, d);
+                d = dot4_i8(w.z & kLo, a.z, d);
+                d = dot4_i8(w.w & kLo, a.w, d);
+                d = dot4_i8((int)((uint32_t)w.x >> 4) & kLo, b.x, d);
+                d = dot4_i8((int)((uint32_t)w.y >> 4) & kLo, b.y, d);
+                d = dot4_i8((int)((uint32_t)w.z >> 4) & kLo, b.z, d);
+                d = dot4_i8((int)((uint32_t)w.w >> 4) & kLo, b.w, d);
+                const double t = ((double)d * (double)ch.s[r][u]) * xsg;
+                acc[r] += ok ? t : 0.0;
+                if (DBG && ok && row0 + r < p.M) p.group_dots[(row0 + r) * ng + g] = d;
+            }
         }
     }
 }
@@ -425,9 +501,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ double red[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // chunks per tile: 64*U float4 columns (fp32) or 64 groups (Q8_0)
+    // chunks per tile: 64*U float4 columns (fp32), 64 groups (Q8_0) or
+    // 64*U groups (Q4_0)
     const int64_t nch = DT == DT_F32 ? (p.K / 4 + kWave * U - 1) / (kWave * U)
-                                     : (p.K / p.gs + 63) / 64;
+                      : DT == DT_Q8  ? (p.K / p.gs + 63) / 64
+                                     : (p.K / 32 + kWave * U - 1) / (kWave * U);
     // balanced contiguous range of tiles for this wave
     const int64_t tiles = (p.M + RPW - 1) / RPW;
     const int64_t nw = (int64_t)gridDim.x * kWaves;
@@ -443,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     }
 
     // 1. input loads
-    typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<PRO, NC>>::type in;
+    typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<DT, PRO, NC>>::type in;
     in.issue(p);
 
     // 2. the first NBUF chunks (dummy loads for a wave with fewer chunks)
@@ -570,6 +648,11 @@ static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t 
 {
     if constexpr (DT == DT_F32) {
         return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s, ev);
+    } else if constexpr (DT == DT_Q4) {
+        // four rows of one group per lane: the fastest of RPW 1-8 x U 1-4
+        // on every 7B matrix shape (MI355X, 512 and 1024 workgroups)
+        if (p.gs != 32) return hipErrorInvalidValue;
+        return launch_nc<DT, PRO, EPI, 4, 1, DBG>(p, max_blocks, s, ev);
     } else {
         const int64_t waves = (int64_t)(max_blocks > 0 ? max_blocks : 512) * kWaves;
         switch (p.gs) {
@@ -592,7 +675,7 @@ hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_bl
 {
 #define L2D_CASE(D, P, E)                                                  \
     if (dt == D && pro == P && epi == E) {                                 \
-        if (D == DT_Q8 && p.group_dots != nullptr)                         \
+        if (D != DT_F32 && p.group_dots != nullptr)                        \
             return launch_shape<D, P, E, true>(p, max_blocks, s, ev);      \
         return launch_shape<D, P, E, false>(p, max_blocks, s, ev);         \
     }
@@ -606,6 +689,7 @@ hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_bl
     L2D_CASE(DT_Q8, PRO_NORM, EPI_SWIGLU)
     L2D_CASE(DT_Q8, PRO_NORM, EPI_LOGITS)
     L2D_CASE(DT_Q8, PRO_PLAIN, EPI_STORE)
+    L2D_CASE(DT_Q4, PRO_PLAIN, EPI_STORE)
 #undef L2D_CASE
     return hipErrorInvalidValue;
 }

@@ -7,7 +7,9 @@
 
 namespace l2d {
 
-enum Dt { DT_F32 = 0, DT_Q8 = 1 };
+// DT_Q4: 4-bit weight codes, two per byte, groups of 32 with an fp32 scale
+// (matvec only; the input vector is quantised to Q8_0 with groups of 32).
+enum Dt { DT_F32 = 0, DT_Q8 = 1, DT_Q4 = 2 };
 
 // The device step record (int32 words), written by the step-start kernel:
 // token, pos, then the sampler's seed (uint64) and temperature (fp64; 0 =
@@ -36,8 +38,8 @@ enum Epi {
 };
 
 struct GemvParams {
-    const void* W;     // fp32 [M][K] or int8 codes [M][K]
-    const float* Ws;   // Q8_0 scales [M][K/gs]
+    const void* W;     // fp32 [M][K], int8 codes [M][K] or Q4_0 nibbles [M][K/2]
+    const float* Ws;   // Q8_0 / Q4_0 scales [M][K/gs]
     int64_t M, K;
     int32_t gs;
     const float* x;     // input vector [K], fp32
@@ -53,7 +55,7 @@ struct GemvParams {
     // EPI_LOGITS
     unsigned long long* argmax;  // [2][kArgmaxSlots][kArgmaxStride], parity pos & 1
     // diagnostics
-    int32_t* group_dots;  // [M][K/gs] exact int32 group dots (Q8_0, test hook)
+    int32_t* group_dots;  // [M][K/gs] exact int32 group dots (Q8_0, Q4_0; test hook)
     int8_t* trace_q;      // workgroup 0 copies its quantised input here
     float* trace_s;
 };

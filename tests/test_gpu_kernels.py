@@ -1,7 +1,8 @@
 """GPU parity of the individual kernels against the oracle, through the C ABI:
 the Q8_0 quantiser (bit-exact codes and scales), the fp32 GEMV (fp64
 accumulation: at most one fp32 ulp from the oracle), and the Q8_0 GEMV
-(exact int32 group dots; outputs at most one ulp away)."""
+(exact int32 group dots; outputs at most one ulp away), and the Q4_0 GEMV
+(same bar: exact group dots against 4-bit weights, one ulp on outputs)."""
 import numpy as np
 import pytest
 
@@ -137,3 +138,83 @@ def test_gemv_rejects_bad_shapes():
         l2d.gemv(l2d.F32, W, None, x, 3, 4)  # odd rows
     with pytest.raises(l2d.L2DError):
         l2d.gemv(l2d.Q8_0, W, W, x, 2, 48, 64)  # gs does not divide cols
+
+
+# Q4_0: small ragged shapes (group counts not a multiple of the 64- and
+# 128-group chunks), the 7B and 13B matvec shapes (q/k/v fused, w1/w3 fused,
+# w2, classifier) and the longest accepted input
+Q4_SHAPES = [(2, 32), (6, 96), (34, 768), (130, 2080), (258, 4128), (4096, 4096), (12288, 4096),
+             (22016, 4096), (4096, 11008), (32000, 4096), (15360, 5120), (5120, 13824), (2, 65536)]
+
+
+def _q40_weights(rows, cols, rng):
+    """Quantised normal weights for small shapes, random bytes and scales
+    for large ones (every nibble pattern is valid Q4_0 data)."""
+    if rows * cols <= 1 << 22:
+        W = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+        q, s = oracle.quantize_q40(W.reshape(-1))
+        return q.reshape(rows, cols // 2), s.reshape(rows, cols // 32)
+    Q = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    S = (rng.uniform(-1.5, 1.5, (rows, cols // 32)) * 3e-3).astype(np.float32)
+    return Q, S
+
+
+@pytest.mark.parametrize("rows,cols", Q4_SHAPES)
+def test_gemv_q40_vs_oracle(rows, cols):
+    torch = need_gpu()
+    log(f"  q4 gemv {rows}x{cols}")
+    rng = np.random.default_rng(rows * 3 + cols)
+    Q, S = _q40_weights(rows, cols, rng)
+    x = synth.normal_f32(rows + 5 * cols, 4, cols, 1.0)
+    gd = torch.zeros(rows * (cols // 32), dtype=torch.int32, device="cuda")
+    out = l2d.gemv(l2d.Q4_0, torch.from_numpy(Q).cuda(), torch.from_numpy(S).cuda(),
+                   torch.from_numpy(x).cuda(), rows, cols, 32, group_dots=gd)
+    g = out.cpu().numpy()
+    r = oracle.matvec_q40(Q, S, x)
+    xq, _ = oracle.quantize(x, 32)
+    dots = gd.cpu().numpy().reshape(rows, cols // 32)
+    for i in sorted(set(range(0, rows, max(1, rows // 64))) | {rows - 1}):
+        np.testing.assert_array_equal(dots[i], oracle.group_dots_q40(Q[i], xq))
+    u = _report(f"q4 {rows}x{cols}", g, r)
+    assert u.max() <= 1
+    assert np.mean(u == 0) > 0.99
+
+
+def test_gemv_q40_extreme_codes():
+    """Codes -8 and 7 only against inputs at +-127 (largest group dots,
+    32 * 8 * 127), an all-zero input and an adversarial one."""
+    torch = need_gpu()
+    rows, cols = 64, 4096
+    lo_hi = np.where(np.arange(rows * cols // 2).reshape(rows, cols // 2) % 3 == 0, 0x00, 0xFF)
+    Q = lo_hi.astype(np.uint8)
+    Q[::5] = 0x0F  # low nibbles 7, high nibbles -8
+    S = np.full((rows, cols // 32), -1e-3, np.float32)
+    for x in (np.full(cols, 2.5, np.float32),
+              np.where(np.arange(cols) % 2 == 0, 3.0, -3.0).astype(np.float32),
+              _adversarial(cols, 32, np.random.default_rng(5))):
+        gd = torch.zeros(rows * (cols // 32), dtype=torch.int32, device="cuda")
+        out = l2d.gemv(l2d.Q4_0, torch.from_numpy(Q).cuda(), torch.from_numpy(S).cuda(),
+                       torch.from_numpy(x).cuda(), rows, cols, 32, group_dots=gd)
+        xq, _ = oracle.quantize(x, 32)
+        dots = gd.cpu().numpy().reshape(rows, cols // 32)
+        for i in range(rows):
+            np.testing.assert_array_equal(dots[i], oracle.group_dots_q40(Q[i], xq))
+        u = ulp_diff(out.cpu().numpy(), oracle.matvec_q40(Q, S, x))
+        assert u.max() <= 1
+    assert np.abs(dots).max() <= 32 * 8 * 127
+    z = l2d.gemv(l2d.Q4_0, torch.from_numpy(Q).cuda(), torch.from_numpy(S).cuda(),
+                 torch.zeros(cols, device="cuda"), rows, cols, 32)
+    assert (z.cpu().numpy() == 0).all()
+
+
+def test_gemv_q40_rejects_bad_shapes():
+    torch = need_gpu()
+    W = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    S = torch.zeros(8, device="cuda")
+    x = torch.zeros(64, device="cuda")
+    with pytest.raises(l2d.L2DError):
+        l2d.gemv(l2d.Q4_0, W, S, x, 2, 64, 64)  # group size other than 32
+    with pytest.raises(l2d.L2DError):
+        l2d.gemv(l2d.Q4_0, W, S, x, 2, 48, 32)  # 32 does not divide cols
+    with pytest.raises(l2d.L2DError):
+        l2d.gemv(l2d.Q4_0, W, None, x, 2, 64, 32)  # no scales
