@@ -31,7 +31,7 @@ extern "C" {
 #define L2D_F32 0  /* fp32 weights and activations (run.c) */
 #define L2D_Q8_0 1 /* int8 weight/activation codes, fp32 group scales (runq.c) */
 #define L2D_Q4_0 2 /* 4-bit weight codes in groups of 32, fp32 group scales (l2d_gemv only;
-                      the 4-bit variant the pomoai.com hub page names) */
+                      the 4-bit variant the ainews article names) */
 
 #define L2D_OK 0
 #define L2D_EINVAL (-1)  /* bad argument: config, group size, token, pos, size */
@@ -199,7 +199,8 @@ int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache);
  * Q8_0 (gitcode porting guide, INT8 quantisation section): x is quantised
  * inside the kernel with the weights' group size, as in the decode step;
  * gs a power of two in [16, 256].
- * Q4_0 (4-bit variant named on the pomoai.com hub page; read as): gs must be
+ * Q4_0 (4-bit variant named in the ainews article's technical deep dive and
+ * tables, and as a next step in the gitcode guide; read as): gs must be
  * 32; code c of a group is stored as c + 8 in [0, 15], byte b of a group's
  * 16 bytes holding code b in its low nibble and code b + 16 in its high
  * nibble; the scale is the group's value of largest magnitude divided by

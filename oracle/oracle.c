@@ -374,9 +374,11 @@ int or_matvec_q80(const int8_t* Q, const float* S, const float* x, int64_t rows,
 }
 
 /*
- * ---- 4-bit group quantisation ("Q4_0"). The hub page's comparison table
- * and notes name a 4-bit Q4_0 variant of the engine, a format "similar to
- * llama.cpp's", without giving its layout. Reading, in the manner of the
+ * ---- 4-bit group quantisation ("Q4_0"). The ainews article (technical
+ * deep dive, benchmark and comparison tables) names a 4-bit Q4_0 variant of
+ * the engine in a llama.cpp-like format, and the gitcode guide (future
+ * optimisation directions) lists 4-bit quantisation after llama.cpp's
+ * format as a next step; neither gives the layout. Reading, in the manner of the
  * gitcode guide's Q8_0 listing: groups of 32 values; m is the group's value
  * of largest magnitude (the first one among equal magnitudes); the scale is
  * the fp32 quotient m / -8 (0 for an all-zero group); a code is the fp32

@@ -1,5 +1,7 @@
 """Pins of the oracle's 4-bit group quantisation and Q4_0 matvec (the
-hub page's Q4_0 variant; reading stated in golden/q40_handworked.json).
+Q4_0 variant named in the ainews article's technical deep dive and tables,
+and as a next step in the gitcode guide; reading stated in
+golden/q40_handworked.json).
 
 - hand-worked groups: scales, clamped codes, tie rules and the nibble order;
 - invariants on random data: codes in [-8, 7], the largest-magnitude value
