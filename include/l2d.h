@@ -131,6 +131,27 @@ const float* l2d_forward(l2d_ctx* ctx, int32_t token, int32_t pos);
 const float* l2d_forward_greedy(l2d_ctx* ctx, int32_t pos);
 
 /*
+ * Batched prompt prefill: the same result as n calls l2d_forward(tokens[i],
+ * pos0 + i), i = 0..n-1 (prompt tokens are fed through the forward pass one
+ * position after another: gitcode guide, main loop; mht18 essay, section 2.3,
+ * the toy forward pass over a sequence), computed as int8 matrix products
+ * over chunks of up to 512 tokens (MFMA): every token's matmul inputs are
+ * quantised on their own, every output is the same fp64 sum of exact int32
+ * group dots, attention of token i covers slots 0..pos0 + i. Writes K/V slots
+ * pos0 .. pos0 + n - 1 of every layer and returns, like l2d_forward, the
+ * device logits of the last token; l2d_last_token gives its argmax (or
+ * sampled token), and l2d_forward_greedy(ctx, pos0 + n) may follow.
+ * tokens is a host array of n ids, read before the call returns.
+ * Asynchronous on the context's stream; the first call allocates the chunk
+ * buffers (about 512 x (3 dim + 2 hidden_dim) x 4 bytes).
+ * Needs Q8_0 weights with group size 64, 128 or 256 and n_heads / n_kv_heads
+ * dividing 8. Returns NULL on error: n <= 0, pos0 < 0, pos0 + n > seq_len,
+ * a token outside [0, vocab), an unsupported model (L2D_EINVAL, see
+ * l2d_last_error), L2D_ENOMEM, L2D_EHIP.
+ */
+const float* l2d_prefill(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0);
+
+/*
  * Next-token selection of the following forwards (mht18 essay, section 3.2:
  * the logits go through a softmax, the next token is a random draw from
  * that distribution, the temperature scaling the logits first).
@@ -251,6 +272,15 @@ void* l2d_stream(l2d_ctx* ctx);
  * 6 step start (embedding row). Synchronous.
  */
 int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, double* avg_seconds);
+
+/*
+ * l2d_prefill with HIP events stamped at every kernel's start and end;
+ * avg_seconds[8] receives the mean duration per launch of each kernel class:
+ * 0 norm + quantise, 1 q/k/v matmul (+RoPE, cache write), 2 attention,
+ * 3 output matmul (+residual), 4 w1/w3 matmul (+SwiGLU), 5 w2 matmul
+ * (+residual), 6 last token's step start, 7 classifier. Synchronous.
+ */
+int l2d_profile_prefill(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0, double* avg_seconds);
 
 /* 1: replay the captured graph (default); 0: launch the step's kernels one by one.
  * Applies when the persistent step kernel is off (l2d_use_persistent). */

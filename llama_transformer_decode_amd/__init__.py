@@ -73,6 +73,9 @@ def lib():
                                         ctypes.POINTER(_vp)]),
             "l2d_forward": (_vp, [_vp, ctypes.c_int32, ctypes.c_int32]),
             "l2d_forward_greedy": (_vp, [_vp, ctypes.c_int32]),
+            "l2d_prefill": (_vp, [_vp, _vp, ctypes.c_int32, ctypes.c_int32]),
+            "l2d_profile_prefill": (ctypes.c_int, [_vp, _vp, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.POINTER(ctypes.c_double)]),
             "l2d_sync": (ctypes.c_int, [_vp]),
             "l2d_last_token": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_int32)]),
             "l2d_read_logits": (ctypes.c_int, [_vp, _vp]),
@@ -109,9 +112,10 @@ EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l
            "l2d_last_token", "l2d_read_logits", "l2d_quantize_q80", "l2d_reset_kv", "l2d_free",
            "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
-           "l2d_set_sampling")
+           "l2d_set_sampling", "l2d_prefill", "l2d_profile_prefill")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
+PREFILL_CLASSES = ("prep", "qkv", "attn", "wo", "w13", "w2", "start", "cls")
 
 
 def last_error(ctx=None) -> str:
@@ -211,6 +215,22 @@ class Context:
         if not p:
             raise L2DError(EINVAL, self.error())
         return p
+
+    def prefill(self, tokens, pos0: int = 0) -> int:
+        """Batched prefill of the prompt tokens at pos0..; returns the device
+        address of the last token's logits."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        p = lib().l2d_prefill(self._h, _np_ptr(t), int(t.size), int(pos0))
+        if not p:
+            raise L2DError(EINVAL, self.error())
+        return p
+
+    def prefill_profile(self, tokens, pos0: int = 0) -> dict:
+        """Mean kernel seconds per class of one batched prefill."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        out = (ctypes.c_double * len(PREFILL_CLASSES))()
+        _check(lib().l2d_profile_prefill(self._h, _np_ptr(t), int(t.size), int(pos0), out), self._h)
+        return {k: out[i] for i, k in enumerate(PREFILL_CLASSES)}
 
     def sync(self):
         _check(lib().l2d_sync(self._h), self._h)

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libl2d.so")
 
-SOURCES = ["gemv.hip", "attn.hip", "step.hip", "mega.hip", "ctx.cpp", "blob.cpp"]
+SOURCES = ["gemv.hip", "attn.hip", "step.hip", "mega.hip", "prefill.hip", "ctx.cpp", "blob.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

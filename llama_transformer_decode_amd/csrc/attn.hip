@@ -53,6 +53,9 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     r.r0 = r0;
     r.n = min(T - r0, per);
     r.fresh = -1;  // the kernel boundary orders the cache write before these loads
+    r.Gt = G;  // one query token: no causal mask within the range
+    r.qstride = 0;
+    r.last0 = 0x3fffffff;
     attn_range<KG, kAThreads>(r, smem);
 
     if (nact == 1) {

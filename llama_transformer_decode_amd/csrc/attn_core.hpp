@@ -21,6 +21,14 @@
 //           accumulators.
 // On return the slot partial sums of the values sit in LDS (attn_value sums
 // them in a fixed order) with the running (m, l) of each head.
+//
+// Several query tokens at once (batched prefill): the G "heads" of a range
+// may be Gt query heads of each of G / Gt consecutive tokens. Head h then
+// belongs to token h / Gt, reads its query row at q + (h / Gt) * qstride +
+// (h % Gt) * hs, and sees positions t <= last0 + h / Gt only (causal mask:
+// later positions score -inf and add exactly nothing). A range starting at
+// position 0 keeps every head's running maximum finite from its first
+// sub-chunk on.
 #pragma once
 
 #include "device.hpp"
@@ -103,6 +111,9 @@ struct AttnRange {
     int kvd, hs, G, g;
     int r0, n;        // positions [r0, r0 + n)
     int fresh;        // the position written in this launch (device-scope loads), or -1
+    int Gt;           // query heads per token (= G for a single token)
+    int qstride;      // floats between consecutive tokens' query rows
+    int last0;        // last position the first token may see (causal limit)
 };
 
 // K and V rows of positions [t0, t0 + n) (n <= sc). Rows written in an
@@ -174,7 +185,10 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
     KVBuf A, B;
     load_kv<NT>(A, r, a, r0, min(a.sc, n));
     if (nsub > 1) load_kv<NT>(B, r, a, r0 + a.sc, min(a.sc, n - a.sc));
-    for (int i = tid; i < G * hs; i += NT) L.qs[i] = ld_dev(r.q + i);
+    for (int i = tid; i < G * hs; i += NT) {
+        const int h = i / hs;
+        L.qs[i] = ld_dev(r.q + (size_t)(h / r.Gt) * r.qstride + (size_t)(h % r.Gt) * hs + i % hs);
+    }
     if (tid < G) {
         L.m_run[tid] = -INFINITY;
         L.l_run[tid] = 0.0;
@@ -213,7 +227,8 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
             }
             if (sub == 0 && tl < m)
 #pragma unroll
-                for (int h = 0; h < KG; h++) L.sc[(size_t)h * a.sc + tl] = sv[h] * scale;
+                for (int h = 0; h < KG; h++)
+                    L.sc[(size_t)h * a.sc + tl] = t0 + tl <= r.last0 + h / r.Gt ? sv[h] * scale : -INFINITY;
         }
         __syncthreads();
         for (int h = wave; h < G; h += NT / kWave) {

@@ -184,6 +184,29 @@ struct KernelTimer {
 
 enum { KC_QKV = 0, KC_ATTN, KC_WO, KC_W13, KC_W2, KC_CLS, KC_BEGIN, KC_COUNT };
 
+// Final RMSNorm of ctx->x -> classifier -> logits and argmax (or sampled
+// token) of the step recorded in the step record.
+int enqueue_classifier(l2d_ctx* ctx, KernelTimer* kt, int cls)
+{
+    GemvParams p;
+    memset(&p, 0, sizeof(p));
+    p.gs = (int32_t)ctx->gs;
+    p.eps = ctx->cfg.norm_eps;
+    p.step = ctx->step;
+    p.W = ctx->wcls;
+    p.Ws = ctx->dt == DT_Q8 ? ctx->wcls_s : nullptr;
+    p.M = ctx->V;
+    p.K = ctx->d;
+    p.x = ctx->x;
+    p.gain = ctx->rms_final;
+    p.out = ctx->logits;
+    p.argmax = ctx->argmax;
+    if (kt) HIP_TRY(ctx, kt->next(cls));
+    HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_LOGITS, p, ctx->max_blocks, ctx->stream,
+                             kt ? &kt->cur : nullptr));
+    return L2D_OK;
+}
+
 // All kernels of one decode step after the step-start kernel.
 int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
 {
@@ -279,23 +302,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         if (kt) HIP_TRY(ctx, kt->next(KC_W2));
         HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
     }
-    // final RMSNorm -> classifier -> argmax
-    GemvParams p;
-    memset(&p, 0, sizeof(p));
-    p.gs = (int32_t)gs;
-    p.eps = ctx->cfg.norm_eps;
-    p.step = ctx->step;
-    p.W = ctx->wcls;
-    p.Ws = ctx->dt == DT_Q8 ? ctx->wcls_s : nullptr;
-    p.M = ctx->V;
-    p.K = d;
-    p.x = ctx->x;
-    p.gain = ctx->rms_final;
-    p.out = ctx->logits;
-    p.argmax = ctx->argmax;
-    if (kt) HIP_TRY(ctx, kt->next(KC_CLS));
-    HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_LOGITS, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
-    return L2D_OK;
+    return enqueue_classifier(ctx, kt, KC_CLS);
 }
 
 int setup_mega(l2d_ctx* ctx, int cus);
@@ -893,6 +900,206 @@ int l2d_gemv_profile(int32_t dtype, const void* const* W, const float* const* W_
         sum += ms * 1e-3;
     }
     *avg_seconds = sum / reps;
+    return L2D_OK;
+}
+
+// ---------------------------------------------------------------- prefill
+
+namespace {
+
+constexpr int kPrefillChunk = 512;  // tokens per batched pass
+enum { PC_PREP = 0, PC_QKV, PC_ATTN, PC_WO, PC_W13, PC_W2, PC_START, PC_CLS, PC_COUNT };
+
+bool prefill_supported(const l2d_ctx* ctx)
+{
+    return ctx->dt == DT_Q8 && (ctx->gs == 64 || ctx->gs == 128 || ctx->gs == 256) &&
+           prefill_attn_supported((int)ctx->G, (int)ctx->hs);
+}
+
+int prefill_buffers(l2d_ctx* ctx)
+{
+    if (ctx->pf_cap > 0) return L2D_OK;
+    int64_t cap = ctx->S < kPrefillChunk ? ctx->S : kPrefillChunk;
+    cap = (cap + 7) / 8 * 8;  // whole token blocks of the attention kernel
+    const int64_t kmax = ctx->d > ctx->h ? ctx->d : ctx->h;
+    ALLOC(ctx->pf_tok, (size_t)cap * 4);
+    ALLOC(ctx->pf_x, (size_t)(cap * ctx->d) * 4);
+    ALLOC(ctx->pf_q, (size_t)(cap * ctx->d) * 4);
+    ALLOC(ctx->pf_o, (size_t)(cap * ctx->d) * 4);
+    ALLOC(ctx->pf_h, (size_t)(cap * ctx->h) * 4);
+    ALLOC(ctx->pf_aq, (size_t)(cap * kmax));
+    ALLOC(ctx->pf_as, (size_t)(cap * (kmax / ctx->gs)) * 4);
+    ALLOC(ctx->pf_cos, (size_t)(cap * (ctx->hs / 2)) * 4);
+    ALLOC(ctx->pf_sin, (size_t)(cap * (ctx->hs / 2)) * 4);
+    // rows past a chunk's last token are read (never used) by the attention
+    // kernel's last token block: keep them finite
+    HIP_TRY(ctx, hipMemsetAsync(ctx->pf_q, 0, (size_t)(cap * ctx->d) * 4, ctx->stream));
+    ctx->pf_cap = (int)cap;
+    return L2D_OK;
+}
+
+// One chunk of m <= pf_cap prompt tokens (already in pf_tok) at positions
+// pos .. pos + m - 1: every layer, leaving the residual rows in pf_x and the
+// K/V rows in the cache.
+int enqueue_prefill_chunk(l2d_ctx* ctx, int m, int pos, KernelTimer* kt)
+{
+    const int64_t d = ctx->d, h = ctx->h, kvd = ctx->kvd, gs = ctx->gs;
+    const int64_t nqkv = d + 2 * kvd;
+    hipStream_t s = ctx->stream;
+    auto ev = [&](int c) -> const LaunchEvents* {
+        if (!kt) return nullptr;
+        if (kt->next(c) != hipSuccess) return nullptr;
+        return &kt->cur;
+    };
+    PrefillEmbedParams e;
+    e.emb = ctx->emb;
+    e.emb_s = ctx->emb_s;
+    e.dtype = ctx->dt;
+    e.gs = (int32_t)gs;
+    e.d = d;
+    e.tokens = ctx->pf_tok;
+    e.m = m;
+    e.x = ctx->pf_x;
+    HIP_TRY(ctx, launch_prefill_embed(e, s));
+    HIP_TRY(ctx, launch_prefill_rope(ctx->freqs, (int)ctx->hs, pos, m, ctx->pf_cos, ctx->pf_sin, s));
+
+    auto prep = [&](const float* x, const float* gain, int64_t K) -> hipError_t {
+        PrefillPrepParams q;
+        q.x = x;
+        q.gain = gain;
+        q.eps = ctx->cfg.norm_eps;
+        q.K = K;
+        q.gs = (int32_t)gs;
+        q.m = m;
+        q.q = ctx->pf_aq;
+        q.s = ctx->pf_as;
+        return launch_prefill_prep(q, gain != nullptr, s, ev(PC_PREP));
+    };
+    for (int64_t l = 0; l < ctx->L; l++) {
+        PrefillGemmParams g;
+        memset(&g, 0, sizeof(g));
+        g.gs = (int32_t)gs;
+        g.m = m;
+        g.aq = ctx->pf_aq;
+        g.as = ctx->pf_as;
+
+        HIP_TRY(ctx, prep(ctx->pf_x, ctx->rms_att + l * d, d));
+        g.W = (const int8_t*)ctx->wqkv + (size_t)(l * nqkv * d);
+        g.Ws = ctx->wqkv_s + (size_t)(l * nqkv * d / gs);
+        g.N = nqkv;
+        g.K = d;
+        g.out = ctx->pf_q;
+        g.ldo = d;
+        g.kcache = ctx->kc + l * ctx->S * kvd;
+        g.vcache = ctx->vc + l * ctx->S * kvd;
+        g.d = (int32_t)d;
+        g.kvd = (int32_t)kvd;
+        g.hs = (int32_t)ctx->hs;
+        g.pos0 = pos;
+        g.rcos = ctx->pf_cos;
+        g.rsin = ctx->pf_sin;
+        HIP_TRY(ctx, launch_prefill_gemm(EPI_QKV, g, s, ev(PC_QKV)));
+
+        PrefillAttnParams a;
+        a.q = ctx->pf_q;
+        a.kc = ctx->kc + l * ctx->S * kvd;
+        a.vc = ctx->vc + l * ctx->S * kvd;
+        a.o = ctx->pf_o;
+        a.d = (int32_t)d;
+        a.kvd = (int32_t)kvd;
+        a.hs = (int32_t)ctx->hs;
+        a.G = (int32_t)ctx->G;
+        a.nkv = (int32_t)ctx->nkv;
+        a.m = m;
+        a.pos0 = pos;
+        HIP_TRY(ctx, launch_prefill_attn(a, s, ev(PC_ATTN)));
+
+        HIP_TRY(ctx, prep(ctx->pf_o, nullptr, d));
+        g.W = (const int8_t*)ctx->wo + (size_t)(l * d * d);
+        g.Ws = ctx->wo_s + (size_t)(l * d * d / gs);
+        g.N = d;
+        g.K = d;
+        g.out = ctx->pf_x;
+        g.ldo = d;
+        HIP_TRY(ctx, launch_prefill_gemm(EPI_RESID, g, s, ev(PC_WO)));
+
+        HIP_TRY(ctx, prep(ctx->pf_x, ctx->rms_ffn + l * d, d));
+        g.W = (const int8_t*)ctx->w13 + (size_t)(l * 2 * h * d);
+        g.Ws = ctx->w13_s + (size_t)(l * 2 * h * d / gs);
+        g.N = 2 * h;
+        g.K = d;
+        g.out = ctx->pf_h;
+        g.ldo = h;
+        HIP_TRY(ctx, launch_prefill_gemm(EPI_SWIGLU, g, s, ev(PC_W13)));
+
+        HIP_TRY(ctx, prep(ctx->pf_h, nullptr, h));
+        g.W = (const int8_t*)ctx->w2 + (size_t)(l * d * h);
+        g.Ws = ctx->w2_s + (size_t)(l * d * h / gs);
+        g.N = d;
+        g.K = h;
+        g.out = ctx->pf_x;
+        g.ldo = d;
+        HIP_TRY(ctx, launch_prefill_gemm(EPI_RESID, g, s, ev(PC_W2)));
+    }
+    return L2D_OK;
+}
+
+int prefill_impl(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0, KernelTimer* kt)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "prefill: null context");
+    if (!tokens || n <= 0 || pos0 < 0 || (int64_t)pos0 + n > ctx->S)
+        return fail(ctx, L2D_EINVAL, "prefill: need tokens, n > 0 and 0 <= pos0, pos0 + n <= seq_len");
+    for (int32_t i = 0; i < n; i++)
+        if (tokens[i] < 0 || tokens[i] >= ctx->V) return fail(ctx, L2D_EINVAL, "prefill: token outside [0, vocab)");
+    if (!prefill_supported(ctx))
+        return fail(ctx, L2D_EINVAL, "prefill: needs Q8_0 weights with group size 64, 128 or 256 and "
+                                     "n_heads / n_kv_heads dividing 8");
+    int rc = prefill_buffers(ctx);
+    if (rc != L2D_OK) return rc;
+    int m = 0;
+    for (int32_t c0 = 0; c0 < n; c0 += m) {
+        m = n - c0 < ctx->pf_cap ? n - c0 : ctx->pf_cap;
+        HIP_TRY(ctx, hipMemcpyAsync(ctx->pf_tok, tokens + c0, (size_t)m * 4, hipMemcpyHostToDevice, ctx->stream));
+        rc = enqueue_prefill_chunk(ctx, m, pos0 + c0, kt);
+        if (rc != L2D_OK) return rc;
+    }
+    // the last token's step: step record, argmax slots and the classifier on
+    // its residual row (the step-start kernel's embedding row is replaced)
+    const int32_t last = pos0 + n - 1;
+    if (kt) HIP_TRY(ctx, kt->next(PC_START));
+    HIP_TRY(ctx, begin(ctx, tokens[n - 1], last, false, kt ? &kt->cur : nullptr));
+    HIP_TRY(ctx, hipMemcpyAsync(ctx->x, ctx->pf_x + (size_t)(m - 1) * ctx->d, (size_t)ctx->d * 4,
+                                hipMemcpyDeviceToDevice, ctx->stream));
+    rc = enqueue_classifier(ctx, kt, PC_CLS);
+    if (rc != L2D_OK) return rc;
+    ctx->last_pos = last;
+    return L2D_OK;
+}
+
+}  // namespace
+
+const float* l2d_prefill(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0)
+{
+    if (prefill_impl(ctx, tokens, n, pos0, nullptr) != L2D_OK) return nullptr;
+    return ctx->logits;
+}
+
+int l2d_profile_prefill(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0, double* avg_seconds)
+{
+    if (!ctx || !avg_seconds) return fail(ctx, L2D_EINVAL, "profile_prefill: null argument");
+    KernelTimer kt;
+    int rc = prefill_impl(ctx, tokens, n, pos0, &kt);
+    if (rc != L2D_OK) return rc;
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    double sum[PC_COUNT] = {0};
+    int cnt[PC_COUNT] = {0};
+    for (size_t i = 0; i < kt.used / 2; i++) {
+        float ms = 0.f;
+        HIP_TRY(ctx, hipEventElapsedTime(&ms, kt.ev[2 * i], kt.ev[2 * i + 1]));
+        sum[kt.cls[i]] += ms * 1e-3;
+        cnt[kt.cls[i]] += 1;
+    }
+    for (int c = 0; c < PC_COUNT; c++) avg_seconds[c] = cnt[c] ? sum[c] / cnt[c] : 0.0;
     return L2D_OK;
 }
 

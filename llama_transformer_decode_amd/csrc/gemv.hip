@@ -506,11 +506,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     const int64_t nch = DT == DT_F32 ? (p.K / 4 + kWave * U - 1) / (kWave * U)
                       : DT == DT_Q8  ? (p.K / p.gs + 63) / 64
                                      : (p.K / 32 + kWave * U - 1) / (kWave * U);
-    // balanced contiguous range of tiles for this wave
+    // balanced contiguous range of tiles for this wave; one-row tiles that
+    // feed a row-pair epilogue (RoPE, SwiGLU) are handed out in pairs, and
+    // the even row's sum waits in a register for the odd row's
+    constexpr bool PAIR1 = RPW == 1 && (EPI == EPI_QKV || EPI == EPI_SWIGLU);
     const int64_t tiles = (p.M + RPW - 1) / RPW;
+    const int64_t units = PAIR1 ? tiles / 2 : tiles;
     const int64_t nw = (int64_t)gridDim.x * kWaves;
     const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
-    const int64_t t_beg = tiles * gw / nw, t_end = tiles * (gw + 1) / nw;
+    const int64_t t_beg = (PAIR1 ? 2 : 1) * (units * gw / nw), t_end = (PAIR1 ? 2 : 1) * (units * (gw + 1) / nw);
     const int64_t iters = (t_end - t_beg) * nch;
     const int pos = (EPI == EPI_QKV || EPI == EPI_LOGITS) ? p.step[kStepPos] : 0;
     uint64_t seed = 0;
@@ -553,6 +557,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 #pragma unroll
     for (int r = 0; r < RPW; r++) acc[r] = 0.0;
     unsigned long long best = 0;
+    double pend = 0.0;  // PAIR1: the even row of the current pair
     int64_t tile = t_beg, ch = 0;
     for (int64_t it = 0; it < iters; it += NBUF) {
 #pragma unroll
@@ -564,7 +569,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
                 for (int r = 0; r < RPW; r++) acc[r] = wave_sum_to_last(acc[r]);
                 if (lane == kWave - 1) {
                     const EpiIn ein{pos, buf[k].res, rcos, rsin, temp, seed};
-                    gemv_epilogue<EPI>(p, tile * RPW, RPW, acc, best, ein);
+                    if constexpr (PAIR1) {
+                        if ((tile & 1) == 0) {
+                            pend = acc[0];
+                        } else {
+                            const double pr[2] = {pend, acc[0]};
+                            gemv_epilogue<EPI>(p, tile - 1, 2, pr, best, ein);
+                        }
+                    } else {
+                        gemv_epilogue<EPI>(p, tile * RPW, RPW, acc, best, ein);
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < RPW; r++) acc[r] = 0.0;
@@ -642,7 +656,8 @@ static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s, 
 // ring beat three or four (fewer registers, more waves); Q8_0 rows are best
 // one per tile when the matrix gives a wave fewer than three two-row tiles
 // (output projection, w2), two per tile otherwise. Epilogues that combine a
-// row pair (RoPE, SwiGLU) always get an even number of rows per tile.
+// row pair (RoPE, SwiGLU) get an even number of rows per tile, or one-row
+// tiles handed out in pairs (group sizes 128 and 256).
 template <int DT, int PRO, int EPI, bool DBG>
 static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t s, const LaunchEvents* ev)
 {

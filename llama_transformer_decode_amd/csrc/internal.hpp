@@ -90,6 +90,65 @@ size_t attention_lds_bytes(int G, int hs, int unused);
 bool attention_supported(int G, int hs);
 int attention_positions_per_subchunk(int hs);
 
+// ---- batched prefill (prefill.hip)
+
+struct PrefillEmbedParams {
+    const void* emb;       // embedding table, device layout
+    const float* emb_s;    // Q8_0 scales
+    int32_t dtype, gs;
+    int64_t d;
+    const int32_t* tokens; // [m]
+    int32_t m;
+    float* x;              // [m][d]
+};
+hipError_t launch_prefill_embed(const PrefillEmbedParams& p, hipStream_t s);
+
+// cos / sin tables [m][hs/2] of positions pos0 .. pos0 + m - 1
+hipError_t launch_prefill_rope(const float* freqs, int hs, int pos0, int m, float* rcos, float* rsin,
+                               hipStream_t s);
+
+struct PrefillPrepParams {
+    const float* x;     // [m][K]
+    const float* gain;  // RMSNorm gain [K] (norm only)
+    double eps;
+    int64_t K;
+    int32_t gs, m;
+    int8_t* q;          // [m][K] codes, plain order
+    float* s;           // [m][K/gs] scales
+};
+hipError_t launch_prefill_prep(const PrefillPrepParams& p, bool norm, hipStream_t s,
+                               const LaunchEvents* ev = nullptr);
+
+struct PrefillGemmParams {
+    const void* W;      // Q8_0 codes [N][K], device (group-interleaved) layout
+    const float* Ws;    // [N][K/gs]
+    int64_t N, K;
+    int32_t gs, m;
+    const int8_t* aq;   // [m][K] input codes, plain order
+    const float* as;    // [m][K/gs]
+    float* out;         // EPI_STORE / EPI_QKV (q rows) / EPI_SWIGLU: [m][ldo]; EPI_RESID: += into [m][ldo]
+    int64_t ldo;
+    // EPI_QKV
+    float* kcache;      // this layer's [seq_len][kv_dim]
+    float* vcache;
+    int32_t d, kvd, hs, pos0;
+    const float* rcos;  // [m][hs/2]
+    const float* rsin;
+};
+hipError_t launch_prefill_gemm(int epi, const PrefillGemmParams& p, hipStream_t s,
+                               const LaunchEvents* ev = nullptr);
+size_t prefill_gemm_grid(int64_t N, int m);
+
+struct PrefillAttnParams {
+    const float* q;     // [>= m rounded up to the token block][d]
+    const float* kc;    // this layer's caches
+    const float* vc;
+    float* o;           // [m][d]
+    int32_t d, kvd, hs, G, nkv, m, pos0;
+};
+bool prefill_attn_supported(int G, int hs);
+hipError_t launch_prefill_attn(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev = nullptr);
+
 struct BeginParams {
     const void* emb;
     const float* emb_s;

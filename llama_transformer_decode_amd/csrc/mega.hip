@@ -529,6 +529,9 @@ __device__ __forceinline__ void attention_phase(const MegaParams& P, int l, unsi
         r.r0 = c * per;
         r.n = min(T - r.r0, per);
         r.fresh = P.pos;
+        r.Gt = G;  // one query token: no causal mask within the range
+        r.qstride = 0;
+        r.last0 = 0x3fffffff;
         attn_range<KG, kMT>(r, smem);
         float* og = P.o + (size_t)g * G * hs;
         if (nact == 1) {

@@ -79,6 +79,20 @@ struct l2d_ctx {
     double* mpart_o = nullptr;
     double* mpart_ml = nullptr;
 
+    // batched prefill (allocated by the first l2d_prefill): chunk capacity
+    // in tokens (a multiple of 8), token ids, residual rows, q rows,
+    // attention outputs, FFN hidden rows, quantised matmul inputs, RoPE tables
+    int pf_cap = 0;
+    int32_t* pf_tok = nullptr;
+    float* pf_x = nullptr;   // [cap][d]
+    float* pf_q = nullptr;   // [cap][d]
+    float* pf_o = nullptr;   // [cap][d]
+    float* pf_h = nullptr;   // [cap][h]
+    int8_t* pf_aq = nullptr; // [cap][max(d, h)]
+    float* pf_as = nullptr;  // [cap][max(d, h) / gs]
+    float* pf_cos = nullptr; // [cap][hs / 2]
+    float* pf_sin = nullptr;
+
     int trace_layer = -1;
     int8_t* trace_q[4] = {nullptr, nullptr, nullptr, nullptr};
     float* trace_s[4] = {nullptr, nullptr, nullptr, nullptr};

@@ -56,6 +56,28 @@ def test_decode_small(name, dtype, steps, mode):
     st.assert_ok()
 
 
+GS_Q8 = synth.Config("gsq8", 256, 512, 2, 8, 2, 320, 48, 13, (synth.Q8_0,))
+
+
+@pytest.mark.parametrize("gs", [16, 32, 128, 256])
+def test_decode_q8_group_sizes(gs):
+    """Q8_0 at every group size the decode step takes besides 64: tile
+    shapes change with the group size (down to one-row tiles handed out in
+    pairs to the RoPE and SwiGLU epilogues at 128 and 256)."""
+    need_gpu()
+    cfg = GS_Q8
+    blob = synth.make_blob(cfg, synth.Q8_0, gs=gs)
+    orc = oracle.Model(blob, synth.Q8_0, gs=gs)
+    forced, _ = synth.trajectory_plan(cfg, 40)
+    fed, _, _ = oracle.trajectory(orc, forced, 40, keep_logits=False)
+    orc.reset_kv()
+    with l2d.Context(blob, synth.Q8_0, group_size=gs) as ctx:
+        set_mode(ctx, "graph")
+        st = decode_and_compare(ctx, orc, fed, label=f"gsq8 gs{gs}")
+    orc.close()
+    st.assert_ok()
+
+
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", [synth.F32, synth.Q8_0])
 def test_decode_110m_full_trajectory(dtype, mode):

@@ -1,0 +1,149 @@
+"""Batched prompt prefill (int8 MFMA matmuls, causal attention over token
+blocks) against the oracle's token-by-token decode, through the C ABI: the
+K/V cache rows the prefill writes, the last token's logits and argmax, and
+the decode that continues from it on the device.
+
+Small models cover group sizes 64, 128 and 256, GQA ratios 1, 2 and 8 (token
+blocks of 8, 4 and 1 per attention workgroup), ragged token counts, prompts
+longer than one 512-token chunk and prefill in two calls at pos0 > 0; the
+7B shape runs at full size."""
+import gc
+
+import numpy as np
+import pytest
+
+import llama_transformer_decode_amd as l2d
+import oracle
+import synth
+from gpu_util import Stats, log, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+TINY_Q8 = synth.Config("tinyq8", 128, 256, 3, 4, 2, 320, 64, 11, (synth.Q8_0,))
+GQA8_Q8 = synth.Config("gqa8q8", 256, 512, 2, 8, 1, 320, 96, 12, (synth.Q8_0,))
+
+
+def _check_cache(ctx, orc, lo: int, hi: int, st: Stats):
+    kc, vc = ctx.kv_cache()
+    st.add("k", kc[:, lo:hi].cpu().numpy(), orc.key_cache()[:, lo:hi])
+    st.add("v", vc[:, lo:hi].cpu().numpy(), orc.value_cache()[:, lo:hi])
+
+
+def _run(cfg, gs: int, calls, cont: int = 6):
+    """calls: list of (start, n) prefill calls over one prompt; then `cont`
+    greedy decode steps on the device, teacher-checked against the oracle."""
+    torch = need_gpu()
+    total = sum(n for _, n in calls)
+    tokens = synth.prompt(cfg.seed + 500, total, abs(cfg.vocab))
+    blob = synth.make_blob(cfg, synth.Q8_0, gs=gs)
+    orc = oracle.Model(blob, synth.Q8_0, gs=gs)
+    cache_st, logit_st = Stats(), Stats()
+    with l2d.Context(blob, synth.Q8_0, group_size=gs) as ctx:
+        for start, n in calls:
+            log(f"  {cfg.name} gs{gs}: prefill {n} tokens at pos {start}")
+            ctx.prefill(tokens[start:start + n], start)
+            for i in range(n):
+                ref = orc.forward(int(tokens[start + i]), start + i)
+            logit_st.add(start + n - 1, ctx.logits(), ref, ctx.last_token())
+        _check_cache(ctx, orc, 0, total, cache_st)
+        # continue: the first step takes the prefill's pick on the device
+        fed = int(np.argmax(ref))
+        for j in range(cont):
+            p = total + j
+            if p >= cfg.seq_len:
+                break
+            if j == 0:
+                ctx.forward_greedy(p)
+            else:
+                ctx.forward(fed, p)
+            r = orc.forward(fed, p)
+            logit_st.add(p, ctx.logits(), r, ctx.last_token())
+            fed = int(np.argmax(r))
+    orc.close()
+    torch.cuda.synchronize()
+    log(f"  cache rows: {cache_st.summary()}")
+    log(f"  logits: {logit_st.summary()}")
+    cache_st.assert_ok()
+    logit_st.assert_ok()
+    return cache_st, logit_st
+
+
+@pytest.mark.parametrize("cfg,gs,calls", [
+    (TINY_Q8, 64, [(0, 41)]),            # G = 2: blocks of 4 tokens, ragged
+    (TINY_Q8, 128, [(0, 37)]),           # two 64-value MFMA parts per group
+    (TINY_Q8, 64, [(0, 1)]),             # a single token
+    (GQA8_Q8, 64, [(0, 50)]),            # G = 8: one token per block
+    (GQA8_Q8, 256, [(0, 33), (33, 20)]),  # four parts per group; second call at pos 33
+], ids=["tiny-g2-gs64", "tiny-gs128", "tiny-one-token", "gqa8-gs64", "gqa8-gs256-two-calls"])
+def test_prefill_small(cfg, gs, calls):
+    cache_st, _ = _run(cfg, gs, calls)
+    assert cache_st.exact / cache_st.n > 0.99
+
+
+def test_prefill_110m_two_chunks_and_two_calls():
+    """601 tokens: one call of 250, then 351 at pos 250 (a 512-token chunk
+    boundary falls inside neither; the first call is one chunk), and a
+    single call of 601 tokens (a full 512-token chunk, then a ragged 89)."""
+    cfg = synth.CONFIGS["110M"]
+    _run(cfg, 64, [(0, 250), (250, 351)], cont=4)
+    _run(cfg, 64, [(0, 601)], cont=4)
+
+
+def test_prefill_matches_own_decode_bitwise():
+    """The prefill and the device's own token-by-token steps leave the same
+    cache rows and logits (both follow the oracle's arithmetic)."""
+    torch = need_gpu()
+    cfg = synth.CONFIGS["110M"]
+    blob = synth.make_blob(cfg, synth.Q8_0)
+    tokens = synth.prompt(77, 96, cfg.vocab)
+    with l2d.Context(blob, synth.Q8_0) as a, l2d.Context(blob, synth.Q8_0) as b:
+        a.prefill(tokens, 0)
+        for i, t in enumerate(tokens):
+            b.forward(int(t), i)
+        la, lb = a.logits(), b.logits()
+        ka, va = a.kv_cache()
+        kb, vb = b.kv_cache()
+        dk = (ka[:, :96] - kb[:, :96]).abs().max().item()
+        dv = (va[:, :96] - vb[:, :96]).abs().max().item()
+        same = float((ka[:, :96] == kb[:, :96]).float().mean().item())
+        log(f"  prefill vs decode: max|dK| {dk:.3g} max|dV| {dv:.3g} K identical {same:.5f}, "
+            f"logits max|d| {np.abs(la - lb).max():.3g}")
+        assert dk <= 1e-5 and dv <= 1e-5
+        assert np.abs(la.astype(np.float64) - lb).max() <= 1e-4
+        assert a.last_token() == b.last_token() or np.sort(lb)[-1] - np.sort(lb)[-2] <= 1e-3
+    torch.cuda.synchronize()
+
+
+def test_prefill_errors():
+    need_gpu()
+    blob = synth.make_blob(TINY_Q8, synth.Q8_0)
+    with l2d.Context(blob, synth.Q8_0) as ctx:
+        with pytest.raises(l2d.L2DError):
+            ctx.prefill([], 0)
+        with pytest.raises(l2d.L2DError):
+            ctx.prefill([1, 2, 3], TINY_Q8.seq_len - 2)   # past the end of the cache
+        with pytest.raises(l2d.L2DError):
+            ctx.prefill([1, TINY_Q8.vocab], 0)           # token out of range
+        with pytest.raises(l2d.L2DError):
+            ctx.prefill([1, 2], -1)
+        ctx.prefill([1, 2], 0)                           # still usable afterwards
+    blob32 = synth.make_blob(synth.CONFIGS["tiny"], synth.F32)
+    with l2d.Context(blob32, synth.F32) as ctx:
+        with pytest.raises(l2d.L2DError):
+            ctx.prefill([1, 2], 0)                       # fp32 weights: not built
+    blob32 = synth.make_blob(TINY_Q8, synth.Q8_0, gs=32)
+    with l2d.Context(blob32, synth.Q8_0, group_size=32) as ctx:
+        with pytest.raises(l2d.L2DError):
+            ctx.prefill([1, 2], 0)                       # group size 32: not built
+
+
+def test_prefill_7b_q8_full_size():
+    """7B Q8_0: 64 prompt tokens, then 24 more at pos 64; every layer's cache
+    rows and the last logits of each call against the oracle."""
+    torch = need_gpu()
+    cfg = synth.CONFIGS["7B"]
+    try:
+        _run(cfg, 64, [(0, 64), (64, 24)], cont=2)
+    finally:
+        gc.collect()
+        torch.cuda.empty_cache()
