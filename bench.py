@@ -13,7 +13,9 @@ same values), timed with HIP events on the context's stream between two
 synchronisations.
 
 Prints one JSON line. value = tokens/s of the Q8_0 step at the headline
-position; per-position and fp32 figures ride along under "detail".
+position; per-position and fp32 figures, the step with sampling on, the
+batched prefill of a 512-token prompt (Q8_0, int8 MFMA) and the Q4_0 matvec
+on the step's matrix shapes ride along under "detail".
 """
 from __future__ import annotations
 
@@ -129,6 +131,43 @@ def gemv_q40_rates(cfg, torch, l2d, reps: int = 20) -> dict:
     return out
 
 
+PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
+
+
+def prefill_rates(cfg, ctx, torch, synth, n: int = 512, reps: int = 3) -> dict:
+    """Batched prefill of an n-token prompt at pos 0 (Q8_0): tokens/s over
+    reps timed calls (HIP events on the context's stream), and the mean
+    kernel time of each class from one kernel-stamped pass. The matmuls'
+    rate is their int8 multiply-adds (2 * rows * cols * n ops) per second."""
+    toks = synth.prompt(4242, n, abs(cfg.vocab))
+    stream = torch.cuda.ExternalStream(ctx.stream_handle())
+    ctx.prefill(toks, 0)
+    ctx.sync()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ctx.prefill(toks, 0)
+    e1.record(stream)
+    ctx.sync()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    prof = ctx.prefill_profile(toks, 0)
+    d, h, kvd = cfg.dim, cfg.hidden_dim, cfg.kv_dim
+    shapes = {"qkv": (d + 2 * kvd, d), "wo": (d, d), "w13": (2 * h, d), "w2": (d, h)}
+    kern = {}
+    for k, v in prof.items():
+        kern[k] = {"avg_us": v * 1e6}
+        if k in shapes and v > 0:
+            N, K = shapes[k]
+            kern[k]["int8_tops"] = 2.0 * N * K * n / v / 1e12
+    out = {"tokens": n, "ms": sec * 1e3, "tok_s": n / sec, "kernels": kern}
+    log(f"[bench] prefill of {n} tokens: {sec * 1e3:.2f} ms, {n / sec:.0f} tok/s; " +
+        ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['int8_tops']:.0f}TOP/s" if 'int8_tops' in v else "")
+                  for k, v in kern.items()))
+    return out
+
+
 def decode_to(ctx, positions, torch, fill=True):
     """Greedy decode from pos 0 through max(positions); returns the token fed
     at each requested position. Without fill the cache stays zero and the
@@ -211,6 +250,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-fill", action="store_true",
                     help="skip the greedy decode that fills the cache (profiling runs)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the batched prefill measurement (Q8_0)")
+    ap.add_argument("--prefill-tokens", type=int, default=512)
     ap.add_argument("--no-q4-gemv", action="store_true",
                     help="skip the Q4_0 matvec measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -263,6 +305,8 @@ def main():
         log(f"[bench] {name} kernels at pos {args.headline_pos}: " +
             ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['gbs']:.0f}GB/s" if 'gbs' in v else "")
                       for k, v in kern.items()))
+        if dt == 1 and not args.no_prefill:
+            detail["prefill_q8_0"] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
         if head is None:
             head = (dt, res[args.headline_pos], kt, b)
         ctx.close()

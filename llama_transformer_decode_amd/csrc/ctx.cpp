@@ -920,7 +920,7 @@ int prefill_buffers(l2d_ctx* ctx)
 {
     if (ctx->pf_cap > 0) return L2D_OK;
     int64_t cap = ctx->S < kPrefillChunk ? ctx->S : kPrefillChunk;
-    cap = (cap + 7) / 8 * 8;  // whole token blocks of the attention kernel
+    cap = (cap + 15) / 16 * 16;  // whole 16-token tiles of the matmul inputs and attention blocks
     const int64_t kmax = ctx->d > ctx->h ? ctx->d : ctx->h;
     ALLOC(ctx->pf_tok, (size_t)cap * 4);
     ALLOC(ctx->pf_x, (size_t)(cap * ctx->d) * 4);

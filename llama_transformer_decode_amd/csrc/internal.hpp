@@ -113,7 +113,7 @@ struct PrefillPrepParams {
     double eps;
     int64_t K;
     int32_t gs, m;
-    int8_t* q;          // [m][K] codes, plain order
+    int8_t* q;          // codes in the matmul's operand order: [m/16][K/gs][gs/64][64 lanes][16]
     float* s;           // [m][K/gs] scales
 };
 hipError_t launch_prefill_prep(const PrefillPrepParams& p, bool norm, hipStream_t s,
@@ -124,7 +124,7 @@ struct PrefillGemmParams {
     const float* Ws;    // [N][K/gs]
     int64_t N, K;
     int32_t gs, m;
-    const int8_t* aq;   // [m][K] input codes, plain order
+    const int8_t* aq;   // input codes in operand order (prefill_prep_kernel), tiles of 16 tokens
     const float* as;    // [m][K/gs]
     float* out;         // EPI_STORE / EPI_QKV (q rows) / EPI_SWIGLU: [m][ldo]; EPI_RESID: += into [m][ldo]
     int64_t ldo;

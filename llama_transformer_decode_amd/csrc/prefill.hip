@@ -84,9 +84,12 @@ hipError_t launch_prefill_rope(const float* freqs, int hs, int pos0, int m, floa
 
 // One workgroup per token row of K values: optional RMSNorm (fp64 sum of
 // squares, v = fp32(g * (x * r)) as in the decode prologue), then Q8_0 codes
-// (plain order, [m][K]) and scales ([m][K/gs]) with the decode quantiser:
-// one wavefront per group of 64 (gs 64) or per 64-value part of a larger
-// group, the group maximum over its lanes.
+// and scales ([m][K/gs]) with the decode quantiser, 16 values per lane, the
+// group maximum over the group's lanes. Codes are stored in the operand
+// order of the matmul's MFMA: for each tile of 16 tokens, group g and
+// 64-value part u of the group, 1 KiB in which lane l = 16*q + (t % 16)
+// holds quarter q of token t's part (so one contiguous 1 KiB load feeds one
+// instruction).
 template <bool NORM>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepParams p)
 {
@@ -108,7 +111,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepParams p)
     const int lpg = gs / 16;             // lanes per group, 16 values each
     const int gpw = kWave / lpg;         // groups per wavefront pass
     const int64_t ng = p.K / gs;
-    int8_t* q = p.q + (int64_t)t * p.K;
+    const int U = gs / 64;               // 64-value parts per group
+    int8_t* q = p.q + (int64_t)(t / 16) * ng * gs * 16;
     float* sc = p.s + (int64_t)t * ng;
     for (int64_t g0 = (int64_t)wave * gpw; g0 < ng; g0 += 4 * gpw) {
         const int64_t g = g0 + lane / lpg;
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepParams p)
         float s;
         const i32x4 codes = quant16(v, lpg, &s);
         if (ok) {
-            *(i32x4*)(q + base) = codes;
+            const int cq = lane % lpg, u = cq / 4, qq = cq % 4;
+            *(i32x4*)(q + (((int64_t)g * U + u) * 64 + qq * 16 + t % 16) * 16) = codes;
             if (lane % lpg == 0) sc[g] = s;
         }
     }
@@ -142,31 +147,46 @@ hipError_t launch_prefill_prep(const PrefillPrepParams& p, bool norm, hipStream_
 
 // ------------------------------------------------------------ int8 MFMA GEMM
 
-// Workgroup tile: 64 weight rows x 64 tokens; wavefront (wr, wt) takes rows
-// 32*wr.. and tokens 32*wt.., i.e. 2 x 2 tiles of 16 x 16. Per group of
+// Workgroup tile: 64 weight rows x 128 tokens; wavefront (wr, wt) takes rows
+// 32*wr.. and tokens 64*wt.., i.e. 2 x 4 tiles of 16 x 16. Per group of
 // gs = 64*U values, tile (i, j) gets U v_mfma_i32_16x16x64_i8 into one int32
 // accumulator (exact: at most 256 * 127^2 < 2^31) and then, for each of the
 // lane's four outputs, acc += (dot * sw) * sx in fp64 (the oracle's order;
 // contraction into an fma is switched off). Operand lanes: lane l holds row
-// (token) l % 16 and the 16-byte quarter l / 16 of each 64-value part of the
+// (token) l % 16 and the 16-byte quarter l / 16 of a 64-value part of the
 // group; output lane l holds rows 4*(l/16) + r, r < 4, of column l % 16.
 //
-// Weights are read in the decode step's group-interleaved layout
-// (q8_perm_offset): quarter q of group j of a 64-group block sits at
-// 16*nb*q + 16*j. Scales of 16 groups of the tile's rows and tokens are
-// staged in LDS, double-buffered, loaded one 16-group stage ahead.
-constexpr int kGR = 64, kGT = 64, kGStage = 16;
+// Weights (the decode step's group-interleaved rows, q8_perm_offset: quarter
+// Q of group j of a 64-group block at 16*nb*Q + 16*j) are staged through LDS
+// in steps of 8 64-value parts: the workgroup reads, per row and quarter,
+// the step's groups as one contiguous run (a 128-byte line for gs 64) and
+// writes them in operand order; the next step's loads are in flight while
+// the current one is used (double buffer). Inputs are already in operand
+// order (prefill_prep_kernel): one contiguous 1 KiB load per tile, issued
+// into a ring of groups ahead of their use. Scales of the step's groups for
+// the tile's rows and tokens are staged with the weights.
+constexpr int kGR = 64, kGT = 128, kGParts = 8;
+constexpr int kTR = 2, kTT = 4;  // 16 x 16 tiles per wavefront: rows, tokens
 
-struct GemmTileLds {
-    float sw[2][kGStage][kGR];
-    float sx[2][kGStage][kGT];
+struct GemmLds {
+    v4i w[2][kGParts][4][kGR];    // [buffer][part][quarter][row], 16 bytes each
+    float sw[2][kGParts][kGR];    // weight scales [buffer][group of the step][row]
+    float sx[2][kGParts][kGT];    // input scales [buffer][group of the step][token]
+};
+
+template <int U>
+struct GemmOps {
+    v4i b[kTT][U];
 };
 
 template <int EPI, int U>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams p)
 {
 #pragma clang fp contract(off)
-    __shared__ GemmTileLds L;
+    constexpr int GPS = kGParts / U;  // groups per step
+    constexpr int kGRing = U == 1 ? 3 : U == 2 ? 2 : 1;
+    extern __shared__ __align__(16) unsigned char gsmem[];
+    GemmLds& L = *(GemmLds*)gsmem;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wt = wave >> 1;
     // XCD-aware order: the token blocks of one row block run on one XCD
@@ -177,125 +197,155 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
     const int rb = xcd + 8 * (slot / ntb), tb = slot % ntb;
     if (rb >= nrb) return;
     const int64_t row0 = (int64_t)rb * kGR, tok0 = (int64_t)tb * kGT;
-    const int64_t K = p.K, gs = p.gs, ng = K / gs;
-
-    // operand addresses: lane's row (token) of each tile and its quarter
+    // group indices and offsets within one row fit in 32 bits (K <= 65536)
+    const int K = (int)p.K, gs = p.gs, ng = K / gs;
+    const int nst = (ng + GPS - 1) / GPS;
     const int rl = lane % 16, ql = lane / 16;
-    const int8_t* wrow[2];
-    const int8_t* xrow[2];
+
+    // ---- weight staging: piece k of this thread = (row, quarter Q, group jg)
+    // with jg fastest, so 8 (gs 64) adjacent lanes read one 128-byte run
+    constexpr int kPieces = kGR * 4 * kGParts / 256;  // 16-byte pieces per thread (8)
+    v4i wreg[kPieces];
+    float swreg[(kGR * GPS + 255) / 256], sxreg[(kGT * GPS + 255) / 256];
+    auto stage_load = [&](int st) {
+        const int g0 = st * GPS;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int64_t row = row0 + 32 * wr + 16 * i + rl;
-        wrow[i] = (const int8_t*)p.W + (row < p.N ? row : p.N - 1) * K;
-        const int64_t tok = tok0 + 32 * wt + 16 * i + rl;
-        xrow[i] = p.aq + (tok < p.m ? tok : p.m - 1) * K;
-    }
-    auto load_ops = [&](int64_t g, v4i (&a)[2][U], v4i (&b)[2][U]) {
-        const int64_t blk = g / 64, j = g % 64;
-        const int64_t nb = (ng - blk * 64) < 64 ? (ng - blk * 64) : 64;
-        const int64_t wbase = blk * 64 * gs + 16 * j;
+        for (int k = 0; k < kPieces; k++) {
+            const int id2 = tid + 256 * k;
+            const int jg = id2 % GPS, Q = (id2 / GPS) % (4 * U), r = id2 / (GPS * 4 * U);
+            int g = g0 + jg;
+            g = g < ng ? g : ng - 1;
+            const int blk = g / 64, jj = g % 64;
+            const int nb = (ng - blk * 64) < 64 ? (ng - blk * 64) : 64;
+            const int64_t row = row0 + r < p.N ? row0 + r : p.N - 1;
+            wreg[k] = *(const v4i*)((const int8_t*)p.W + row * K + blk * 64 * gs + 16 * nb * Q + 16 * jj);
+        }
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t q = 4 * u + ql;
+        for (int k = 0; k < (kGR * GPS + 255) / 256; k++) {
+            const int id2 = tid + 256 * k;
+            if (id2 < kGR * GPS) {
+                const int jg = id2 % GPS, r = id2 / GPS;
+                const int g = g0 + jg < ng ? g0 + jg : ng - 1;
+                const int64_t row = row0 + r < p.N ? row0 + r : p.N - 1;
+                swreg[k] = p.Ws[row * ng + g];
+            }
+        }
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                a[i][u] = *(const v4i*)(wrow[i] + wbase + 16 * nb * q);
-                b[i][u] = *(const v4i*)(xrow[i] + g * gs + 16 * q);
+        for (int k = 0; k < (kGT * GPS + 255) / 256; k++) {
+            const int id2 = tid + 256 * k;
+            if (id2 < kGT * GPS) {
+                const int jg = id2 % GPS, t = id2 / GPS;
+                const int g = g0 + jg < ng ? g0 + jg : ng - 1;
+                const int64_t tok = tok0 + t < p.m ? tok0 + t : p.m - 1;
+                sxreg[k] = p.as[tok * ng + g];
             }
         }
     };
-    // scales of stage st (16 groups) into LDS buffer bf: thread -> (row or
-    // token, 4 consecutive groups)
-    auto stage_load = [&](int64_t st, float (&w4)[4], float (&x4)[4]) {
-        const int who = tid / 4, part = tid % 4;  // 64 rows/tokens x 4 parts of 4 groups
-        const int64_t g = st * kGStage + part * 4;
-        const int64_t row = row0 + who < p.N ? row0 + who : p.N - 1;
-        const int64_t tok = tok0 + who < p.m ? tok0 + who : p.m - 1;
+    auto stage_store = [&](int bf) {
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int64_t gg = g + k < ng ? g + k : ng - 1;
-            w4[k] = p.Ws[row * ng + gg];
-            x4[k] = p.as[tok * ng + gg];
+        for (int k = 0; k < kPieces; k++) {
+            const int id2 = tid + 256 * k;
+            const int jg = id2 % GPS, Q = (id2 / GPS) % (4 * U), r = id2 / (GPS * 4 * U);
+            L.w[bf][jg * U + Q / 4][Q % 4][r] = wreg[k];
         }
-    };
-    auto stage_store = [&](int bf, const float (&w4)[4], const float (&x4)[4]) {
-        const int who = tid / 4, part = tid % 4;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            L.sw[bf][part * 4 + k][who] = w4[k];
-            L.sx[bf][part * 4 + k][who] = x4[k];
+        for (int k = 0; k < (kGR * GPS + 255) / 256; k++) {
+            const int id2 = tid + 256 * k;
+            if (id2 < kGR * GPS) L.sw[bf][id2 % GPS][id2 / GPS] = swreg[k];
+        }
+#pragma unroll
+        for (int k = 0; k < (kGT * GPS + 255) / 256; k++) {
+            const int id2 = tid + 256 * k;
+            if (id2 < kGT * GPS) L.sx[bf][id2 % GPS][id2 / GPS] = sxreg[k];
         }
     };
 
-    double acc[2][2][4];
+    // ---- inputs: tile j of this wavefront = token tile (tok0 + 64wt)/16 + j
+    const int8_t* xtile[kTT];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int j = 0; j < kTT; j++) {
+        int64_t tt = (tok0 + 64 * wt) / 16 + j;
+        const int64_t last = (p.m - 1) / 16;
+        tt = tt < last ? tt : last;
+        xtile[j] = p.aq + tt * (int64_t)ng * gs * 16 + lane * 16;
+    }
+    auto load_ops = [&](int g, GemmOps<U>& o) {
+        const int gc = g < ng ? g : ng - 1;
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int j = 0; j < kTT; j++) o.b[j][u] = *(const v4i*)(xtile[j] + ((int64_t)gc * U + u) * 1024);
+    };
+
+    double acc[kTR][kTT][4];
+#pragma unroll
+    for (int i = 0; i < kTR; i++)
+#pragma unroll
+        for (int j = 0; j < kTT; j++)
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[i][j][r] = 0.0;
 
-    const int64_t nst = (ng + kGStage - 1) / kGStage;
-    float w4[4], x4[4];
-    stage_load(0, w4, x4);
-    stage_store(0, w4, x4);
-    v4i a[2][U], b[2][U], an[2][U], bn[2][U];
-    load_ops(0, a, b);
+    GemmOps<U> ops[kGRing];
+#pragma unroll
+    for (int k = 0; k < kGRing; k++) load_ops(k, ops[k]);
+    stage_load(0);
+    stage_store(0);
+    if (nst > 1) stage_load(1);
     __syncthreads();
-    for (int64_t st = 0; st < nst; st++) {
-        const int bf = (int)(st & 1);
-        if (st + 1 < nst) stage_load(st + 1, w4, x4);
-        const int64_t gend = (st + 1) * kGStage < ng ? (st + 1) * kGStage : ng;
-        for (int64_t g = st * kGStage; g < gend; g++) {
-            // next group's operands in flight while this one is used
-            load_ops(g + 1 < ng ? g + 1 : g, an, bn);
-            const int gi = (int)(g - st * kGStage);
-            v4i d[2][2];
+
+    auto use_group = [&](const GemmOps<U>& o, int g) {
+        const int bf = (g / GPS) & 1, gl = g % GPS;
+        double sx[kTT];
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+        for (int j = 0; j < kTT; j++) sx[j] = (double)L.sx[bf][gl][64 * wt + 16 * j + rl];
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    v4i c = {0, 0, 0, 0};
+        for (int i = 0; i < kTR; i++) {
+            const f32x4 sw4 = *(const f32x4*)&L.sw[bf][gl][32 * wr + 16 * i + 4 * ql];
+            const double sw[4] = {(double)sw4.x, (double)sw4.y, (double)sw4.z, (double)sw4.w};
+            v4i a[U];
 #pragma unroll
-                    for (int u = 0; u < U; u++) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i][u], b[j][u], c, 0, 0, 0);
-                    d[i][j] = c;
-                }
+            for (int u = 0; u < U; u++) a[u] = L.w[bf][gl * U + u][ql][32 * wr + 16 * i + rl];
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const double sx = (double)L.sx[bf][gi][32 * wt + 16 * j + rl];
+            for (int j = 0; j < kTT; j++) {
+                v4i c = {0, 0, 0, 0};
 #pragma unroll
-                for (int i = 0; i < 2; i++) {
-                    const f32x4 sw4 = *(const f32x4*)&L.sw[bf][gi][32 * wr + 16 * i + 4 * ql];
-                    const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+                for (int u = 0; u < U; u++) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], o.b[j][u], c, 0, 0, 0);
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const double t = ((double)d[i][j][r] * (double)swv[r]) * sx;
-                        acc[i][j][r] = acc[i][j][r] + t;
-                    }
+                for (int r = 0; r < 4; r++) {
+                    const double t = ((double)c[r] * sw[r]) * sx[j];
+                    acc[i][j][r] = acc[i][j][r] + t;
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int u = 0; u < U; u++) {
-                    a[i][u] = an[i][u];
-                    b[i][u] = bn[i][u];
-                }
         }
-        if (st + 1 < nst) {
-            stage_store(bf ^ 1, w4, x4);
-            __syncthreads();
+    };
+
+    for (int g0 = 0; g0 < ng; g0 += kGRing) {
+#pragma unroll
+        for (int k = 0; k < kGRing; k++) {
+            const int g = g0 + k;
+            if (g < ng) {
+                if (g > 0 && g % GPS == 0) {
+                    // step g / GPS: its weights and scales (loaded a step
+                    // ago) into the buffer last read two steps ago
+                    const int st = g / GPS;
+                    stage_store(st & 1);
+                    __syncthreads();
+                    if (st + 1 < nst) stage_load(st + 1);
+                }
+                use_group(ops[k], g);
+            }
+            load_ops(g + kGRing, ops[k]);
         }
     }
 
     // epilogue: lane holds rows row0 + 32wr + 16i + 4ql + r of token
-    // tok0 + 32wt + 16j + rl
+    // tok0 + 64wt + 16j + rl
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int64_t t = tok0 + 32 * wt + 16 * j + rl;
+    for (int j = 0; j < kTT; j++) {
+        const int64_t t = tok0 + 64 * wt + 16 * j + rl;
         if (t >= p.m) continue;
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < kTR; i++) {
             const int64_t rbase = row0 + 32 * wr + 16 * i + 4 * ql;
             float y[4];
 #pragma unroll
@@ -355,16 +405,31 @@ size_t prefill_gemm_grid(int64_t N, int m)
     return (size_t)(8 * ((nrb + 7) / 8) * ntb);
 }
 
+// the staging buffers exceed the default 64 KiB of dynamic LDS
+template <int EPI, int U>
+static hipError_t gemm_lds_attr()
+{
+    static bool done = false;
+    if (!done) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<EPI, U>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmLds));
+        if (e != hipSuccess) return e;
+        done = true;
+    }
+    return hipSuccess;
+}
+
 template <int EPI>
 static hipError_t launch_gemm_epi(const PrefillGemmParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     const dim3 grid((unsigned)prefill_gemm_grid(p.N, p.m));
 #define L2D_PG(UU)                                                                                   \
+    if (hipError_t e_ = gemm_lds_attr<EPI, UU>(); e_ != hipSuccess) return e_;                      \
     if (ev)                                                                                          \
-        hipExtLaunchKernelGGL((prefill_gemm_kernel<EPI, UU>), grid, dim3(256), 0u, s, ev->start,     \
-                              ev->stop, 0u, p);                                                      \
+        hipExtLaunchKernelGGL((prefill_gemm_kernel<EPI, UU>), grid, dim3(256), (uint32_t)sizeof(GemmLds), \
+                              s, ev->start, ev->stop, 0u, p);                                        \
     else                                                                                             \
-        hipLaunchKernelGGL((prefill_gemm_kernel<EPI, UU>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((prefill_gemm_kernel<EPI, UU>), grid, dim3(256), sizeof(GemmLds), s, p);
     switch (p.gs) {
     case 64: L2D_PG(1) break;
     case 128: L2D_PG(2) break;
@@ -401,7 +466,8 @@ __global__ __launch_bounds__(kPAThreads) void prefill_attn_kernel(PrefillAttnPar
     extern __shared__ __align__(16) unsigned char smem[];
     const int g = blockIdx.x;
     const int TB = KG / p.G;
-    const int t0 = blockIdx.y * TB;
+    // the longest ranges (last tokens) first, so the grid ends on short ones
+    const int t0 = (gridDim.y - 1 - blockIdx.y) * TB;
     const int tlast = min(t0 + TB, p.m) - 1;
     AttnRange r;
     r.q = p.q + (size_t)t0 * p.d + (size_t)g * p.G * p.hs;

@@ -80,7 +80,7 @@ struct l2d_ctx {
     double* mpart_ml = nullptr;
 
     // batched prefill (allocated by the first l2d_prefill): chunk capacity
-    // in tokens (a multiple of 8), token ids, residual rows, q rows,
+    // in tokens (a multiple of 16), token ids, residual rows, q rows,
     // attention outputs, FFN hidden rows, quantised matmul inputs, RoPE tables
     int pf_cap = 0;
     int32_t* pf_tok = nullptr;
