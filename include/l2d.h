@@ -135,17 +135,20 @@ const float* l2d_forward_greedy(l2d_ctx* ctx, int32_t pos);
  * pos0 + i), i = 0..n-1 (prompt tokens are fed through the forward pass one
  * position after another: gitcode guide, main loop; mht18 essay, section 2.3,
  * the toy forward pass over a sequence), computed as int8 matrix products
- * over chunks of up to 512 tokens (MFMA): every token's matmul inputs are
- * quantised on their own, every output is the same fp64 sum of exact int32
- * group dots, attention of token i covers slots 0..pos0 + i. Writes K/V slots
+ * over chunks of up to 512 tokens (MFMA): for Q8_0 every token's matmul
+ * inputs are quantised on their own and every output is the same fp64 sum of
+ * exact int32 group dots; for fp32 every output is an fp64 sum of the exact
+ * products (fp64 MFMA; the summation order differs, as in the decode step's
+ * GEMV); attention of token i covers slots 0..pos0 + i. Writes K/V slots
  * pos0 .. pos0 + n - 1 of every layer and returns, like l2d_forward, the
  * device logits of the last token; l2d_last_token gives its argmax (or
  * sampled token), and l2d_forward_greedy(ctx, pos0 + n) may follow.
  * tokens is a host array of n ids, read before the call returns.
  * Asynchronous on the context's stream; the first call allocates the chunk
- * buffers (about 512 x (3 dim + 2 hidden_dim) x 4 bytes).
- * Needs Q8_0 weights with group size 64, 128 or 256 and n_heads / n_kv_heads
- * dividing 8. Returns NULL on error: n <= 0, pos0 < 0, pos0 + n > seq_len,
+ * buffers (about 512 x (3 dim + 2 hidden_dim) x 4 bytes, plus 512 x
+ * max(dim, hidden_dim) x 4 for fp32 weights).
+ * Needs fp32 weights, or Q8_0 with group size 64, 128 or 256, and
+ * n_heads / n_kv_heads dividing 8. Returns NULL on error: n <= 0, pos0 < 0, pos0 + n > seq_len,
  * a token outside [0, vocab), an unsupported model (L2D_EINVAL, see
  * l2d_last_error), L2D_ENOMEM, L2D_EHIP.
  */

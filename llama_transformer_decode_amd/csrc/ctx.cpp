@@ -912,8 +912,8 @@ enum { PC_PREP = 0, PC_QKV, PC_ATTN, PC_WO, PC_W13, PC_W2, PC_START, PC_CLS, PC_
 
 bool prefill_supported(const l2d_ctx* ctx)
 {
-    return ctx->dt == DT_Q8 && (ctx->gs == 64 || ctx->gs == 128 || ctx->gs == 256) &&
-           prefill_attn_supported((int)ctx->G, (int)ctx->hs);
+    const bool dt_ok = ctx->dt == DT_F32 || (ctx->dt == DT_Q8 && (ctx->gs == 64 || ctx->gs == 128 || ctx->gs == 256));
+    return dt_ok && ctx->d % 4 == 0 && ctx->h % 4 == 0 && prefill_attn_supported((int)ctx->G, (int)ctx->hs);
 }
 
 int prefill_buffers(l2d_ctx* ctx)
@@ -927,7 +927,8 @@ int prefill_buffers(l2d_ctx* ctx)
     ALLOC(ctx->pf_q, (size_t)(cap * ctx->d) * 4);
     ALLOC(ctx->pf_o, (size_t)(cap * ctx->d) * 4);
     ALLOC(ctx->pf_h, (size_t)(cap * ctx->h) * 4);
-    ALLOC(ctx->pf_aq, (size_t)(cap * kmax));
+    // matmul inputs: int8 codes (Q8_0) or normalised fp32 rows (fp32 weights)
+    ALLOC(ctx->pf_aq, (size_t)(cap * kmax) * (ctx->dt == DT_F32 ? 4 : 1));
     ALLOC(ctx->pf_as, (size_t)(cap * (kmax / ctx->gs)) * 4);
     ALLOC(ctx->pf_cos, (size_t)(cap * (ctx->hs / 2)) * 4);
     ALLOC(ctx->pf_sin, (size_t)(cap * (ctx->hs / 2)) * 4);
@@ -945,6 +946,9 @@ int enqueue_prefill_chunk(l2d_ctx* ctx, int m, int pos, KernelTimer* kt)
 {
     const int64_t d = ctx->d, h = ctx->h, kvd = ctx->kvd, gs = ctx->gs;
     const int64_t nqkv = d + 2 * kvd;
+    const bool f32 = ctx->dt == DT_F32;
+    const size_t es = elt(ctx->dt);
+    float* xn = (float*)ctx->pf_aq;  // fp32 weights: normalised input rows
     hipStream_t s = ctx->stream;
     auto ev = [&](int c) -> const LaunchEvents* {
         if (!kt) return nullptr;
@@ -973,19 +977,25 @@ int enqueue_prefill_chunk(l2d_ctx* ctx, int m, int pos, KernelTimer* kt)
         q.m = m;
         q.q = ctx->pf_aq;
         q.s = ctx->pf_as;
+        q.xo = f32 ? xn : nullptr;
         return launch_prefill_prep(q, gain != nullptr, s, ev(PC_PREP));
+    };
+    auto scales = [&](float* base, int64_t off_elems) -> const float* {
+        return f32 ? nullptr : base + off_elems / gs;
     };
     for (int64_t l = 0; l < ctx->L; l++) {
         PrefillGemmParams g;
         memset(&g, 0, sizeof(g));
+        g.dtype = ctx->dt;
         g.gs = (int32_t)gs;
         g.m = m;
         g.aq = ctx->pf_aq;
         g.as = ctx->pf_as;
 
         HIP_TRY(ctx, prep(ctx->pf_x, ctx->rms_att + l * d, d));
-        g.W = (const int8_t*)ctx->wqkv + (size_t)(l * nqkv * d);
-        g.Ws = ctx->wqkv_s + (size_t)(l * nqkv * d / gs);
+        g.a32 = xn;
+        g.W = (const uint8_t*)ctx->wqkv + (size_t)(l * nqkv * d) * es;
+        g.Ws = scales(ctx->wqkv_s, l * nqkv * d);
         g.N = nqkv;
         g.K = d;
         g.out = ctx->pf_q;
@@ -1014,9 +1024,10 @@ int enqueue_prefill_chunk(l2d_ctx* ctx, int m, int pos, KernelTimer* kt)
         a.pos0 = pos;
         HIP_TRY(ctx, launch_prefill_attn(a, s, ev(PC_ATTN)));
 
-        HIP_TRY(ctx, prep(ctx->pf_o, nullptr, d));
-        g.W = (const int8_t*)ctx->wo + (size_t)(l * d * d);
-        g.Ws = ctx->wo_s + (size_t)(l * d * d / gs);
+        if (!f32) HIP_TRY(ctx, prep(ctx->pf_o, nullptr, d));
+        g.a32 = ctx->pf_o;
+        g.W = (const uint8_t*)ctx->wo + (size_t)(l * d * d) * es;
+        g.Ws = scales(ctx->wo_s, l * d * d);
         g.N = d;
         g.K = d;
         g.out = ctx->pf_x;
@@ -1024,17 +1035,19 @@ int enqueue_prefill_chunk(l2d_ctx* ctx, int m, int pos, KernelTimer* kt)
         HIP_TRY(ctx, launch_prefill_gemm(EPI_RESID, g, s, ev(PC_WO)));
 
         HIP_TRY(ctx, prep(ctx->pf_x, ctx->rms_ffn + l * d, d));
-        g.W = (const int8_t*)ctx->w13 + (size_t)(l * 2 * h * d);
-        g.Ws = ctx->w13_s + (size_t)(l * 2 * h * d / gs);
+        g.a32 = xn;
+        g.W = (const uint8_t*)ctx->w13 + (size_t)(l * 2 * h * d) * es;
+        g.Ws = scales(ctx->w13_s, l * 2 * h * d);
         g.N = 2 * h;
         g.K = d;
         g.out = ctx->pf_h;
         g.ldo = h;
         HIP_TRY(ctx, launch_prefill_gemm(EPI_SWIGLU, g, s, ev(PC_W13)));
 
-        HIP_TRY(ctx, prep(ctx->pf_h, nullptr, h));
-        g.W = (const int8_t*)ctx->w2 + (size_t)(l * d * h);
-        g.Ws = ctx->w2_s + (size_t)(l * d * h / gs);
+        if (!f32) HIP_TRY(ctx, prep(ctx->pf_h, nullptr, h));
+        g.a32 = ctx->pf_h;
+        g.W = (const uint8_t*)ctx->w2 + (size_t)(l * d * h) * es;
+        g.Ws = scales(ctx->w2_s, l * d * h);
         g.N = d;
         g.K = h;
         g.out = ctx->pf_x;
@@ -1052,8 +1065,8 @@ int prefill_impl(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0, K
     for (int32_t i = 0; i < n; i++)
         if (tokens[i] < 0 || tokens[i] >= ctx->V) return fail(ctx, L2D_EINVAL, "prefill: token outside [0, vocab)");
     if (!prefill_supported(ctx))
-        return fail(ctx, L2D_EINVAL, "prefill: needs Q8_0 weights with group size 64, 128 or 256 and "
-                                     "n_heads / n_kv_heads dividing 8");
+        return fail(ctx, L2D_EINVAL, "prefill: needs fp32 weights or Q8_0 with group size 64, 128 or 256, "
+                                     "and n_heads / n_kv_heads dividing 8");
     int rc = prefill_buffers(ctx);
     if (rc != L2D_OK) return rc;
     int m = 0;

@@ -115,17 +115,20 @@ struct PrefillPrepParams {
     int32_t gs, m;
     int8_t* q;          // codes in the matmul's operand order: [m/16][K/gs][gs/64][64 lanes][16]
     float* s;           // [m][K/gs] scales
+    float* xo;          // fp32 weights: the normalised rows [m][K] instead of codes (q, s unused)
 };
 hipError_t launch_prefill_prep(const PrefillPrepParams& p, bool norm, hipStream_t s,
                                const LaunchEvents* ev = nullptr);
 
 struct PrefillGemmParams {
-    const void* W;      // Q8_0 codes [N][K], device (group-interleaved) layout
+    int32_t dtype;      // DT_Q8 (int8 MFMA) or DT_F32 (fp64 MFMA)
+    const void* W;      // Q8_0 codes [N][K], device (group-interleaved) layout, or fp32 [N][K]
     const float* Ws;    // [N][K/gs]
     int64_t N, K;
     int32_t gs, m;
     const int8_t* aq;   // input codes in operand order (prefill_prep_kernel), tiles of 16 tokens
     const float* as;    // [m][K/gs]
+    const float* a32;   // fp32 weights: input rows [m][K]
     float* out;         // EPI_STORE / EPI_QKV (q rows) / EPI_SWIGLU: [m][ldo]; EPI_RESID: += into [m][ldo]
     int64_t ldo;
     // EPI_QKV

@@ -90,7 +90,7 @@ hipError_t launch_prefill_rope(const float* freqs, int hs, int pos0, int m, floa
 // 64-value part u of the group, 1 KiB in which lane l = 16*q + (t % 16)
 // holds quarter q of token t's part (so one contiguous 1 KiB load feeds one
 // instruction).
-template <bool NORM>
+template <bool NORM, bool Q8>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepParams p)
 {
     __shared__ double red[4];
@@ -106,6 +106,13 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepParams p)
         __syncthreads();
         ss = red[0] + red[1] + red[2] + red[3];
         r = 1.0 / sqrt(ss / (double)p.K + p.eps);
+    }
+    if (!Q8) {
+        // fp32 weights: the normalised row itself feeds the matmul
+        float* xo = p.xo + (int64_t)t * p.K;
+        for (int64_t i = tid; i < p.K; i += 256)
+            xo[i] = NORM ? (float)((double)p.gain[i] * ((double)x[i] * r)) : x[i];
+        return;
     }
     const int gs = p.gs;
     const int lpg = gs / 16;             // lanes per group, 16 values each
@@ -136,8 +143,9 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrefillPrepParams p)
 
 hipError_t launch_prefill_prep(const PrefillPrepParams& p, bool norm, hipStream_t s, const LaunchEvents* ev)
 {
-    if (p.gs < 16 || p.gs > 1024 || p.K % p.gs) return hipErrorInvalidValue;
-    const auto k = norm ? prefill_prep_kernel<true> : prefill_prep_kernel<false>;
+    if (p.xo == nullptr && (p.gs < 64 || p.gs > 256 || p.K % p.gs)) return hipErrorInvalidValue;
+    const auto k = p.xo != nullptr ? (norm ? prefill_prep_kernel<true, false> : prefill_prep_kernel<false, false>)
+                                   : (norm ? prefill_prep_kernel<true, true> : prefill_prep_kernel<false, true>);
     if (ev)
         hipExtLaunchKernelGGL(k, dim3((unsigned)p.m), dim3(256), 0u, s, ev->start, ev->stop, 0u, p);
     else
@@ -146,6 +154,60 @@ hipError_t launch_prefill_prep(const PrefillPrepParams& p, bool norm, hipStream_
 }
 
 // ------------------------------------------------------------ int8 MFMA GEMM
+
+// Epilogue of four consecutive output rows rbase..rbase+3 (rbase a multiple
+// of 4, so row pairs stay whole) of token t: the decode step's epilogue
+// arithmetic, on row-major [m][ldo] outputs.
+template <int EPI>
+__device__ __forceinline__ void prefill_epilogue(const PrefillGemmParams& p, int64_t t, int64_t rbase,
+                                                 const float (&y)[4])
+{
+    if (EPI == EPI_STORE) {
+        for (int r = 0; r < 4; r++)
+            if (rbase + r < p.N) p.out[t * p.ldo + rbase + r] = y[r];
+    } else if (EPI == EPI_RESID) {
+        for (int r = 0; r < 4; r++)
+            if (rbase + r < p.N) {
+                float* o = p.out + t * p.ldo + rbase + r;
+                *o = (float)((double)*o + (double)y[r]);
+            }
+    } else if (EPI == EPI_SWIGLU) {
+        for (int r = 0; r < 4; r += 2)
+            if (rbase + r + 1 < p.N) {
+                const double z = (double)y[r];
+                const double h3 = (double)y[r + 1];
+                const double silu = z / (1.0 + exp(-z));
+                p.out[t * p.ldo + (rbase + r) / 2] = (float)(silu * h3);
+            }
+    } else if (EPI == EPI_QKV) {
+        const int64_t pos = p.pos0 + t;
+        for (int r = 0; r < 4; r += 2) {
+            const int64_t row = rbase + r;
+            if (row + 1 >= p.N) continue;
+            const float av = y[r], bv = y[r + 1];
+            if (row < p.d + p.kvd) {
+                const int64_t within = row < p.d ? row : row - p.d;
+                const int jj = (int)((within % p.hs) / 2);
+                const double c = (double)p.rcos[t * (p.hs / 2) + jj];
+                const double s = (double)p.rsin[t * (p.hs / 2) + jj];
+                const float ra = (float)((double)av * c - (double)bv * s);
+                const float rb2 = (float)((double)av * s + (double)bv * c);
+                if (row < p.d) {
+                    p.out[t * p.ldo + row] = ra;
+                    p.out[t * p.ldo + row + 1] = rb2;
+                } else {
+                    float* ks = p.kcache + pos * p.kvd + within;
+                    ks[0] = ra;
+                    ks[1] = rb2;
+                }
+            } else {
+                float* vs = p.vcache + pos * p.kvd + (row - p.d - p.kvd);
+                vs[0] = av;
+                vs[1] = bv;
+            }
+        }
+    }
+}
 
 // Workgroup tile: 64 weight rows x 128 tokens; wavefront (wr, wt) takes rows
 // 32*wr.. and tokens 64*wt.., i.e. 2 x 4 tiles of 16 x 16. Per group of
@@ -346,55 +408,131 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
         if (t >= p.m) continue;
 #pragma unroll
         for (int i = 0; i < kTR; i++) {
-            const int64_t rbase = row0 + 32 * wr + 16 * i + 4 * ql;
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) y[r] = (float)acc[i][j][r];
-            if (EPI == EPI_STORE) {
-                for (int r = 0; r < 4; r++)
-                    if (rbase + r < p.N) p.out[t * p.ldo + rbase + r] = y[r];
-            } else if (EPI == EPI_RESID) {
-                for (int r = 0; r < 4; r++)
-                    if (rbase + r < p.N) {
-                        float* o = p.out + t * p.ldo + rbase + r;
-                        *o = (float)((double)*o + (double)y[r]);
-                    }
-            } else if (EPI == EPI_SWIGLU) {
-                for (int r = 0; r < 4; r += 2)
-                    if (rbase + r + 1 < p.N) {
-                        const double z = (double)y[r];
-                        const double h3 = (double)y[r + 1];
-                        const double silu = z / (1.0 + exp(-z));
-                        p.out[t * p.ldo + (rbase + r) / 2] = (float)(silu * h3);
-                    }
-            } else if (EPI == EPI_QKV) {
-                const int64_t pos = p.pos0 + t;
-                for (int r = 0; r < 4; r += 2) {
-                    const int64_t row = rbase + r;
-                    if (row + 1 >= p.N) continue;
-                    const float av = y[r], bv = y[r + 1];
-                    if (row < p.d + p.kvd) {
-                        const int64_t within = row < p.d ? row : row - p.d;
-                        const int jj = (int)((within % p.hs) / 2);
-                        const double c = (double)p.rcos[t * (p.hs / 2) + jj];
-                        const double s = (double)p.rsin[t * (p.hs / 2) + jj];
-                        const float ra = (float)((double)av * c - (double)bv * s);
-                        const float rb2 = (float)((double)av * s + (double)bv * c);
-                        if (row < p.d) {
-                            p.out[t * p.ldo + row] = ra;
-                            p.out[t * p.ldo + row + 1] = rb2;
-                        } else {
-                            float* ks = p.kcache + pos * p.kvd + within;
-                            ks[0] = ra;
-                            ks[1] = rb2;
-                        }
-                    } else {
-                        float* vs = p.vcache + pos * p.kvd + (row - p.d - p.kvd);
-                        vs[0] = av;
-                        vs[1] = bv;
-                    }
-                }
-            }
+            prefill_epilogue<EPI>(p, t, row0 + 32 * wr + 16 * i + 4 * ql, y);
+        }
+    }
+}
+
+// fp32 weights: the same tiles on v_mfma_f64_16x16x4f64. A product of two
+// fp32 values is exact in fp64, so each output is an fp64 sum of the exact
+// products w * x (the oracle's fp32 matvec up to summation order, as in the
+// decode step's fp32 GEMV). Output lane l, register r of this instruction
+// holds row l/16 + 4r of column l % 16 (checked on MI355X with an in-bounds
+// probe); feeding operand row i with weight row 4*(i%4) + i/4 leaves each
+// lane four consecutive weight rows, as the epilogues need. Weights and
+// inputs are staged through LDS in steps of 32 values of K, double-buffered.
+constexpr int kFK = 32;  // K values per step
+
+struct GemmF32Lds {
+    float w[2][kFK][kGR];  // [buffer][k][row]
+    float x[2][kFK][kGT];  // [buffer][k][token]
+};
+
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void prefill_gemm_f32_kernel(PrefillGemmParams p)
+{
+    __shared__ GemmF32Lds L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wt = wave >> 1;
+    const int nrb = (int)((p.N + kGR - 1) / kGR), ntb = (p.m + kGT - 1) / kGT;
+    const int id = blockIdx.x, xcd = id % 8, slot = id / 8;
+    const int rb = xcd + 8 * (slot / ntb), tb = slot % ntb;
+    if (rb >= nrb) return;
+    const int64_t row0 = (int64_t)rb * kGR, tok0 = (int64_t)tb * kGT;
+    const int K = (int)p.K;
+    const int nst = (K + kFK - 1) / kFK;
+    const int rl = lane % 16, ql = lane / 16;
+    const int perm = 4 * (rl % 4) + rl / 4;  // weight row of operand row rl
+
+    // staging: weights 64 rows x 32 values (2 float4 per thread), inputs
+    // 128 tokens x 32 values (4 float4 per thread); 8 lanes read one row's
+    // 128 contiguous bytes
+    f32x4 wreg[2], xreg[4];
+    auto stage_load = [&](int st) {
+        const int k0 = st * kFK;
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int id2 = tid + 256 * c, r = id2 / 8, kq = id2 % 8;
+            const int64_t row = row0 + r < p.N ? row0 + r : p.N - 1;
+            int k = k0 + 4 * kq;
+            k = k < K ? k : K - 4;
+            wreg[c] = *(const f32x4*)((const float*)p.W + row * K + k);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int id2 = tid + 256 * c, t = id2 / 8, kq = id2 % 8;
+            const int64_t tok = tok0 + t < p.m ? tok0 + t : p.m - 1;
+            int k = k0 + 4 * kq;
+            k = k < K ? k : K - 4;
+            xreg[c] = *(const f32x4*)(p.a32 + tok * K + k);
+        }
+    };
+    auto stage_store = [&](int bf, int st) {
+        const int k0 = st * kFK;
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int id2 = tid + 256 * c, r = id2 / 8, kq = id2 % 8;
+            const bool ok = k0 + 4 * kq < K;  // values past K contribute zero
+            L.w[bf][4 * kq + 0][r] = ok ? wreg[c].x : 0.f;
+            L.w[bf][4 * kq + 1][r] = ok ? wreg[c].y : 0.f;
+            L.w[bf][4 * kq + 2][r] = ok ? wreg[c].z : 0.f;
+            L.w[bf][4 * kq + 3][r] = ok ? wreg[c].w : 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int id2 = tid + 256 * c, t = id2 / 8, kq = id2 % 8;
+            const bool ok = k0 + 4 * kq < K;
+            L.x[bf][4 * kq + 0][t] = ok ? xreg[c].x : 0.f;
+            L.x[bf][4 * kq + 1][t] = ok ? xreg[c].y : 0.f;
+            L.x[bf][4 * kq + 2][t] = ok ? xreg[c].z : 0.f;
+            L.x[bf][4 * kq + 3][t] = ok ? xreg[c].w : 0.f;
+        }
+    };
+
+    v4d acc[kTR][kTT];
+#pragma unroll
+    for (int i = 0; i < kTR; i++)
+#pragma unroll
+        for (int j = 0; j < kTT; j++) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+
+    stage_load(0);
+    stage_store(0, 0);
+    if (nst > 1) stage_load(1);
+    __syncthreads();
+    for (int st = 0; st < nst; st++) {
+        const int bf = st & 1;
+#pragma unroll
+        for (int ks = 0; ks < kFK / 4; ks++) {
+            const int kk = 4 * ks + ql;
+            double a[kTR], b[kTT];
+#pragma unroll
+            for (int i = 0; i < kTR; i++) a[i] = (double)L.w[bf][kk][32 * wr + 16 * i + perm];
+#pragma unroll
+            for (int j = 0; j < kTT; j++) b[j] = (double)L.x[bf][kk][64 * wt + 16 * j + rl];
+#pragma unroll
+            for (int i = 0; i < kTR; i++)
+#pragma unroll
+                for (int j = 0; j < kTT; j++) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (st + 1 < nst) {
+            stage_store(bf ^ 1, st + 1);
+            __syncthreads();
+            if (st + 2 < nst) stage_load(st + 2);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kTT; j++) {
+        const int64_t t = tok0 + 64 * wt + 16 * j + rl;
+        if (t >= p.m) continue;
+#pragma unroll
+        for (int i = 0; i < kTR; i++) {
+            const float y[4] = {(float)acc[i][j][0], (float)acc[i][j][1], (float)acc[i][j][2], (float)acc[i][j][3]};
+            prefill_epilogue<EPI>(p, t, row0 + 32 * wr + 16 * i + 4 * ql, y);
         }
     }
 }
@@ -440,9 +578,31 @@ static hipError_t launch_gemm_epi(const PrefillGemmParams& p, hipStream_t s, con
     return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t launch_gemm_f32_epi(const PrefillGemmParams& p, hipStream_t s, const LaunchEvents* ev)
+{
+    const dim3 grid((unsigned)prefill_gemm_grid(p.N, p.m));
+    if (ev)
+        hipExtLaunchKernelGGL(prefill_gemm_f32_kernel<EPI>, grid, dim3(256), 0u, s, ev->start, ev->stop, 0u, p);
+    else
+        hipLaunchKernelGGL(prefill_gemm_f32_kernel<EPI>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_gemm(int epi, const PrefillGemmParams& p, hipStream_t s, const LaunchEvents* ev)
 {
-    if (p.N <= 0 || p.m <= 0 || p.K % p.gs) return hipErrorInvalidValue;
+    if (p.N <= 0 || p.m <= 0) return hipErrorInvalidValue;
+    if (p.dtype == DT_F32) {
+        if (p.K % 4) return hipErrorInvalidValue;
+        switch (epi) {
+        case EPI_STORE: return launch_gemm_f32_epi<EPI_STORE>(p, s, ev);
+        case EPI_RESID: return launch_gemm_f32_epi<EPI_RESID>(p, s, ev);
+        case EPI_SWIGLU: return launch_gemm_f32_epi<EPI_SWIGLU>(p, s, ev);
+        case EPI_QKV: return launch_gemm_f32_epi<EPI_QKV>(p, s, ev);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (p.K % p.gs) return hipErrorInvalidValue;
     switch (epi) {
     case EPI_STORE: return launch_gemm_epi<EPI_STORE>(p, s, ev);
     case EPI_RESID: return launch_gemm_epi<EPI_RESID>(p, s, ev);
@@ -497,25 +657,40 @@ __global__ __launch_bounds__(kPAThreads) void prefill_attn_kernel(PrefillAttnPar
     }
 }
 
-int prefill_attn_heads(int G) { return G <= kMaxG ? kMaxG : G; }
-
-bool prefill_attn_supported(int G, int hs)
+// Query rows per workgroup: the most (8, 4, 2, or G itself) that are a
+// multiple of G and whose LDS fits in 64 KiB; 0 if none.
+static int prefill_attn_rows(int G, int hs)
 {
-    return G >= 1 && G <= kMaxG && (kMaxG % G) == 0 && attn_core_supported<kPAThreads>(kMaxG, hs) &&
-           attn_core_lds_bytes<kPAThreads>(kMaxG, hs) <= 64 * 1024;
+    for (int kg = kMaxG; kg >= 1; kg /= 2)
+        if (kg >= G && kg % G == 0 && attn_core_supported<kPAThreads>(kg, hs) &&
+            attn_core_lds_bytes<kPAThreads>(kg, hs) <= 64 * 1024)
+            return kg;
+    return 0;
 }
+
+bool prefill_attn_supported(int G, int hs) { return G >= 1 && prefill_attn_rows(G, hs) > 0; }
 
 hipError_t launch_prefill_attn(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
-    if (!prefill_attn_supported(p.G, p.hs)) return hipErrorInvalidValue;
-    const int TB = kMaxG / p.G;
+    const int kg = prefill_attn_rows(p.G, p.hs);
+    if (kg == 0) return hipErrorInvalidValue;
+    const int TB = kg / p.G;
     const dim3 grid((unsigned)p.nkv, (unsigned)((p.m + TB - 1) / TB));
-    const size_t lds = attn_core_lds_bytes<kPAThreads>(kMaxG, p.hs);
-    if (ev)
-        hipExtLaunchKernelGGL(prefill_attn_kernel<kMaxG>, grid, dim3(kPAThreads), (uint32_t)lds, s, ev->start,
-                              ev->stop, 0u, p);
-    else
-        hipLaunchKernelGGL(prefill_attn_kernel<kMaxG>, grid, dim3(kPAThreads), lds, s, p);
+    const size_t lds = attn_core_lds_bytes<kPAThreads>(kg, p.hs);
+#define L2D_PA(KG)                                                                                  \
+    if (ev)                                                                                         \
+        hipExtLaunchKernelGGL(prefill_attn_kernel<KG>, grid, dim3(kPAThreads), (uint32_t)lds, s,    \
+                              ev->start, ev->stop, 0u, p);                                          \
+    else                                                                                            \
+        hipLaunchKernelGGL(prefill_attn_kernel<KG>, grid, dim3(kPAThreads), lds, s, p);
+    switch (kg) {
+    case 8: L2D_PA(8) break;
+    case 4: L2D_PA(4) break;
+    case 2: L2D_PA(2) break;
+    case 1: L2D_PA(1) break;
+    default: return hipErrorInvalidValue;
+    }
+#undef L2D_PA
     return hipGetLastError();
 }
 

@@ -1,12 +1,16 @@
-"""Batched prompt prefill (int8 MFMA matmuls, causal attention over token
-blocks) against the oracle's token-by-token decode, through the C ABI: the
-K/V cache rows the prefill writes, the last token's logits and argmax, and
-the decode that continues from it on the device.
+"""Batched prompt prefill (int8 MFMA matmuls for Q8_0, fp64 MFMA for fp32
+weights, causal attention over token blocks) against the oracle's
+token-by-token decode, through the C ABI: the K/V cache rows the prefill
+writes, the last token's logits and argmax, and the decode that continues
+from it on the device.
 
 Small models cover group sizes 64, 128 and 256, GQA ratios 1, 2 and 8 (token
-blocks of 8, 4 and 1 per attention workgroup), ragged token counts, prompts
-longer than one 512-token chunk and prefill in two calls at pos0 > 0; the
-7B shape runs at full size."""
+blocks of 8, 4 and 1 per attention workgroup), head sizes 8 to 128, ragged
+token counts, prompts longer than one 512-token chunk and prefill in two
+calls at pos0 > 0; the 7B shape runs at full size in both dtypes. Q8_0 is
+bit-identical by construction (same exact group dots, same fp64 order); fp32
+sums the same exact products in another fp64 order, like the decode step's
+fp32 GEMV, and is held to the logits tolerance."""
 import gc
 
 import numpy as np
@@ -29,18 +33,18 @@ def _check_cache(ctx, orc, lo: int, hi: int, st: Stats):
     st.add("v", vc[:, lo:hi].cpu().numpy(), orc.value_cache()[:, lo:hi])
 
 
-def _run(cfg, gs: int, calls, cont: int = 6):
+def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0):
     """calls: list of (start, n) prefill calls over one prompt; then `cont`
     greedy decode steps on the device, teacher-checked against the oracle."""
     torch = need_gpu()
     total = sum(n for _, n in calls)
     tokens = synth.prompt(cfg.seed + 500, total, abs(cfg.vocab))
-    blob = synth.make_blob(cfg, synth.Q8_0, gs=gs)
-    orc = oracle.Model(blob, synth.Q8_0, gs=gs)
+    blob = synth.make_blob(cfg, dtype, gs=gs)
+    orc = oracle.Model(blob, dtype, gs=gs)
     cache_st, logit_st = Stats(), Stats()
-    with l2d.Context(blob, synth.Q8_0, group_size=gs) as ctx:
+    with l2d.Context(blob, dtype, group_size=gs) as ctx:
         for start, n in calls:
-            log(f"  {cfg.name} gs{gs}: prefill {n} tokens at pos {start}")
+            log(f"  {cfg.name} dt{dtype} gs{gs}: prefill {n} tokens at pos {start}")
             ctx.prefill(tokens[start:start + n], start)
             for i in range(n):
                 ref = orc.forward(int(tokens[start + i]), start + i)
@@ -78,6 +82,17 @@ def _run(cfg, gs: int, calls, cont: int = 6):
 def test_prefill_small(cfg, gs, calls):
     cache_st, _ = _run(cfg, gs, calls)
     assert cache_st.exact / cache_st.n > 0.99
+
+
+@pytest.mark.parametrize("name,calls", [
+    ("tiny", [(0, 45)]),                  # head size 8, G = 2
+    ("15M", [(0, 100), (100, 60)]),       # head size 48, second call at pos 100
+    ("110M", [(0, 520)]),                 # a full 512-token chunk, then 8
+])
+def test_prefill_fp32(name, calls):
+    cfg = synth.CONFIGS[name]
+    cache_st, _ = _run(cfg, 64, calls, cont=4, dtype=synth.F32)
+    assert cache_st.exact / cache_st.n > 0.9
 
 
 def test_prefill_110m_two_chunks_and_two_calls():
@@ -127,10 +142,6 @@ def test_prefill_errors():
         with pytest.raises(l2d.L2DError):
             ctx.prefill([1, 2], -1)
         ctx.prefill([1, 2], 0)                           # still usable afterwards
-    blob32 = synth.make_blob(synth.CONFIGS["tiny"], synth.F32)
-    with l2d.Context(blob32, synth.F32) as ctx:
-        with pytest.raises(l2d.L2DError):
-            ctx.prefill([1, 2], 0)                       # fp32 weights: not built
     blob32 = synth.make_blob(TINY_Q8, synth.Q8_0, gs=32)
     with l2d.Context(blob32, synth.Q8_0, group_size=32) as ctx:
         with pytest.raises(l2d.L2DError):
@@ -144,6 +155,17 @@ def test_prefill_7b_q8_full_size():
     cfg = synth.CONFIGS["7B"]
     try:
         _run(cfg, 64, [(0, 64), (64, 24)], cont=2)
+    finally:
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+def test_prefill_7b_fp32_full_size():
+    """7B fp32: 20 prompt tokens, then 8 more at pos 20."""
+    torch = need_gpu()
+    cfg = synth.CONFIGS["7B"]
+    try:
+        _run(cfg, 64, [(0, 20), (20, 8)], cont=1, dtype=synth.F32)
     finally:
         gc.collect()
         torch.cuda.empty_cache()
