@@ -14,7 +14,8 @@ synchronisations.
 
 Prints one JSON line. value = tokens/s of the Q8_0 step at the headline
 position; per-position and fp32 figures, the step with sampling on, the
-batched prefill of a 512-token prompt (Q8_0, int8 MFMA) and the Q4_0 matvec
+batched prefill of a 512-token prompt (int8 MFMA for Q8_0, fp64 MFMA for
+fp32) and the Q4_0 matvec
 on the step's matrix shapes ride along under "detail".
 """
 from __future__ import annotations
@@ -135,10 +136,11 @@ PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
 
 
 def prefill_rates(cfg, ctx, torch, synth, n: int = 512, reps: int = 3) -> dict:
-    """Batched prefill of an n-token prompt at pos 0 (Q8_0): tokens/s over
-    reps timed calls (HIP events on the context's stream), and the mean
-    kernel time of each class from one kernel-stamped pass. The matmuls'
-    rate is their int8 multiply-adds (2 * rows * cols * n ops) per second."""
+    """Batched prefill of an n-token prompt at pos 0: tokens/s over reps
+    timed calls (HIP events on the context's stream), and the mean kernel
+    time of each class from one kernel-stamped pass. The matmuls' rate is
+    their multiply-adds (2 * rows * cols * n ops) per second: int8 MFMA ops
+    for Q8_0, fp64 MFMA flops for fp32 weights."""
     toks = synth.prompt(4242, n, abs(cfg.vocab))
     stream = torch.cuda.ExternalStream(ctx.stream_handle())
     ctx.prefill(toks, 0)
@@ -160,10 +162,10 @@ def prefill_rates(cfg, ctx, torch, synth, n: int = 512, reps: int = 3) -> dict:
         kern[k] = {"avg_us": v * 1e6}
         if k in shapes and v > 0:
             N, K = shapes[k]
-            kern[k]["int8_tops"] = 2.0 * N * K * n / v / 1e12
+            kern[k]["tops"] = 2.0 * N * K * n / v / 1e12
     out = {"tokens": n, "ms": sec * 1e3, "tok_s": n / sec, "kernels": kern}
     log(f"[bench] prefill of {n} tokens: {sec * 1e3:.2f} ms, {n / sec:.0f} tok/s; " +
-        ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['int8_tops']:.0f}TOP/s" if 'int8_tops' in v else "")
+        ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['tops']:.1f}TOP/s" if 'tops' in v else "")
                   for k, v in kern.items()))
     return out
 
@@ -251,7 +253,7 @@ def main():
     ap.add_argument("--no-fill", action="store_true",
                     help="skip the greedy decode that fills the cache (profiling runs)")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the batched prefill measurement (Q8_0)")
+                    help="skip the batched prefill measurement")
     ap.add_argument("--prefill-tokens", type=int, default=512)
     ap.add_argument("--no-q4-gemv", action="store_true",
                     help="skip the Q4_0 matvec measurement")
@@ -305,8 +307,8 @@ def main():
         log(f"[bench] {name} kernels at pos {args.headline_pos}: " +
             ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['gbs']:.0f}GB/s" if 'gbs' in v else "")
                       for k, v in kern.items()))
-        if dt == 1 and not args.no_prefill:
-            detail["prefill_q8_0"] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
+        if not args.no_prefill:
+            detail["prefill_" + name] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
         if head is None:
             head = (dt, res[args.headline_pos], kt, b)
         ctx.close()
