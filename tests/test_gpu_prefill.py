@@ -5,7 +5,7 @@ writes, the last token's logits and argmax, and the decode that continues
 from it on the device.
 
 Small models cover group sizes 64, 128 and 256, GQA ratios 1, 2 and 8 (token
-blocks of 8, 4 and 1 per attention workgroup), head sizes 8 to 128, ragged
+blocks of 4, 2 and 1 per attention workgroup), head sizes 8 to 128, ragged
 token counts, prompts longer than one 512-token chunk and prefill in two
 calls at pos0 > 0; the 7B shape runs at full size in both dtypes. Q8_0 is
 bit-identical by construction (same exact group dots, same fp64 order); fp32
@@ -73,7 +73,7 @@ def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0):
 
 
 @pytest.mark.parametrize("cfg,gs,calls", [
-    (TINY_Q8, 64, [(0, 41)]),            # G = 2: blocks of 4 tokens, ragged
+    (TINY_Q8, 64, [(0, 41)]),            # G = 2: blocks of 2 tokens, ragged
     (TINY_Q8, 128, [(0, 37)]),           # two 64-value MFMA parts per group
     (TINY_Q8, 64, [(0, 1)]),             # a single token
     (GQA8_Q8, 64, [(0, 50)]),            # G = 8: one token per block
