@@ -17,6 +17,7 @@ _SO = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 Q8_0 = 1
+Q4_0 = 2
 
 
 def build(force: bool = False) -> str:
@@ -222,7 +223,9 @@ def sample(logits: np.ndarray, temperature: float, seed: int, pos: int) -> int:
 class Model:
     """The oracle over a weight blob (numpy uint8, kept alive here)."""
 
-    def __init__(self, blob: np.ndarray, dtype: int, gs: int = 64):
+    def __init__(self, blob: np.ndarray, dtype: int, gs: int | None = None):
+        if gs is None:
+            gs = 32 if dtype == Q4_0 else 64
         self._blob = blob
         h = ctypes.c_void_p()
         rc = _load().or_open(_ptr(blob), blob.size, dtype, gs, ctypes.byref(h))

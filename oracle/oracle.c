@@ -43,6 +43,7 @@
 
 #define OR_F32 0
 #define OR_Q8_0 1
+#define OR_Q4_0 2
 
 #define OR_OK 0
 #define OR_EINVAL -1
@@ -53,10 +54,12 @@ typedef struct {
     int32_t dim, hidden_dim, n_layers, n_heads, n_kv_heads, vocab_size, seq_len;
 } or_config;
 
-/* one matrix: fp32 values, or Q8_0 codes + one fp32 scale per gs elements */
+/* one matrix: fp32 values, Q8_0 codes, or Q4_0 packed codes (two per
+   byte), with one fp32 scale per gs elements */
 typedef struct {
     const float* f;
     const int8_t* q;
+    const uint8_t* p;
     const float* s;
 } or_mat;
 
@@ -98,10 +101,15 @@ static int take_mat(or_model* m, const uint8_t** p, const uint8_t* end, int64_t 
     if (m->dtype == OR_F32) {
         if (!take(p, end, 4 * n, &a)) return 0;
         w->f = (const float*)a;
-    } else {
+    } else if (m->dtype == OR_Q8_0) {
         if (!take(p, end, n, &a)) return 0;
         w->q = (const int8_t*)a;
         if (!take(p, end, 4 * (n / m->gs), &a)) return 0;
+        w->s = (const float*)a;
+    } else {
+        if (!take(p, end, n / 2, &a)) return 0;
+        w->p = (const uint8_t*)a;
+        if (!take(p, end, 4 * (n / 32), &a)) return 0;
         w->s = (const float*)a;
     }
     return 1;
@@ -115,11 +123,17 @@ static int take_mat(or_model* m, const uint8_t** p, const uint8_t* end, int64_t 
  * notes, Q&A page, shared_weights question). The two legacy freq_cis tables,
  * seq_len*head_size/2 floats each, are skipped (same Q&A page, question on
  * skipping freq_cis in memory_map_weights).
+ * dtype OR_Q4_0 (gs must be 32) reads the 4-bit variant as a whole model:
+ * every matrix, the embedding included, is stored as packed Q4_0 codes
+ * [n/2] followed by fp32 scales [n/32] (the group layout described at
+ * or_quantize_q40); every matvec quantises its input to Q8_0 with groups of
+ * 32 (W4A8, the Q8_0 scheme with 4-bit weights); norm gains, legacy tables,
+ * KV cache and activations stay fp32.
  */
 int or_open(const void* blob, int64_t nbytes, int dtype, int gs, or_model** out)
 {
     *out = NULL;
-    if (!blob || nbytes < 28 || (dtype != OR_F32 && dtype != OR_Q8_0)) return OR_EINVAL;
+    if (!blob || nbytes < 28 || (dtype != OR_F32 && dtype != OR_Q8_0 && dtype != OR_Q4_0)) return OR_EINVAL;
     or_model* m = (or_model*)calloc(1, sizeof(or_model));
     if (!m) return OR_ENOMEM;
     memcpy(&m->c, blob, 28);
@@ -141,6 +155,12 @@ int or_open(const void* blob, int64_t nbytes, int dtype, int gs, or_model** out)
     m->kvd = m->nkv * m->hs;
     m->kvmul = m->nh / m->nkv;
     if (dtype == OR_Q8_0 && (gs <= 0 || m->d % gs || m->h % gs)) {
+        free(m);
+        return OR_EINVAL;
+    }
+    /* Q4_0 model: every matrix stored as 4-bit groups of 32 (the reading
+       below), every matvec input quantised to Q8_0 with the same groups */
+    if (dtype == OR_Q4_0 && (gs != 32 || m->d % 32 || m->h % 32)) {
         free(m);
         return OR_EINVAL;
     }
@@ -333,11 +353,19 @@ static void matvec_q80_rows(float* out, const int8_t* aq, const float* as, const
     }
 }
 
+static void matvec_q40_rows(float* out, const int8_t* aq, const float* as, const uint8_t* Q,
+                            const float* S, int64_t rows, int64_t cols);
+
 static void matvec(or_model* m, float* out, const float* x, const or_mat* w, int64_t woff,
                    int64_t rows, int64_t cols, int trace_slot)
 {
     if (m->dtype == OR_F32) {
         matvec_f32_rows(out, x, w->f + woff, rows, cols);
+        return;
+    }
+    if (m->dtype == OR_Q4_0) {
+        or_quantize(x, cols, 32, m->aq, m->as);
+        matvec_q40_rows(out, m->aq, m->as, w->p + woff / 2, w->s + woff / 32, rows, cols);
         return;
     }
     int gs = m->gs;
@@ -438,6 +466,22 @@ int or_group_dots_q40(const uint8_t* wq, const int8_t* xq, int64_t cols, int32_t
     return OR_OK;
 }
 
+/* rows of a Q4_0 matvec over already quantised input codes aq / scales as */
+static void matvec_q40_rows(float* out, const int8_t* aq, const float* as, const uint8_t* Q,
+                            const float* S, int64_t rows, int64_t cols)
+{
+    const int64_t ng = cols / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; i++) {
+        const uint8_t* qr = Q + i * (cols / 2);
+        const float* sr = S + i * ng;
+        double acc = 0.0;
+        for (int64_t g = 0; g < ng; g++)
+            acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g] * (double)as[g];
+        out[i] = (float)acc;
+    }
+}
+
 /* Q4_0 matvec: Q packed [rows][cols/2], S [rows][cols/32]; x quantised first */
 int or_matvec_q40(const uint8_t* Q, const float* S, const float* x, int64_t rows, int64_t cols, float* out)
 {
@@ -450,16 +494,7 @@ int or_matvec_q40(const uint8_t* Q, const float* S, const float* x, int64_t rows
         return OR_ENOMEM;
     }
     or_quantize(x, cols, 32, aq, as);
-    const int64_t ng = cols / 32;
-    #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < rows; i++) {
-        const uint8_t* qr = Q + i * (cols / 2);
-        const float* sr = S + i * ng;
-        double acc = 0.0;
-        for (int64_t g = 0; g < ng; g++)
-            acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g] * (double)as[g];
-        out[i] = (float)acc;
-    }
+    matvec_q40_rows(out, aq, as, Q, S, rows, cols);
     free(aq);
     free(as);
     return OR_OK;
@@ -654,9 +689,18 @@ int or_forward(or_model* m, int token, int pos)
     if (token < 0 || token >= m->V || pos < 0 || pos >= m->S) return OR_EINVAL;
     int64_t d = m->d, h = m->h, kvd = m->kvd, hs = m->hs;
 
-    /* embedding row; Q8_0 dequantises it (code times its group scale) */
+    /* embedding row; Q8_0 and Q4_0 dequantise it (code times its group scale) */
     if (m->dtype == OR_F32) {
         memcpy(m->x, m->emb.f + (int64_t)token * d, (size_t)d * 4);
+    } else if (m->dtype == OR_Q4_0) {
+        const uint8_t* pr = m->emb.p + (int64_t)token * d / 2;
+        const float* sr = m->emb.s + (int64_t)token * d / 32;
+        for (int64_t i = 0; i < d; i++) {
+            const int64_t g = i / 32, j = i % 32;
+            const uint8_t b = pr[g * 16 + j % 16];
+            const int code = (j < 16 ? (b & 15) : (b >> 4)) - 8;
+            m->x[i] = (float)((double)code * (double)sr[g]);
+        }
     } else {
         const int8_t* qr = m->emb.q + (int64_t)token * d;
         const float* sr = m->emb.s + (int64_t)token * d / m->gs;

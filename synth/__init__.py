@@ -20,6 +20,7 @@ _SO = os.path.join(_HERE, "libsynth.so")
 
 F32 = 0
 Q8_0 = 1
+Q4_0 = 2  # 4-bit groups of 32 (gs is always 32)
 
 
 @dataclass(frozen=True)
@@ -120,6 +121,8 @@ def _ccfg(cfg) -> _CCfg:
 
 
 def blob_bytes(cfg, dtype: int, gs: int = GS) -> int:
+    if dtype == Q4_0:
+        gs = 32
     return int(_load().synth_blob_bytes(ctypes.byref(_ccfg(cfg)), dtype, gs))
 
 
@@ -127,6 +130,8 @@ def make_blob(cfg, dtype: int, seed: int | None = None, gs: int = GS) -> np.ndar
     """Return the blob as a uint8 numpy array (header + arrays)."""
     if seed is None:
         seed = cfg.seed
+    if dtype == Q4_0:
+        gs = 32
     n = blob_bytes(cfg, dtype, gs)
     if n < 0:
         raise ValueError("invalid config for blob")

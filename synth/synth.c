@@ -19,7 +19,10 @@
  *
  * In the Q8_0 blob every matrix (E, wq, wk, wv, wo, w1, w2, w3, wcls) is
  * stored as int8 codes[n] followed by fp32 scales[n/GS]; norm gains and the
- * legacy tables stay fp32.
+ * legacy tables stay fp32. In the Q4_0 blob (dtype 2, groups of 32) every
+ * matrix is stored as packed 4-bit codes[n/2] (16 bytes per group: byte b
+ * holds code b + 8 in its low nibble and code b + 16 + 8 in its high one)
+ * followed by fp32 scales[n/32].
  *
  * Values. Every element is a pure function of (seed, tensor id, element
  * index) through the splitmix64 finaliser (Steele, Lea, Flood, "Fast
@@ -31,6 +34,9 @@
  *   - Q8_0 matrices: codes are the same centred sum mapped to [-127, 127]
  *     with integer arithmetic; each group scale is drawn uniformly from
  *     [0.75, 1.25] x 0.02/sd(code), so dequantised weights have sd ~0.02.
+ *   - Q4_0 matrices: the centred sum mapped to [-8, 8] with integer
+ *     arithmetic and 8 clipped to 7; scales as for Q8_0 with the 4-bit
+ *     code's sd.
  *   - norm gains are 1.0; the legacy freq_cis tables are NaN so that a loader
  *     that fails to skip them poisons every logit.
  */
@@ -106,7 +112,8 @@ static int valid(const synth_config* c, int dtype, int gs)
         c->n_kv_heads <= 0 || c->vocab_size == 0 || c->seq_len <= 0)
         return 0;
     if (c->dim % c->n_heads) return 0;
-    if (dtype == 1) {
+    if (dtype == 2 && gs != 32) return 0;
+    if (dtype == 1 || dtype == 2) {
         /* groups never straddle a matrix row */
         if (gs <= 0 || c->dim % gs || c->hidden_dim % gs) return 0;
         part p[16];
@@ -117,7 +124,8 @@ static int valid(const synth_config* c, int dtype, int gs)
     return 1;
 }
 
-/* total blob bytes; dtype 0 = fp32, 1 = Q8_0 with group size gs; -1 if invalid */
+/* total blob bytes; dtype 0 = fp32, 1 = Q8_0 with group size gs, 2 = Q4_0
+   (gs 32); -1 if invalid */
 int64_t synth_blob_bytes(const synth_config* c, int dtype, int gs)
 {
     if (!valid(c, dtype, gs)) return -1;
@@ -127,6 +135,8 @@ int64_t synth_blob_bytes(const synth_config* c, int dtype, int gs)
     for (int i = 0; i < n; i++) {
         if (dtype == 1 && p[i].is_matrix)
             bytes += p[i].n + 4 * (p[i].n / gs);
+        else if (dtype == 2 && p[i].is_matrix)
+            bytes += p[i].n / 2 + 4 * (p[i].n / 32);
         else
             bytes += 4 * p[i].n;
     }
@@ -154,6 +164,33 @@ static void fill_codes(int8_t* dst, int64_t n, uint64_t seed, int tid)
         dst[i] = (int8_t)(bell(draw(seed, (uint64_t)tid, (uint64_t)i)) * 127 / 131070);
 }
 
+/* 4-bit codes of element i: the bell sum mapped to [-8, 8], 8 clipped to 7 */
+static inline int code4(uint64_t seed, int tid, int64_t i)
+{
+    const int64_t c = bell(draw(seed, (uint64_t)tid, (uint64_t)i)) * 8 / 131070;
+    return c > 7 ? 7 : (int)c;
+}
+
+static void fill_codes4(uint8_t* dst, int64_t n, uint64_t seed, int tid)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < n / 32; g++)
+        for (int b = 0; b < 16; b++)
+            dst[g * 16 + b] = (uint8_t)((code4(seed, tid, g * 32 + b) + 8) |
+                                        ((code4(seed, tid, g * 32 + b + 16) + 8) << 4));
+}
+
+static void fill_scales_sd(float* dst, int64_t ng, uint64_t seed, int tid, double code_sd)
+{
+    const double base = 0.02 / code_sd;
+    #pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < ng; g++) {
+        double u = (double)(draw(seed, (uint64_t)(T_SCALE_BASE + tid), (uint64_t)g) >> 11) *
+                   (1.0 / 9007199254740992.0);
+        dst[g] = (float)(base * (0.75 + 0.5 * u));
+    }
+}
+
 static void fill_scales(float* dst, int64_t ng, uint64_t seed, int tid)
 {
     /* sd of a code is bell_sd * 127 / 131070 */
@@ -178,7 +215,13 @@ int synth_fill_blob(const synth_config* c, int dtype, int gs, uint64_t seed, uin
     part p[16];
     int n = parts_of(c, p);
     for (int i = 0; i < n; i++) {
-        if (dtype == 1 && p[i].is_matrix) {
+        if (dtype == 2 && p[i].is_matrix) {
+            fill_codes4(ptr, p[i].n, seed, p[i].tid);
+            ptr += p[i].n / 2;
+            /* n / 2 is a multiple of 16: the scales stay 4-byte aligned */
+            fill_scales_sd((float*)ptr, p[i].n / 32, seed, p[i].tid, bell_sd() * 8.0 / 131070.0);
+            ptr += 4 * (p[i].n / 32);
+        } else if (dtype == 1 && p[i].is_matrix) {
             int8_t* q = (int8_t*)ptr;
             fill_codes(q, p[i].n, seed, p[i].tid);
             ptr += p[i].n;

@@ -4,7 +4,8 @@ GPU library, for the brute-force reference and for building twin models.
 Layout: seven int32 (dim, hidden_dim, n_layers, n_heads, n_kv_heads,
 vocab_size, seq_len), then E, rms_att, wq, wk, wv, wo, rms_ffn, w1, w2, w3,
 rms_final, freq_cis_real, freq_cis_imag, and wcls when vocab_size < 0. A
-Q8_0 matrix is int8 codes[n] followed by fp32 scales[n/gs].
+Q8_0 matrix is int8 codes[n] followed by fp32 scales[n/gs]; a Q4_0 matrix
+(dtype 2) is packed 4-bit codes[n/2] followed by fp32 scales[n/32].
 """
 from __future__ import annotations
 
@@ -34,6 +35,11 @@ def layout(hdr, dtype: int, gs: int = 64):
             sshape = shape[:-1] + (shape[-1] // gs,)
             out.append((name, "s", off, sshape))
             off += 4 * (n // gs)
+        elif dtype == 2 and name in MATS:
+            out.append((name, "p", off, shape[:-1] + (shape[-1] // 2,)))
+            off += n // 2
+            out.append((name, "s", off, shape[:-1] + (shape[-1] // 32,)))
+            off += 4 * (n // 32)
         else:
             out.append((name, "f", off, shape))
             off += 4 * n
@@ -49,11 +55,13 @@ def view(blob: np.ndarray, dtype: int, gs: int = 64) -> dict:
         n = int(np.prod(shape))
         if kind == "q":
             w[name + ".q"] = blob[off:off + n].view(np.int8).reshape(shape)
+        elif kind == "p":
+            w[name + ".p"] = blob[off:off + n].reshape(shape)
         else:
             w[name + ("." + kind if kind == "s" else "")] = \
                 blob[off:off + 4 * n].view(np.float32).reshape(shape)
     if hdr[5] > 0:
-        for k in ("q", "s"):
+        for k in ("q", "p", "s"):
             if "emb." + k in w:
                 w["wcls." + k] = w["emb." + k]
         if "emb" in w:

@@ -12,7 +12,9 @@ interleaved pairs with freq_j = fp32(10000^(-2j/hs)) and an fp32 angle; score
 scale 1/sqrt(hs); query head h reads kv head h // (n_heads/n_kv_heads);
 SwiGLU silu(w1 x) * w3 x; Q8_0 activations quantised per group as the
 gitcode porting guide's quantize listing (float max, float division by 127,
-round half away from zero).
+round half away from zero). Q4_0 models (dtype 2): 4-bit weight codes
+unpacked from their 16-byte groups, inputs quantised to Q8_0 with groups of
+32, the same exact integer group dots.
 """
 from __future__ import annotations
 
@@ -39,12 +41,24 @@ def quantize_rows(x: np.ndarray, gs: int):
     return q.astype(np.int8).reshape(T, n), scale
 
 
+def unpack_q4(P: np.ndarray) -> np.ndarray:
+    """4-bit codes in [-8, 7] of packed groups (..., n/2) -> (..., n): byte b
+    of a 16-byte group holds code b + 8 (low nibble) and code b + 16 + 8."""
+    g = P.reshape(P.shape[:-1] + (P.shape[-1] // 16, 16)).astype(np.int16)
+    codes = np.concatenate([(g & 15) - 8, (g >> 4) - 8], axis=-1)
+    return codes.reshape(P.shape[:-1] + (P.shape[-1] * 2,)).astype(np.int8)
+
+
 def matmul(xs: np.ndarray, w: dict, name: str, layer, dtype: int, gs: int):
     """rows of xs (T, cols) times the matrix name[layer]^T -> (T, rows) fp32."""
     if dtype == 0:
         W = w[name] if layer is None else w[name][layer]
         return (xs.astype(f64) @ W.astype(f64).T).astype(f32), None
-    Q = w[name + ".q"] if layer is None else w[name + ".q"][layer]
+    if dtype == 2:
+        Q = unpack_q4(w[name + ".p"] if layer is None else w[name + ".p"][layer])
+        gs = 32
+    else:
+        Q = w[name + ".q"] if layer is None else w[name + ".q"][layer]
     S = w[name + ".s"] if layer is None else w[name + ".s"][layer]
     rows, cols = Q.shape
     ng = cols // gs
@@ -95,6 +109,10 @@ def forward_all(blob: np.ndarray, dtype: int, tokens, gs: int = 64, trace_layer=
     pos = np.arange(T)
     if dtype == 0:
         x = w["emb"][tokens].astype(f32)
+    elif dtype == 2:
+        q = unpack_q4(w["emb.p"][tokens]).astype(f64)
+        s = np.repeat(w["emb.s"][tokens].astype(f64), 32, axis=1)
+        x = (q * s).astype(f32)
     else:
         q = w["emb.q"][tokens].astype(f64)
         s = np.repeat(w["emb.s"][tokens].astype(f64), gs, axis=1)

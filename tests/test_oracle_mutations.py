@@ -51,6 +51,10 @@ MUTATIONS = {
     "q40_clamp_8": ("v = r < -8.0f ? -8 : r > 7.0f ? 7 : (int)r;", "v = r < -8.0f ? -8 : r > 8.0f ? 8 : (int)r;"),
     "q40_input_scale_dropped": ("acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g] * (double)as[g];",
                                 "acc += (double)q40_group_dot(qr + g * 16, aq + g * 32) * (double)sr[g];"),
+    "q40_model_embedding_nibbles_swapped": ("const int code = (j < 16 ? (b & 15) : (b >> 4)) - 8;",
+                                            "const int code = (j < 16 ? (b >> 4) : (b & 15)) - 8;"),
+    "q40_model_weight_offset": ("matvec_q40_rows(out, m->aq, m->as, w->p + woff / 2, w->s + woff / 32, rows, cols);",
+                                "matvec_q40_rows(out, m->aq, m->as, w->p + woff / 2, w->s + woff / 64, rows, cols);"),
     "sample_temperature_multiplies": ("return (float)((double)logit / temperature + g);",
                                       "return (float)((double)logit * temperature + g);"),
     "sample_gumbel_sign": ("const double g = -log(-log(u));", "const double g = log(-log(u));"),
@@ -65,6 +69,7 @@ PIN_TESTS = [
     pins.test_rope_preserves_pair_norms_and_relative_position,
     lambda: pins.test_oracle_matches_full_sequence_bruteforce(pins.TINY, 0, 12),
     lambda: pins.test_oracle_matches_full_sequence_bruteforce(pins.TINY_Q8, 1, 8),
+    lambda: pins.test_oracle_matches_full_sequence_bruteforce(pins.TINY_Q4, 2, 8),
     pins.test_attention_pos0_is_v_and_equal_keys_give_mean_v,
     pins.test_rmsnorm_closed_form_through_embedding,
     sampling_pins.test_splitmix64_published_outputs,

@@ -25,6 +25,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TINY = synth.CONFIGS["tiny"]
 TINY_Q8 = synth.Config("tinyq8", 128, 256, 3, 4, 2, 320, 64, 11, (synth.Q8_0,))
 TINY_Q8_UNSHARED = TINY_Q8.replace(name="tinyq8u", vocab_size=-320, seed=12)
+TINY_Q4 = synth.Config("tinyq4", 128, 256, 3, 4, 2, 320, 64, 21, (synth.Q4_0,))
+TINY_Q4_UNSHARED = TINY_Q4.replace(name="tinyq4u", vocab_size=-320, seed=22)
 
 
 def _ulp(x):
@@ -223,6 +225,8 @@ def _traj(model, n):
     (TINY, synth.F32, 64),
     (TINY_Q8, synth.Q8_0, 48),
     (TINY_Q8_UNSHARED, synth.Q8_0, 24),
+    (TINY_Q4, synth.Q4_0, 40),
+    (TINY_Q4_UNSHARED, synth.Q4_0, 24),
 ])
 def test_oracle_matches_full_sequence_bruteforce(cfg, dtype, n):
     """Cached decode == non-cached causal recomputation at every position."""
