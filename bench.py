@@ -13,10 +13,10 @@ same values), timed with HIP events on the context's stream between two
 synchronisations.
 
 Prints one JSON line. value = tokens/s of the Q8_0 step at the headline
-position; per-position and fp32 figures, the step with sampling on, the
-batched prefill of a 512-token prompt (int8 MFMA for Q8_0, fp64 MFMA for
-fp32) and the Q4_0 matvec
-on the step's matrix shapes ride along under "detail".
+position. Under "detail" ride along: per-position, fp32 and Q4_0 (4-bit
+weights) figures, the step with sampling on, the batched prefill of a
+512-token prompt (int8 MFMA for Q8_0, fp64 MFMA for fp32) and the Q4_0
+matvec on the step's matrix shapes.
 """
 from __future__ import annotations
 
@@ -45,7 +45,9 @@ def step_bytes(cfg, dtype: int, pos: int, gs: int = 64) -> dict:
     and the k/v slot written."""
     d, h, L, V = cfg.dim, cfg.hidden_dim, cfg.n_layers, cfg.vocab
     kvd = cfg.kv_dim
-    bpp = 4.0 if dtype == 0 else 1.0 + 4.0 / gs
+    # bytes per weight: fp32 4; Q8_0 code byte + scale share; Q4_0 half a
+    # byte + a 4-byte scale per 32
+    bpp = 4.0 if dtype == 0 else 1.0 + 4.0 / gs if dtype == 1 else 0.5 + 4.0 / 32
     qkv = (d + 2 * kvd) * d * bpp
     wo = d * d * bpp
     w13 = 2 * h * d * bpp
@@ -195,7 +197,7 @@ def decode_to(ctx, positions, torch, fill=True):
 def bench_dtype(cfg, dtype, positions, steps, warmup, torch, l2d, synth, fill=True):
     t = time.time()
     blob = synth.make_blob(cfg, dtype)
-    log(f"[bench] {cfg.name} dtype={'q8_0' if dtype else 'fp32'}: blob {blob.size / 1e9:.2f} GB "
+    log(f"[bench] {cfg.name} dtype={('fp32', 'q8_0', 'q4_0')[dtype]}: blob {blob.size / 1e9:.2f} GB "
         f"generated in {time.time() - t:.1f}s")
     t = time.time()
     ctx = l2d.Context(blob, dtype)
@@ -247,7 +249,7 @@ def main():
     ap.add_argument("--config", default="7B")
     ap.add_argument("--positions", default="1,512,2048")
     ap.add_argument("--headline-pos", type=int, default=512)
-    ap.add_argument("--dtypes", default="q8_0,fp32")
+    ap.add_argument("--dtypes", default="q8_0,fp32,q4_0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-fill", action="store_true",
@@ -280,11 +282,13 @@ def main():
         del a, b
     cfg = synth.CONFIGS[args.config]
     positions = sorted({int(p) for p in args.positions.split(",")} | {args.headline_pos})
-    dtypes = [0 if d.strip() == "fp32" else 1 for d in args.dtypes.split(",")]
+    codes = {"fp32": 0, "q8_0": 1, "q4_0": 2}
+    names = {v: k for k, v in codes.items()}
+    dtypes = [codes[d.strip()] for d in args.dtypes.split(",")]
     detail = {}
     head = None
     for dt in dtypes:
-        name = "q8_0" if dt else "fp32"
+        name = names[dt]
         ctx, fed, res = bench_dtype(cfg, dt, positions, args.steps, args.warmup, torch, l2d, synth,
                                     not args.no_fill)
         # per-kernel HIP-event timing at the headline position
@@ -307,7 +311,7 @@ def main():
         log(f"[bench] {name} kernels at pos {args.headline_pos}: " +
             ", ".join(f"{k} {v['avg_us']:.1f}us" + (f" {v['gbs']:.0f}GB/s" if 'gbs' in v else "")
                       for k, v in kern.items()))
-        if not args.no_prefill:
+        if not args.no_prefill and dt != 2:  # no batched prefill for 4-bit weights
             detail["prefill_" + name] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
         if head is None:
             head = (dt, res[args.headline_pos], kt, b)
@@ -328,10 +332,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xint8->int32, fp32/fp64" if dt else "f32 (fp64 accumulate)",
+        "dtype": {0: "f32 (fp64 accumulate)", 1: "int8xint8->int32, fp32/fp64",
+                  2: "int4xint8->int32, fp32/fp64"}[dt],
         "data": "synthetic: seeded random N(0,0.02)-like weights of the 7B shape",
         "config": {"workload": f"{cfg.name}-shape Llama-2 decode step, "
-                               f"{'Q8_0 GS=64' if dt else 'fp32'}, batch 1, pos {args.headline_pos}",
+                               f"{('fp32', 'Q8_0 GS=64', 'Q4_0 GS=32')[dt]}, batch 1, pos {args.headline_pos}",
                    "global_batch": 1, "seq_len": cfg.seq_len, "pos": args.headline_pos,
                    "parallelism": "single GPU"},
         "hbm_step_gbs": r["step_gbs"],

@@ -30,8 +30,8 @@ extern "C" {
 
 #define L2D_F32 0  /* fp32 weights and activations (run.c) */
 #define L2D_Q8_0 1 /* int8 weight/activation codes, fp32 group scales (runq.c) */
-#define L2D_Q4_0 2 /* 4-bit weight codes in groups of 32, fp32 group scales (l2d_gemv only;
-                      the 4-bit variant the ainews article names) */
+#define L2D_Q4_0 2 /* 4-bit weight codes in groups of 32, fp32 group scales, int8 activations
+                      (the 4-bit variant the ainews article names; group_size 32) */
 
 #define L2D_OK 0
 #define L2D_EINVAL (-1)  /* bad argument: config, group size, token, pos, size */
@@ -49,8 +49,8 @@ extern "C" {
  */
 typedef struct {
     int32_t dim, hidden_dim, n_layers, n_heads, n_kv_heads, vocab_size, seq_len;
-    int32_t dtype;      /* L2D_F32 or L2D_Q8_0 */
-    int32_t group_size; /* Q8_0 group size GS (64 for the workloads); ignored for fp32 */
+    int32_t dtype;      /* L2D_F32, L2D_Q8_0 or L2D_Q4_0 */
+    int32_t group_size; /* Q8_0 group size GS (64 for the workloads); 32 for Q4_0; ignored for fp32 */
     double rope_theta;  /* 10000 */
     double norm_eps;    /* 1e-5 */
 } l2d_config;
@@ -61,6 +61,9 @@ typedef struct {
  * cols the input size. fp32: the matrix pointer is float*, the *_s scale
  * pointer is NULL. Q8_0: the matrix pointer is int8_t codes[rows*cols] and
  * *_s is float scales[rows*cols/GS], one per group of GS consecutive codes.
+ * Q4_0: the matrix pointer is uint8_t packed codes[rows*cols/2], 16 bytes
+ * per group of 32 (byte b: code b + 8 in the low nibble, code b + 16 + 8 in
+ * the high nibble), *_s float scales[rows*cols/32].
  * Per-layer arrays are stacked over layers: wq is [n_layers][dim][dim], etc.
  */
 typedef struct {
@@ -86,7 +89,8 @@ typedef struct l2d_ctx l2d_ctx;
  * w1, w2, w3, rms_final, the two legacy freq_cis tables of
  * seq_len*head_size/2 floats each (skipped: RoPE is computed on the fly,
  * Q&A page, freq_cis question), then wcls when vocab_size < 0. In a Q8_0 blob
- * each matrix is codes[n] then scales[n/GS]. cfg gets the header plus dtype,
+ * each matrix is codes[n] then scales[n/GS]; in a Q4_0 blob (group_size 32)
+ * packed codes[n/2] then scales[n/32]. cfg gets the header plus dtype,
  * group_size, rope_theta = 10000, norm_eps = 1e-5.
  * Errors: L2D_EINVAL for a bad dtype/GS or an invalid header (dim % n_heads,
  * n_heads % n_kv_heads, odd head_size, GS not dividing dim and hidden_dim,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libl2d.so")
 
 F32 = 0
 Q8_0 = 1
-Q4_0 = 2  # matvec (gemv) only
+Q4_0 = 2  # 4-bit weights in groups of 32 (group_size 32)
 
 OK, EINVAL, EFORMAT, ENOMEM, EHIP = 0, -1, -2, -3, -4
 
@@ -168,7 +168,9 @@ def device_view(ptr: int, shape, dtype: str = "<f4"):
 class Context:
     """A decode context: device weights, KV cache and the captured step."""
 
-    def __init__(self, blob: np.ndarray, dtype: int, group_size: int = 64, stream=None):
+    def __init__(self, blob: np.ndarray, dtype: int, group_size: int | None = None, stream=None):
+        if group_size is None:
+            group_size = 32 if dtype == Q4_0 else 64
         self.cfg, w = blob_parse(blob, dtype, group_size)
         h = _vp()
         _check(lib().l2d_init(ctypes.byref(self.cfg), ctypes.byref(w),

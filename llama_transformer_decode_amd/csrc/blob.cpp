@@ -6,7 +6,8 @@
 // legacy freq_cis tables of seq_len*head_size/2 floats each that are skipped
 // (Q&A page, freq_cis question), and wcls only when vocab_size < 0 (Q&A page,
 // shared_weights question). In a Q8_0 blob each matrix is int8 codes[n]
-// followed by fp32 scales[n/GS]. Every offset is 64-bit: the Q&A page
+// followed by fp32 scales[n/GS]; in a Q4_0 blob packed 4-bit codes[n/2]
+// followed by fp32 scales[n/32]. Every offset is 64-bit: the Q&A page
 // records a pointer-arithmetic overflow at 13B and above.
 #include <stdint.h>
 #include <string.h>
@@ -38,6 +39,9 @@ void take_matrix(Cursor& c, int32_t dtype, int32_t gs, uint64_t n, const void** 
     if (dtype == L2D_F32) {
         *m = c.take(n * 4);
         *s = nullptr;
+    } else if (dtype == L2D_Q4_0) {
+        *m = c.take(n / 2);
+        *s = (const float*)c.take((n / 32) * 4);
     } else {
         *m = c.take(n);
         *s = (const float*)c.take((n / (uint64_t)gs) * 4);
@@ -50,12 +54,14 @@ extern "C" int l2d_blob_parse(const void* blob, uint64_t nbytes, int32_t dtype, 
                               l2d_config* cfg, l2d_weights* w)
 {
     if (!blob || !cfg || !w || nbytes < 28) return l2d::fail(nullptr, L2D_EINVAL, "blob_parse: null pointer or blob shorter than its header");
-    if (dtype != L2D_F32 && dtype != L2D_Q8_0) return l2d::fail(nullptr, L2D_EINVAL, "blob_parse: dtype must be L2D_F32 or L2D_Q8_0");
+    if (dtype != L2D_F32 && dtype != L2D_Q8_0 && dtype != L2D_Q4_0)
+        return l2d::fail(nullptr, L2D_EINVAL, "blob_parse: dtype must be L2D_F32, L2D_Q8_0 or L2D_Q4_0");
+    if (dtype == L2D_Q4_0 && gs != 32) return l2d::fail(nullptr, L2D_EINVAL, "blob_parse: Q4_0 needs group size 32");
     l2d_config c;
     memset(&c, 0, sizeof(c));
     memcpy(&c, blob, 28);
     c.dtype = dtype;
-    c.group_size = dtype == L2D_Q8_0 ? gs : 0;
+    c.group_size = dtype == L2D_F32 ? 0 : gs;
     c.rope_theta = 10000.0;
     c.norm_eps = 1e-5;
     int rc = l2d::validate_config(&c);

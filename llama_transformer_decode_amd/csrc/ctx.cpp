@@ -42,7 +42,11 @@ int validate_config(const l2d_config* c)
     if (c->n_heads % c->n_kv_heads) return bad("config: n_heads must be a multiple of n_kv_heads");
     const int hs = c->dim / c->n_heads;
     if (hs % 2) return bad("config: head_size must be even (RoPE rotates pairs)");
-    if (c->dtype != L2D_F32 && c->dtype != L2D_Q8_0) return bad("config: unknown dtype");
+    if (c->dtype != L2D_F32 && c->dtype != L2D_Q8_0 && c->dtype != L2D_Q4_0) return bad("config: unknown dtype");
+    if (c->dtype == L2D_Q4_0) {
+        if (c->group_size != 32) return bad("config: Q4_0 group size must be 32");
+        if (c->dim % 32 || c->hidden_dim % 32) return bad("config: Q4_0 needs dim and hidden_dim multiples of 32");
+    }
     if (c->dtype == L2D_Q8_0) {
         const int gs = c->group_size;
         if (!pow2(gs) || gs < 16 || gs > 256)
@@ -151,6 +155,9 @@ void release(l2d_ctx* ctx)
 
 size_t elt(int dt) { return dt == DT_F32 ? 4 : 1; }
 
+// device bytes of n weights of dtype dt (Q4_0: two codes per byte)
+size_t mat_bytes(int dt, int64_t n) { return dt == DT_F32 ? (size_t)n * 4 : dt == DT_Q8 ? (size_t)n : (size_t)n / 2; }
+
 // Start/stop events of each launch of the kernel-by-kernel step, by kernel
 // class; the events are stamped at the kernel's own start and end.
 struct KernelTimer {
@@ -194,7 +201,7 @@ int enqueue_classifier(l2d_ctx* ctx, KernelTimer* kt, int cls)
     p.eps = ctx->cfg.norm_eps;
     p.step = ctx->step;
     p.W = ctx->wcls;
-    p.Ws = ctx->dt == DT_Q8 ? ctx->wcls_s : nullptr;
+    p.Ws = ctx->dt != DT_F32 ? ctx->wcls_s : nullptr;
     p.M = ctx->V;
     p.K = ctx->d;
     p.x = ctx->x;
@@ -212,11 +219,11 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
 {
     const int64_t d = ctx->d, h = ctx->h, kvd = ctx->kvd;
     const int64_t nqkv = d + 2 * kvd;
-    const size_t es = elt(ctx->dt);
+    const int dt = ctx->dt;
     const int64_t gs = ctx->gs;
     hipStream_t s = ctx->stream;
     auto scales = [&](float* base, int64_t off_elems) -> const float* {
-        return ctx->dt == DT_Q8 ? base + off_elems / gs : nullptr;
+        return dt != DT_F32 ? base + off_elems / gs : nullptr;
     };
     for (int64_t l = 0; l < ctx->L; l++) {
         const bool tr = tracing && l == ctx->trace_layer;
@@ -227,7 +234,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.step = ctx->step;
 
         // RMSNorm -> q/k/v matvec -> RoPE -> KV-cache slot pos
-        p.W = (const uint8_t*)ctx->wqkv + (size_t)(l * nqkv * d) * es;
+        p.W = (const uint8_t*)ctx->wqkv + mat_bytes(dt, l * nqkv * d);
         p.Ws = scales(ctx->wqkv_s, l * nqkv * d);
         p.M = nqkv;
         p.K = d;
@@ -264,7 +271,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         HIP_TRY(ctx, launch_attention(a, s, kt ? &kt->cur : nullptr));
 
         // output projection + residual
-        p.W = (const uint8_t*)ctx->wo + (size_t)(l * d * d) * es;
+        p.W = (const uint8_t*)ctx->wo + mat_bytes(dt, l * d * d);
         p.Ws = scales(ctx->wo_s, l * d * d);
         p.M = d;
         p.K = d;
@@ -277,7 +284,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
 
         // RMSNorm -> w1/w3 matvec -> SwiGLU
-        p.W = (const uint8_t*)ctx->w13 + (size_t)(l * 2 * h * d) * es;
+        p.W = (const uint8_t*)ctx->w13 + mat_bytes(dt, l * 2 * h * d);
         p.Ws = scales(ctx->w13_s, l * 2 * h * d);
         p.M = 2 * h;
         p.K = d;
@@ -290,7 +297,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
 
         // w2 matvec + residual
-        p.W = (const uint8_t*)ctx->w2 + (size_t)(l * d * h) * es;
+        p.W = (const uint8_t*)ctx->w2 + mat_bytes(dt, l * d * h);
         p.Ws = scales(ctx->w2_s, l * d * h);
         p.M = d;
         p.K = h;
@@ -330,7 +337,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     rc = check_supported(ctx, cfg);
     if (rc != L2D_OK) return rc;
     ctx->cfg = *cfg;
-    ctx->dt = cfg->dtype == L2D_F32 ? DT_F32 : DT_Q8;
+    ctx->dt = cfg->dtype == L2D_F32 ? DT_F32 : cfg->dtype == L2D_Q8_0 ? DT_Q8 : DT_Q4;
     ctx->d = cfg->dim;
     ctx->h = cfg->hidden_dim;
     ctx->L = cfg->n_layers;
@@ -341,14 +348,15 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ctx->hs = ctx->d / ctx->nh;
     ctx->kvd = ctx->nkv * ctx->hs;
     ctx->G = ctx->nh / ctx->nkv;
-    ctx->gs = ctx->dt == DT_Q8 ? cfg->group_size : 1;
+    ctx->gs = ctx->dt != DT_F32 ? cfg->group_size : 1;
     const bool q8 = ctx->dt == DT_Q8;
+    const bool quant = ctx->dt != DT_F32;  // scales present (Q8_0, Q4_0)
     if (!w || !w->emb || !w->rms_att || !w->wq || !w->wk || !w->wv || !w->wo || !w->rms_ffn ||
         !w->w1 || !w->w2 || !w->w3 || !w->rms_final || !w->wcls)
         return fail(ctx, L2D_EINVAL, "init: a weight pointer is NULL");
-    if (q8 && (!w->emb_s || !w->wq_s || !w->wk_s || !w->wv_s || !w->wo_s || !w->w1_s ||
-               !w->w2_s || !w->w3_s || !w->wcls_s))
-        return fail(ctx, L2D_EINVAL, "init: a Q8_0 scale pointer is NULL");
+    if (quant && (!w->emb_s || !w->wq_s || !w->wk_s || !w->wv_s || !w->wo_s || !w->w1_s ||
+                  !w->w2_s || !w->w3_s || !w->wcls_s))
+        return fail(ctx, L2D_EINVAL, "init: a scale pointer is NULL");
 
     HIP_TRY(ctx, hipGetDevice(&ctx->device));
     int cus = 0;
@@ -366,23 +374,25 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     const int64_t d = ctx->d, h = ctx->h, L = ctx->L, V = ctx->V, kvd = ctx->kvd;
     const int64_t gs = ctx->gs;
     const size_t es = elt(ctx->dt);
+    const int dt = ctx->dt;
     const int64_t nqkv = d + 2 * kvd;
-    auto sbytes = [&](int64_t n) -> size_t { return q8 ? (size_t)(n / gs) * 4 : 0; };
+    auto sbytes = [&](int64_t n) -> size_t { return quant ? (size_t)(n / gs) * 4 : 0; };
+    auto mb = [&](int64_t n) -> size_t { return mat_bytes(dt, n); };
 
-    ALLOC(ctx->emb, (size_t)(V * d) * es);
-    if (q8) ALLOC(ctx->emb_s, sbytes(V * d));
-    ALLOC(ctx->wqkv, (size_t)(L * nqkv * d) * es);
-    if (q8) ALLOC(ctx->wqkv_s, sbytes(L * nqkv * d));
-    ALLOC(ctx->wo, (size_t)(L * d * d) * es);
-    if (q8) ALLOC(ctx->wo_s, sbytes(L * d * d));
-    ALLOC(ctx->w13, (size_t)(L * 2 * h * d) * es);
-    if (q8) ALLOC(ctx->w13_s, sbytes(L * 2 * h * d));
-    ALLOC(ctx->w2, (size_t)(L * d * h) * es);
-    if (q8) ALLOC(ctx->w2_s, sbytes(L * d * h));
+    ALLOC(ctx->emb, mb(V * d));
+    if (quant) ALLOC(ctx->emb_s, sbytes(V * d));
+    ALLOC(ctx->wqkv, mb(L * nqkv * d));
+    if (quant) ALLOC(ctx->wqkv_s, sbytes(L * nqkv * d));
+    ALLOC(ctx->wo, mb(L * d * d));
+    if (quant) ALLOC(ctx->wo_s, sbytes(L * d * d));
+    ALLOC(ctx->w13, mb(L * 2 * h * d));
+    if (quant) ALLOC(ctx->w13_s, sbytes(L * 2 * h * d));
+    ALLOC(ctx->w2, mb(L * d * h));
+    if (quant) ALLOC(ctx->w2_s, sbytes(L * d * h));
     const bool shared = cfg->vocab_size > 0;
     if (!shared) {
-        ALLOC(ctx->wcls, (size_t)(V * d) * es);
-        if (q8) ALLOC(ctx->wcls_s, sbytes(V * d));
+        ALLOC(ctx->wcls, mb(V * d));
+        if (quant) ALLOC(ctx->wcls_s, sbytes(V * d));
     }
     ALLOC(ctx->rms_att, (size_t)(L * d) * 4);
     ALLOC(ctx->rms_ffn, (size_t)(L * d) * 4);
@@ -421,7 +431,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     // the arrays that go through it
     size_t stage = 0;
     for (int64_t n : {L * d * d, L * kvd * d, L * h * d, V * d}) {
-        if ((size_t)n * es > stage) stage = (size_t)n * es;
+        if (mb(n) > stage) stage = mb(n);
         if (sbytes(n) > stage) stage = sbytes(n);
     }
     void* staging = nullptr;
@@ -434,8 +444,6 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     }
     auto up_all = [&]() -> int {
         int r;
-        const size_t lpitch = (size_t)(nqkv * d) * es;
-        const size_t rb = (size_t)d * es;
         if (q8) {
             // codes: group-interleaved rows, placed by the permute kernel
             const int64_t all = 1ll << 62;
@@ -463,19 +471,36 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
             if ((r = upload(ctx, ctx->w2_s, w->w2_s, sbytes(L * d * h)))) return r;
             if (!shared && (r = upload(ctx, ctx->wcls_s, w->wcls_s, sbytes(V * d)))) return r;
         } else {
-            if ((r = upload(ctx, ctx->emb, w->emb, (size_t)(V * d) * es))) return r;
+            // fp32 values, or Q4_0 packed codes (rows read in place)
+            const size_t lp = mb(nqkv * d), rw = mb(d);
+            if ((r = upload(ctx, ctx->emb, w->emb, mb(V * d)))) return r;
             // q, k, v rows of each layer side by side: [L][d + 2kvd][d]
-            if ((r = upload_rows(ctx, ctx->wqkv, lpitch, w->wq, (size_t)(d * d) * es, L, staging))) return r;
-            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)(d * d) * es, lpitch, w->wk,
-                                 (size_t)(kvd * d) * es, L, staging))) return r;
-            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + (size_t)((d + kvd) * d) * es, lpitch, w->wv,
-                                 (size_t)(kvd * d) * es, L, staging))) return r;
-            if ((r = upload(ctx, ctx->wo, w->wo, (size_t)(L * d * d) * es))) return r;
+            if ((r = upload_rows(ctx, ctx->wqkv, lp, w->wq, mb(d * d), L, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + mb(d * d), lp, w->wk, mb(kvd * d), L, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv + mb((d + kvd) * d), lp, w->wv, mb(kvd * d), L,
+                                 staging))) return r;
+            if ((r = upload(ctx, ctx->wo, w->wo, mb(L * d * d)))) return r;
             // w1 / w3 rows interleaved: [L][h][2][d]
-            if ((r = upload_rows(ctx, ctx->w13, 2 * rb, w->w1, rb, L * h, staging))) return r;
-            if ((r = upload_rows(ctx, (uint8_t*)ctx->w13 + rb, 2 * rb, w->w3, rb, L * h, staging))) return r;
-            if ((r = upload(ctx, ctx->w2, w->w2, (size_t)(L * d * h) * es))) return r;
-            if (!shared && (r = upload(ctx, ctx->wcls, w->wcls, (size_t)(V * d) * es))) return r;
+            if ((r = upload_rows(ctx, ctx->w13, 2 * rw, w->w1, rw, L * h, staging))) return r;
+            if ((r = upload_rows(ctx, (uint8_t*)ctx->w13 + rw, 2 * rw, w->w3, rw, L * h, staging))) return r;
+            if ((r = upload(ctx, ctx->w2, w->w2, mb(L * d * h)))) return r;
+            if (!shared && (r = upload(ctx, ctx->wcls, w->wcls, mb(V * d)))) return r;
+            if (quant) {
+                // scales: plain [row][K/32], rows placed like the codes
+                if ((r = upload(ctx, ctx->emb_s, w->emb_s, sbytes(V * d)))) return r;
+                const size_t sp = sbytes(nqkv * d);
+                if ((r = upload_rows(ctx, ctx->wqkv_s, sp, w->wq_s, sbytes(d * d), L, staging))) return r;
+                if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv_s + sbytes(d * d), sp, w->wk_s,
+                                     sbytes(kvd * d), L, staging))) return r;
+                if ((r = upload_rows(ctx, (uint8_t*)ctx->wqkv_s + sbytes((d + kvd) * d), sp, w->wv_s,
+                                     sbytes(kvd * d), L, staging))) return r;
+                if ((r = upload(ctx, ctx->wo_s, w->wo_s, sbytes(L * d * d)))) return r;
+                const size_t sb = sbytes(d);
+                if ((r = upload_rows(ctx, ctx->w13_s, 2 * sb, w->w1_s, sb, L * h, staging))) return r;
+                if ((r = upload_rows(ctx, (uint8_t*)ctx->w13_s + sb, 2 * sb, w->w3_s, sb, L * h, staging))) return r;
+                if ((r = upload(ctx, ctx->w2_s, w->w2_s, sbytes(L * d * h)))) return r;
+                if (!shared && (r = upload(ctx, ctx->wcls_s, w->wcls_s, sbytes(V * d)))) return r;
+            }
         }
         if ((r = upload(ctx, ctx->rms_att, w->rms_att, (size_t)(L * d) * 4))) return r;
         if ((r = upload(ctx, ctx->rms_ffn, w->rms_ffn, (size_t)(L * d) * 4))) return r;

@@ -704,6 +704,10 @@ hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_bl
     L2D_CASE(DT_Q8, PRO_NORM, EPI_SWIGLU)
     L2D_CASE(DT_Q8, PRO_NORM, EPI_LOGITS)
     L2D_CASE(DT_Q8, PRO_PLAIN, EPI_STORE)
+    L2D_CASE(DT_Q4, PRO_NORM, EPI_QKV)
+    L2D_CASE(DT_Q4, PRO_PLAIN, EPI_RESID)
+    L2D_CASE(DT_Q4, PRO_NORM, EPI_SWIGLU)
+    L2D_CASE(DT_Q4, PRO_NORM, EPI_LOGITS)
     L2D_CASE(DT_Q4, PRO_PLAIN, EPI_STORE)
 #undef L2D_CASE
     return hipErrorInvalidValue;

@@ -686,6 +686,7 @@ __global__ __launch_bounds__(kMT, 1) void step_kernel(MegaParams P)
 
 bool mega_supported(int dt, int gs, int64_t d, int64_t h, int G, int hs)
 {
+    if (dt != DT_F32 && dt != DT_Q8) return false;  // built for fp32 and Q8_0 only
     if (dt == DT_Q8 && gs != 64) return false;
     // matvec inputs held in registers by the prologue: 16 (fp32: 4) values
     // per thread in up to 4 (fp32: 8) batches

@@ -10,8 +10,8 @@ namespace l2d {
 // Step start: record (token, pos) for the captured kernels, clear this
 // step's argmax slot, and write the embedding row of token into the residual
 // stream x (the first step of the toy forward pass, mht18 essay section
-// 2.3). Q8_0 rows are dequantised: x_i = code_i * scale of its group (fp32
-// product, exact before the one rounding). In greedy mode the token is the
+// 2.3). Q8_0 and Q4_0 rows are dequantised: x_i = code_i * scale of its
+// group (fp32 product, exact before the one rounding). In greedy mode the token is the
 // argmax of the previous step, read from the other argmax slot.
 __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
 {
@@ -39,10 +39,16 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
         const int64_t off = (int64_t)token * p.d + i;
         if (p.dtype == DT_F32) {
             p.x[i] = ((const float*)p.emb)[off];
-        } else {
+        } else if (p.dtype == DT_Q8) {
             // codes are stored group-interleaved within the row
             const int8_t c = ((const int8_t*)p.emb)[(int64_t)token * p.d + q8_perm_offset(i, p.d, p.gs)];
             p.x[i] = (float)((double)c * (double)p.emb_s[off / p.gs]);
+        } else {
+            // Q4_0: byte b of a 32-value group holds codes b and b + 16
+            const int64_t g = off / 32, j = off % 32;
+            const uint8_t b = ((const uint8_t*)p.emb)[g * 16 + j % 16];
+            const int c = (j < 16 ? (b & 15) : (b >> 4)) - 8;
+            p.x[i] = (float)((double)c * (double)p.emb_s[g]);
         }
     }
     if (i == 0) {

@@ -29,6 +29,7 @@ from gpu_util import MODES, decode_and_compare, log, need_gpu, set_mode
 pytestmark = pytest.mark.gpu
 
 TINY_Q8 = synth.Config("tinyq8", 128, 256, 3, 4, 2, 320, 64, 11, (synth.Q8_0,))
+TINY_Q4 = synth.Config("tinyq4", 128, 256, 3, 4, 2, 320, 64, 21, (synth.Q4_0,))
 
 
 def _trajectory(cfg, dtype, n):
@@ -45,10 +46,11 @@ def _trajectory(cfg, dtype, n):
     ("tiny", synth.F32, 256),
     ("15M", synth.F32, 256),
     ("tinyq8", synth.Q8_0, 64),
+    ("tinyq4", synth.Q4_0, 64),
 ])
 def test_decode_small(name, dtype, steps, mode):
     need_gpu()
-    cfg = TINY_Q8 if name == "tinyq8" else synth.CONFIGS[name]
+    cfg = {"tinyq8": TINY_Q8, "tinyq4": TINY_Q4}.get(name) or synth.CONFIGS[name]
     blob, orc, fed = _trajectory(cfg, dtype, steps)
     with l2d.Context(blob, dtype) as ctx:
         set_mode(ctx, mode)
@@ -239,6 +241,21 @@ def test_decode_7b_fp32_full_size():
 
 def test_decode_7b_q8_full_size():
     _full_size("7B", synth.Q8_0, [512, 2048])
+
+
+def test_decode_7b_q4_full_size():
+    _full_size("7B", synth.Q4_0, [512, 2048])
+
+
+def test_decode_110m_q4_trajectory():
+    """110M with 4-bit weights, 512 teacher-forced steps (graph replay)."""
+    need_gpu()
+    cfg = synth.CONFIGS["110M"]
+    blob, orc, fed = _trajectory(cfg, synth.Q4_0, 512)
+    with l2d.Context(blob, synth.Q4_0) as ctx:
+        set_mode(ctx, "graph")
+        st = decode_and_compare(ctx, orc, fed, label="110M Q4_0 graph")
+    st.assert_ok()
 
 
 def test_decode_13b_q8_full_size():
