@@ -1,10 +1,13 @@
-// attn.hip - the standalone attention kernels of the kernel-by-kernel step:
-// grid (n_kv_heads, NS), workgroup (g, c) runs the attention of kv head g
-// over a contiguous range of about (pos+1)/NS positions (rounded up to whole
+// attn.hip - the attention kernel of the kernel-by-kernel step: grid
+// (n_kv_heads, NS), workgroup (g, c) runs the attention of kv head g over a
+// contiguous range of about (pos+1)/NS positions (rounded up to whole
 // sub-chunks; see attn_core.hpp for the computation). One active range: o is
-// written directly. Several: each writes (m, l, acc) and a small merge kernel
-// launched right after combines them, o = sum_c e^{m_c - M} acc_c /
-// sum_c e^{m_c - M} l_c (no atomics or device-scope fences needed).
+// written directly. Several: each range stores its (m, l, acc) with
+// device-scope stores, waits for them to complete and counts itself done on
+// its kv head's counter; the range that completes the count merges all of
+// them, o = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c, reading them with
+// device-scope loads, and resets the counter. No fence or cache write-back
+// is needed, and no second kernel.
 // Workgroups beyond the active ranges exit at once: the grid is sized once,
 // pos is read from device memory, and the same launch serves every position
 // of a captured graph.
@@ -64,77 +67,74 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
                 (float)(attn_value<kAThreads>(smem, G, hs, e) / attn_l<kAThreads>(smem, G, hs, e / hs));
         return;
     }
-    // Several ranges: write (acc, m, l); the merge kernel that follows in
-    // the stream combines them (the kernel boundary orders the stores)
+    // Several ranges: store (acc, m, l) at the device coherence point, then
+    // count this range done; the last one merges
     const size_t pbase = ((size_t)g * NS + split) * G;
-    for (int e = tid; e < G * hs; e += kAThreads) p.part_o[pbase * hs + e] = attn_value<kAThreads>(smem, G, hs, e);
+    for (int e = tid; e < G * hs; e += kAThreads) st_dev(p.part_o + pbase * hs + e, attn_value<kAThreads>(smem, G, hs, e));
     if (tid < G) {
-        p.part_ml[(pbase + tid) * 2 + 0] = attn_m<kAThreads>(smem, G, hs, tid);
-        p.part_ml[(pbase + tid) * 2 + 1] = attn_l<kAThreads>(smem, G, hs, tid);
+        st_dev(p.part_ml + (pbase + tid) * 2, attn_m<kAThreads>(smem, G, hs, tid));
+        st_dev(p.part_ml + (pbase + tid) * 2 + 1, attn_l<kAThreads>(smem, G, hs, tid));
     }
-}
-
-// Merge of the split results, o = sum_c e^{m_c - M} acc_c / sum_c e^{m_c - M} l_c
-// with M = max_c m_c, in fp64. Four adjacent lanes share an output element
-// and take every fourth split; their partial maxima and sums combine by DPP
-// in a fixed order. Does nothing when one split covered all positions (the
-// attention kernel then wrote o itself).
-__global__ __launch_bounds__(256) void attention_merge_kernel(AttnParams p)
-{
-    const int T = p.step[1] + 1;
-    int nact;
-    attn_split(T, p.nsplit, attn_shape<kAThreads>(p.hs).sc, &nact);
-    if (nact == 1) return;
-    const int G = p.G, hs = p.hs;
-    const int64_t n_out = (int64_t)p.nkv * G * hs;
-    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2;
-    const int sub = threadIdx.x & 3;
-    const int64_t ec = e < n_out ? e : n_out - 1;  // clamped: all lanes join the DPP sums
-    const int64_t g = ec / (G * hs);
-    const int64_t within = ec % (G * hs);
-    const int64_t h = within / hs;
-    const size_t base = (size_t)g * p.nsplit;
-    // this lane's splits c = sub + 4k (k < 16, NS <= 64), loads issued together
-    constexpr int KMAX = 16;
-    double m[KMAX], l[KMAX], o[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; k++) {
-        const int c = min(sub + 4 * k, nact - 1);
-        m[k] = p.part_ml[((base + c) * G + h) * 2];
-        l[k] = p.part_ml[((base + c) * G + h) * 2 + 1];
-        o[k] = p.part_o[((base + c) * G) * hs + within];
+    wait_vm_all();
+    __syncthreads();
+    __shared__ int last;
+    if (tid == 0) {
+        uint32_t* ctr = p.ctr + (size_t)g * 32;
+        const uint32_t done = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = done + 1 == (uint32_t)nact;
+        if (last) st_dev(ctr, 0u);  // the next use is a later launch
     }
-    double M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < KMAX; k++)
-        if (sub + 4 * k < nact) M = fmax(M, m[k]);
-    M = fmax(M, __hiloint2double(dpp_xor1(__double2hiint(M)), dpp_xor1(__double2loint(M))));
-    M = fmax(M, __hiloint2double(dpp_xor2(__double2hiint(M)), dpp_xor2(__double2loint(M))));
-    double O = 0.0, L = 0.0;
-#pragma unroll
-    for (int k = 0; k < KMAX; k++) {
-        if (sub + 4 * k < nact) {
-            const double w = exp(m[k] - M);
-            L += w * l[k];
-            O += w * o[k];
-        }
+    __syncthreads();
+    if (!last) return;
+    // Merge of kv head g's ranges, in fp64. First the weight of every (head,
+    // range), w_c = e^{m_c - M} with M the head's maximum, and the head's
+    // sum_c w_c l_c: one wavefront per head, a lane per range, fixed-order
+    // wave reductions. Then each output element: four adjacent lanes take
+    // every fourth range (all their loads issued together) and combine by
+    // DPP in a fixed order. Every lane of a wave joins the DPP steps.
+    __shared__ double wsh[kMaxG][64];
+    __shared__ double lsh[kMaxG];
+    const size_t base = (size_t)g * NS;
+    for (int t = tid; t < G * 64; t += kAThreads) {
+        const int h = t / 64, c = t % 64;
+        const bool ok = c < nact;
+        const double mc = ok ? ld_dev(p.part_ml + ((base + c) * G + h) * 2) : -INFINITY;
+        const double lc = ok ? ld_dev(p.part_ml + ((base + c) * G + h) * 2 + 1) : 0.0;
+        const double M = wave_max(mc);
+        const double w = ok ? exp(mc - M) : 0.0;
+        const double Ls = wave_sum(w * lc);
+        wsh[h][c] = w;
+        if ((t & 63) == 0) lsh[h] = Ls;
     }
-    O += __hiloint2double(dpp_xor1(__double2hiint(O)), dpp_xor1(__double2loint(O)));
-    O += __hiloint2double(dpp_xor2(__double2hiint(O)), dpp_xor2(__double2loint(O)));
-    L += __hiloint2double(dpp_xor1(__double2hiint(L)), dpp_xor1(__double2loint(L)));
-    L += __hiloint2double(dpp_xor2(__double2hiint(L)), dpp_xor2(__double2loint(L)));
-    if (sub == 0 && e < n_out) p.o[e] = (float)(O / L);
+    __syncthreads();
+    const int sub = tid & 3;
+    constexpr int KMAX = 16;  // ranges per lane: NS <= 64
+    for (int e0 = 0; e0 < G * hs; e0 += kAThreads / 4) {
+        const int e = e0 + (tid >> 2);
+        const int ec = e < G * hs ? e : G * hs - 1;
+        const int h = ec / hs;
+        double o[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; k++) o[k] = ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec);
+        double O = 0.0;
+#pragma unroll
+        for (int k = 0; k < KMAX; k++)
+            if (sub + 4 * k < nact) O += wsh[h][sub + 4 * k] * o[k];
+        O += __hiloint2double(dpp_xor1(__double2hiint(O)), dpp_xor1(__double2loint(O)));
+        O += __hiloint2double(dpp_xor2(__double2hiint(O)), dpp_xor2(__double2loint(O)));
+        if (sub == 0 && e < G * hs) p.o[(size_t)g * G * hs + e] = (float)(O / lsh[h]);
+    }
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
+    if (p.nsplit > 64) return hipErrorInvalidValue;  // the merge takes at most 64 ranges
     const size_t lds = attention_lds_bytes(p.G, p.hs, 0);
     const dim3 grid(p.nkv, p.nsplit);
-    hipEvent_t e0 = ev ? ev->start : nullptr;
 #define L2D_ATT(GG)                                                                                \
     if (ev)                                                                                        \
-        hipExtLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), (uint32_t)lds, s, e0,   \
-                              nullptr, 0u, p);                                                     \
+        hipExtLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), (uint32_t)lds, s,       \
+                              ev->start, ev->stop, 0u, p);                                         \
     else                                                                                           \
         hipLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), lds, s, p);
     switch (p.G) {
@@ -145,14 +145,6 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEven
     default: return hipErrorInvalidValue;
     }
 #undef L2D_ATT
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t threads = (int64_t)p.nkv * p.G * p.hs * 4;
-    const dim3 mgrid((unsigned)((threads + 255) / 256));
-    if (ev)
-        hipExtLaunchKernelGGL(attention_merge_kernel, mgrid, dim3(256), 0u, s, nullptr, ev->stop, 0u, p);
-    else
-        hipLaunchKernelGGL(attention_merge_kernel, mgrid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

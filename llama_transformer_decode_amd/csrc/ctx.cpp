@@ -260,6 +260,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         a.o = ctx->o;
         a.part_o = ctx->part_o;
         a.part_ml = ctx->part_ml;
+        a.ctr = ctx->attn_ctr;
         a.step = ctx->step;
         a.S = (int32_t)ctx->S;
         a.nkv = (int32_t)ctx->nkv;
@@ -421,6 +422,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     const size_t nparts = (size_t)ctx->nkv * ctx->nsplit * ctx->G;
     ALLOC(ctx->part_o, nparts * ctx->hs * 8);
     ALLOC(ctx->part_ml, nparts * 2 * 8);
+    ALLOC(ctx->attn_ctr, (size_t)ctx->nkv * 32 * 4);
     for (int i = 0; i < 4; i++) {
         const int64_t n = i == 3 ? h : d;
         ALLOC(ctx->trace_q[i], (size_t)n);
@@ -527,6 +529,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, (size_t)kArgmaxWords * 8, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     rc = capture(ctx);
@@ -801,6 +804,7 @@ int l2d_reset_kv(l2d_ctx* ctx)
     const size_t kvbytes = (size_t)(ctx->L * ctx->S * ctx->kvd) * 4;
     HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
     ctx->last_pos = -1;
     return L2D_OK;
 }

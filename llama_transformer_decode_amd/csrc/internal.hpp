@@ -81,6 +81,7 @@ struct AttnParams {
     float* o;          // [n_heads * hs]
     double* part_o;    // [nkv][nsplit][G][hs]
     double* part_ml;   // [nkv][nsplit][G][2]
+    uint32_t* ctr;     // [nkv][32]: ranges of each kv head done this launch (zero between launches)
     const int32_t* step;
     int32_t S, nkv, hs, kvd, G, nsplit;
 };

@@ -61,6 +61,7 @@ struct l2d_ctx {
     unsigned long long* argmax = nullptr;  // [2][kArgmaxSlots][kArgmaxStride]
     double* part_o = nullptr;
     double* part_ml = nullptr;
+    uint32_t* attn_ctr = nullptr;  // [nkv][32] ranges done per kv head (attention merge)
     int nsplit = 0;
 
     hipGraph_t graph = nullptr;
