@@ -218,3 +218,27 @@ def test_gemv_q40_rejects_bad_shapes():
         l2d.gemv(l2d.Q4_0, W, S, x, 2, 48, 32)  # 32 does not divide cols
     with pytest.raises(l2d.L2DError):
         l2d.gemv(l2d.Q4_0, W, None, x, 2, 64, 32)  # no scales
+
+
+def test_gemv_profile_matches_gemv():
+    """The timed entry point runs the same kernel: same output as l2d_gemv on
+    the last copy, a positive mean duration; Q8_0 is refused (its codes need
+    the device layout)."""
+    torch = need_gpu()
+    rows, cols = 512, 4096
+    rng = np.random.default_rng(9)
+    Ws, Ss = [], []
+    for _ in range(3):
+        Q, S = _q40_weights(rows, cols, rng)
+        Ws.append(torch.from_numpy(Q).cuda())
+        Ss.append(torch.from_numpy(S).cuda())
+    x = torch.from_numpy(synth.normal_f32(1, 9, cols, 1.0)).cuda()
+    sec, out = l2d.gemv_profile(l2d.Q4_0, Ws, Ss, x, rows, cols, 32, reps=5)  # last launch uses copy 1
+    ref = l2d.gemv(l2d.Q4_0, Ws[1], Ss[1], x, rows, cols, 32)
+    np.testing.assert_array_equal(out.cpu().numpy(), ref.cpu().numpy())
+    assert 0 < sec < 1e-2
+    Wf = [torch.from_numpy(synth.normal_f32(2, 10, rows * cols, 0.02)).cuda()]
+    sec, out = l2d.gemv_profile(l2d.F32, Wf, None, x, rows, cols, 1, reps=2)
+    np.testing.assert_array_equal(out.cpu().numpy(), l2d.gemv(l2d.F32, Wf[0], None, x, rows, cols).cpu().numpy())
+    with pytest.raises(l2d.L2DError):
+        l2d.gemv_profile(l2d.Q8_0, Wf, Ss[:1], x, rows, cols, 64, reps=1)

@@ -96,3 +96,59 @@ def test_zero_temperature_is_greedy_and_bad_temperature_rejected():
         for bad in (-1.0, float("nan"), float("inf")):
             with pytest.raises(l2d.L2DError):
                 ctx.set_sampling(bad, 1)
+
+
+@pytest.mark.parametrize("dtype", [synth.Q8_0, synth.F32])
+def test_sampled_chain_after_batched_prefill(dtype):
+    """A 40-token prompt through the batched prefill with sampling on, then
+    the device's own sampled continuation: equals the host loop feeding the
+    prompt and then the oracle's draws (the prefill's last step draws the
+    first generated token exactly as a single-token step would)."""
+    need_gpu()
+    cfg = synth.CONFIGS["110M"]
+    blob = synth.make_blob(cfg, dtype)
+    orc = oracle.Model(blob, dtype)
+    prompt = synth.prompt(31, 40, cfg.vocab)
+    n = 24
+    want = []
+    for p, t in enumerate(prompt):
+        r = orc.forward(int(t), p)
+    tok = oracle.sample(r, T, SEED, len(prompt) - 1)
+    want.append(tok)
+    for p in range(len(prompt), len(prompt) + n - 1):
+        r = orc.forward(tok, p)
+        tok = oracle.sample(r, T, SEED, p)
+        want.append(tok)
+    orc.close()
+    with l2d.Context(blob, dtype) as ctx:
+        ctx.set_sampling(T, SEED)
+        ctx.prefill(prompt, 0)
+        got = [ctx.last_token()]
+        for p in range(len(prompt), len(prompt) + n - 1):
+            ctx.forward_greedy(p)
+            got.append(ctx.last_token())
+    np.testing.assert_array_equal(np.array(got), np.array(want))
+
+
+def test_q4_0_sampled_chain_equals_host_loop():
+    """Sampling on top of the 4-bit decode step (110M, Q4_0)."""
+    need_gpu()
+    cfg = synth.CONFIGS["110M"]
+    blob = synth.make_blob(cfg, synth.Q4_0)
+    orc = oracle.Model(blob, synth.Q4_0)
+    n = 64
+    want = []
+    tok = 1
+    for p in range(n):
+        r = orc.forward(tok, p)
+        tok = oracle.sample(r, T, SEED, p)
+        want.append(tok)
+    orc.close()
+    with l2d.Context(blob, synth.Q4_0) as ctx:
+        ctx.set_sampling(T, SEED)
+        ctx.forward(1, 0)
+        got = [ctx.last_token()]
+        for p in range(1, n):
+            ctx.forward_greedy(p)
+            got.append(ctx.last_token())
+    np.testing.assert_array_equal(np.array(got), np.array(want))
