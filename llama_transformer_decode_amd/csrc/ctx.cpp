@@ -409,12 +409,14 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ALLOC(ctx->logits, (size_t)V * 4);
     ALLOC(ctx->step, 64);
     ALLOC(ctx->argmax, (size_t)kArgmaxWords * 8);
-    // attention position splits: about 2048 workgroups over the kv heads at
-    // full context (splits of at least one sub-chunk; the grid is sized
-    // once, inactive splits exit), at most 64 splits to merge per head
+    // attention position splits: at most about three workgroups per CU over
+    // the kv heads (fewer, longer ranges beat more, shorter ones once that
+    // fills the chip: measured from pos 128 to 4095 at the 7B and 13B
+    // shapes), splits of at least one sub-chunk (the grid is sized once,
+    // inactive splits exit), at most 64 splits to merge per head
     {
         const int64_t sc = attention_positions_per_subchunk((int)ctx->hs);
-        int64_t ns = 2048 / ctx->nkv;
+        int64_t ns = ((int64_t)3 * cus + ctx->nkv / 2) / ctx->nkv;
         if (ns > 64) ns = 64;
         if (ns > (ctx->S + sc - 1) / sc) ns = (ctx->S + sc - 1) / sc;
         ctx->nsplit = (int)(ns < 1 ? 1 : ns);
