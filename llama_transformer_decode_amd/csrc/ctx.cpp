@@ -294,8 +294,18 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.out = ctx->hb;
         p.trace_q = tr ? ctx->trace_q[2] : nullptr;
         p.trace_s = tr ? ctx->trace_s[2] : nullptr;
+        // quantised weights: hb is quantised once, group by group, as the
+        // w1/w3 matvec completes it, and the w2 matvec takes the codes
+        const bool hbq = dt != DT_F32;
+        p.oq = hbq ? ctx->hb_q : nullptr;
+        p.os = hbq ? ctx->hb_s : nullptr;
+        p.octr = hbq ? ctx->hb_ctr : nullptr;
+        p.ogs = (int32_t)gs;
         if (kt) HIP_TRY(ctx, kt->next(KC_W13));
         HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        p.oq = nullptr;
+        p.os = nullptr;
+        p.octr = nullptr;
 
         // w2 matvec + residual
         p.W = (const uint8_t*)ctx->w2 + mat_bytes(dt, l * d * h);
@@ -303,12 +313,17 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.M = d;
         p.K = h;
         p.x = ctx->hb;
+        p.xq = hbq ? ctx->hb_q : nullptr;
+        p.xs = hbq ? ctx->hb_s : nullptr;
         p.gain = nullptr;
         p.out = ctx->x;
         p.trace_q = tr ? ctx->trace_q[3] : nullptr;
         p.trace_s = tr ? ctx->trace_s[3] : nullptr;
         if (kt) HIP_TRY(ctx, kt->next(KC_W2));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        HIP_TRY(ctx, launch_gemv(ctx->dt, hbq ? PRO_CODES : PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s,
+                                 kt ? &kt->cur : nullptr));
+        p.xq = nullptr;
+        p.xs = nullptr;
     }
     return enqueue_classifier(ctx, kt, KC_CLS);
 }
@@ -406,6 +421,9 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ALLOC(ctx->q, (size_t)d * 4);
     ALLOC(ctx->o, (size_t)d * 4);
     ALLOC(ctx->hb, (size_t)h * 4);
+    ALLOC(ctx->hb_q, (size_t)h);
+    ALLOC(ctx->hb_s, (size_t)(h / gs + 1) * 4);
+    ALLOC(ctx->hb_ctr, (size_t)(h / gs + 1) * kGroupCtrStride * 4);
     ALLOC(ctx->logits, (size_t)V * 4);
     ALLOC(ctx->step, 64);
     ALLOC(ctx->argmax, (size_t)kArgmaxWords * 8);
@@ -532,6 +550,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, (size_t)kArgmaxWords * 8, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->hb_ctr, 0, (size_t)(ctx->h / ctx->gs + 1) * kGroupCtrStride * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     rc = capture(ctx);
@@ -807,6 +826,7 @@ int l2d_reset_kv(l2d_ctx* ctx)
     HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->hb_ctr, 0, (size_t)(ctx->h / ctx->gs + 1) * kGroupCtrStride * 4, ctx->stream));
     ctx->last_pos = -1;
     return L2D_OK;
 }

@@ -290,6 +290,63 @@ __device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_o
     return i32x4{w[0], w[1], w[2], w[3]};
 }
 
+// Q8_0 quantisation of a vector y that many waves produce, each wave a
+// contiguous range, done once per group instead of by every consumer.
+
+// One wave quantises group y[0, gs) (values read with device-scope loads):
+// lane l takes elements l, l + 64, ...; codes to q[0, gs), the scale to *s.
+__device__ __forceinline__ void quantize_group_wave(const float* y, int gs, int8_t* q, float* s, int lane)
+{
+    constexpr int kMaxPer = 4;  // gs <= 256
+    float v[kMaxPer];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxPer; k++) {
+        const int i = lane + k * kWave;
+        v[k] = i < gs ? ld_dev(y + i) : 0.0f;
+        m = fmaxf(m, fabsf(v[k]));
+    }
+    m = wave_maxf(m);
+    const float sc = q80_scale(m);
+#pragma unroll
+    for (int k = 0; k < kMaxPer; k++) {
+        const int i = lane + k * kWave;
+        if (i < gs) q[i] = (int8_t)q80_code(v[k], sc);
+    }
+    if (lane == 0) *s = sc;
+}
+
+// Called by a whole wave after it has stored y[lo, hi) with device-scope
+// stores. For every group of gs values it touched, it adds its count of
+// elements to the group's counter (relaxed, device scope, after waiting for
+// its stores to complete); the wave that brings a count to gs reads the
+// group back, quantises it into q/s and resets the counter for the next
+// use. A range holding a whole group quantises it without counting.
+// Counter g sits at ctr[g * ctr_stride].
+__device__ __forceinline__ void quantize_completed_groups(const float* y, int64_t lo, int64_t hi, int gs,
+                                                          int8_t* q, float* s, uint32_t* ctr,
+                                                          int ctr_stride, int lane)
+{
+    if (lo >= hi) return;
+    wait_vm_all();
+    for (int64_t g = lo / gs; g * gs < hi; g++) {
+        const int64_t a = lo > g * gs ? lo : g * gs;
+        const int64_t b = hi < (g + 1) * gs ? hi : (g + 1) * gs;
+        const uint32_t cnt = (uint32_t)(b - a);
+        bool last = cnt == (uint32_t)gs;
+        if (!last) {
+            uint32_t old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(ctr + g * ctr_stride, cnt, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            old = __shfl(old, 0, kWave);
+            last = old + cnt == (uint32_t)gs;
+            if (last && lane == 0) st_dev(ctr + g * ctr_stride, 0u);
+        }
+        if (last) quantize_group_wave(y + g * gs, gs, q + g * gs, s + g, lane);
+    }
+}
+
 }  // namespace l2d
 
 namespace l2d {

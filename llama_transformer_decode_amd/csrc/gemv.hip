@@ -72,9 +72,26 @@ __device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; 
 __device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // fp32 input: thread t holds float4 chunks t, t+256, ... (NC of them)
+// An empty asm that claims to redefine v: no use of v can be scheduled
+// before this point (the loads themselves are not moved).
+template <class T>
+__device__ __forceinline__ void hold(T& v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 template <int PRO, int NC>
 struct InputF32 {
     f32x4 x[NC], g[NC];
+
+    __device__ __forceinline__ void fence()
+    {
+#pragma unroll
+        for (int j = 0; j < NC; j++) {
+            hold(x[j]);
+            if (PRO == PRO_NORM) hold(g[j]);
+        }
+    }
 
     __device__ __forceinline__ void issue(const GemvParams& p)
     {
@@ -144,6 +161,18 @@ __device__ __forceinline__ int64_t input_chunk_slot(int64_t c, int64_t K, int gs
     return (c & 1) * (K / 32) + (c >> 1);
 }
 
+// Workgroup 0 copies the quantised input it holds in LDS to the trace
+// buffers, back in plain element order (test hook).
+template <int DT>
+__device__ __forceinline__ void trace_input(const GemvParams& p, const unsigned char* smem)
+{
+    if (p.trace_q == nullptr || blockIdx.x != 0) return;
+    for (int64_t c = threadIdx.x; c < p.K / 16; c += kThreads)
+        ((i32x4*)p.trace_q)[c] = ((const i32x4*)smem)[input_chunk_slot<DT>(c, p.K, p.gs)];
+    for (int64_t g = threadIdx.x; g < p.K / p.gs; g += kThreads)
+        p.trace_s[g] = ((const float*)(smem + p.K))[g];
+}
+
 // Quantised input (Q8_0 codes of x for the Q8_0 and Q4_0 matvecs): thread t
 // holds 16-value chunks t, t+256, ... (NC of them); lanes of one group
 // (lpg = gs/16) are adjacent. Codes go to LDS at input_chunk_slot, scales in
@@ -154,6 +183,18 @@ template <int DT, int PRO, int NC>
 struct InputQ8 {
     static constexpr int N = NC > 0 ? NC : 1;
     f32x4 x[N][4], g[N][4];
+
+    __device__ __forceinline__ void fence()
+    {
+        if (NC == 0) return;
+#pragma unroll
+        for (int j = 0; j < N; j++)
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                hold(x[j][k]);
+                if (PRO == PRO_NORM) hold(g[j][k]);
+            }
+    }
 
     __device__ __forceinline__ void issue(const GemvParams& p)
     {
@@ -241,13 +282,86 @@ struct InputQ8 {
             }
         }
         __syncthreads();
-        if (p.trace_q != nullptr && blockIdx.x == 0) {
-            // back to plain element order for the trace
-            for (int64_t c = threadIdx.x; c < nq; c += kThreads)
-                ((i32x4*)p.trace_q)[c] = ((const i32x4*)smem)[input_chunk_slot<DT>(c, p.K, p.gs)];
-            for (int64_t g = threadIdx.x; g < p.K / p.gs; g += kThreads)
-                p.trace_s[g] = ((const float*)(smem + p.K))[g];
+        trace_input<DT>(p, smem);
+    }
+};
+
+// Already quantised input (PRO_CODES: Q8_0 codes and scales of x, written by
+// the producing kernel): the same LDS image as InputQ8 builds, without the
+// per-workgroup quantisation. Thread t holds 16-code chunks t, t+256, ...
+template <int DT, int NC>
+struct InputCodes {
+    static constexpr int N = NC > 0 ? NC : 1;
+    i32x4 c[N];
+    float sc[N];
+
+    __device__ __forceinline__ void fence()
+    {
+        if (NC == 0) return;
+#pragma unroll
+        for (int j = 0; j < N; j++) {
+            hold(c[j]);
+            hold(sc[j]);
         }
+    }
+
+    __device__ __forceinline__ void issue(const GemvParams& p)
+    {
+        if (NC == 0) return;
+        const int64_t nq = p.K / 16;
+        const int lpg = p.gs / 16;
+#pragma unroll
+        for (int j = 0; j < N; j++) {
+            const int64_t k = imin((int64_t)j * kThreads + threadIdx.x, nq - 1);
+            c[j] = *(const i32x4*)(p.xq + 16 * k);
+            sc[j] = p.xs[k / lpg];
+        }
+    }
+
+    __device__ __forceinline__ void put(const GemvParams& p, unsigned char* smem, int64_t k, i32x4 codes,
+                                        float scale, int lpg)
+    {
+        int csum = 0;
+        if (DT == DT_Q4) csum = lanes_sum_i32(dot16_i8(codes, i32x4{0x01010101, 0x01010101, 0x01010101,
+                                                                 0x01010101}), lpg);
+        if (k < p.K / 16) {
+            ((i32x4*)smem)[input_chunk_slot<DT>(k, p.K, p.gs)] = codes;
+            if ((k & (lpg - 1)) == 0) {
+                ((float*)(smem + p.K))[k / lpg] = scale;
+                if (DT == DT_Q4) ((int*)(smem + p.K))[p.K / p.gs + k / lpg] = -8 * csum;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void finish(const GemvParams& p, unsigned char* smem, double*)
+    {
+        const int64_t nq = p.K / 16;
+        const int lpg = p.gs / 16;
+        if (NC > 0) {
+#pragma unroll
+            for (int j = 0; j < N; j++) {
+                if ((int64_t)j * kThreads >= nq) break;  // uniform
+                put(p, smem, (int64_t)j * kThreads + threadIdx.x, c[j], sc[j], lpg);
+            }
+        } else {
+            for (int64_t base = 0; base < nq; base += 4 * kThreads) {
+                i32x4 a[4];
+                float b[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int64_t k = imin(base + (int64_t)j * kThreads + threadIdx.x, nq - 1);
+                    a[j] = *(const i32x4*)(p.xq + 16 * k);
+                    b[j] = p.xs[k / lpg];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    if (base + (int64_t)j * kThreads >= nq) break;  // uniform
+                    put(p, smem, base + (int64_t)j * kThreads + threadIdx.x, a[j], b[j], lpg);
+                }
+            }
+        }
+        __syncthreads();
+        trace_input<DT>(p, smem);
     }
 };
 
@@ -301,7 +415,8 @@ __device__ __forceinline__ void gemv_epilogue(const GemvParams& p, int64_t row0,
                 const double z = (double)(float)acc[r];
                 const double h3 = (double)(float)acc[r + 1];
                 const double silu = z / (1.0 + exp(-z));
-                p.out[row / 2] = (float)(silu * h3);
+                // device scope: the wave completing a group reads it back
+                st_dev(p.out + row / 2, (float)(silu * h3));
             }
         }
     } else if (EPI == EPI_QKV) {
@@ -525,8 +640,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     }
 
     // 1. input loads
-    typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<DT, PRO, NC>>::type in;
+    typename std::conditional<PRO == PRO_CODES, InputCodes<DT, NC>,
+        typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<DT, PRO, NC>>::type>::type in;
     in.issue(p);
+    // the RoPE frequency of this thread's pair (q/k/v epilogue)
+    float freq = 0.0f;
+    if (EPI == EPI_QKV && (int)threadIdx.x < p.hs / 2) freq = p.freqs[threadIdx.x];
+    // keep every input load ahead of the weight prefetch: the prologue then
+    // waits only for its own loads, not for the weights in flight behind them
+    __builtin_amdgcn_sched_barrier(0);
 
     // 2. the first NBUF chunks (dummy loads for a wave with fewer chunks)
     Chunk<DT, RPW, U> buf[NBUF];
@@ -540,13 +662,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     };
 #pragma unroll
     for (int k = 0; k < NBUF; k++) load_next(buf[k]);
+    __builtin_amdgcn_sched_barrier(0);
+    in.fence();
+    hold(freq);
 
     // 3. prologue. RoPE table of this pos first: fp32 cosine / sine of the
     //    fp32 angle pos*freq_j, correctly rounded (fp64 value rounded once)
     float* rcos = (float*)(smem + gemv_input_bytes(DT, p.K, p.gs));
     float* rsin = rcos + p.hs / 2;
     if (EPI == EPI_QKV && (int)threadIdx.x < p.hs / 2) {
-        const float ang = (float)pos * p.freqs[threadIdx.x];
+        const float ang = (float)pos * freq;
         rcos[threadIdx.x] = (float)cos((double)ang);
         rsin[threadIdx.x] = (float)sin((double)ang);
     }
@@ -589,6 +714,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
                 ++tile;
             }
         }
+    }
+    if (EPI == EPI_SWIGLU && p.oq != nullptr) {
+        // this wave stored outputs [rows / 2) of its tile range
+        const int64_t r_lo = t_beg * RPW, r_hi = imin(t_end * RPW, p.M);
+        quantize_completed_groups(p.out, r_lo / 2, r_hi / 2, p.ogs, p.oq, p.os, p.octr, kGroupCtrStride, lane);
     }
     if (EPI == EPI_LOGITS) {
         // workgroup maximum, then one atomic into a slot chosen by workgroup
@@ -644,7 +774,7 @@ static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s, 
         if (per_thread <= 16) return launch_t<DT, PRO, EPI, RPW, U, 16, DBG>(p, b, s, ev);
         return hipErrorInvalidValue;
     } else {
-        if (PRO == PRO_PLAIN) return launch_t<DT, PRO, EPI, RPW, U, 0, DBG>(p, b, s, ev);
+        if (PRO != PRO_NORM) return launch_t<DT, PRO, EPI, RPW, U, 0, DBG>(p, b, s, ev);
         return hipErrorInvalidValue;  // RMSNorm inputs longer than 16384
     }
 }
@@ -701,11 +831,13 @@ hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_bl
     L2D_CASE(DT_F32, PRO_PLAIN, EPI_STORE)
     L2D_CASE(DT_Q8, PRO_NORM, EPI_QKV)
     L2D_CASE(DT_Q8, PRO_PLAIN, EPI_RESID)
+    L2D_CASE(DT_Q8, PRO_CODES, EPI_RESID)
     L2D_CASE(DT_Q8, PRO_NORM, EPI_SWIGLU)
     L2D_CASE(DT_Q8, PRO_NORM, EPI_LOGITS)
     L2D_CASE(DT_Q8, PRO_PLAIN, EPI_STORE)
     L2D_CASE(DT_Q4, PRO_NORM, EPI_QKV)
     L2D_CASE(DT_Q4, PRO_PLAIN, EPI_RESID)
+    L2D_CASE(DT_Q4, PRO_CODES, EPI_RESID)
     L2D_CASE(DT_Q4, PRO_NORM, EPI_SWIGLU)
     L2D_CASE(DT_Q4, PRO_NORM, EPI_LOGITS)
     L2D_CASE(DT_Q4, PRO_PLAIN, EPI_STORE)

@@ -24,9 +24,13 @@ constexpr int kArgmaxSlots = 64;
 constexpr int kArgmaxStride = 16;  // u64 per slot
 constexpr int kArgmaxWords = 2 * kArgmaxSlots * kArgmaxStride;
 
+// spacing of per-group completion counters (uint32): one 64-byte line each
+constexpr int kGroupCtrStride = 16;
+
 // GEMV input-vector preparation (the "prologue", run by every workgroup into
-// its LDS): PRO_PLAIN takes x as is; PRO_NORM applies RMSNorm with gain.
-enum Pro { PRO_PLAIN = 0, PRO_NORM = 1 };
+// its LDS): PRO_PLAIN takes x as is; PRO_NORM applies RMSNorm with gain;
+// PRO_CODES takes x already quantised to Q8_0 (codes xq, scales xs).
+enum Pro { PRO_PLAIN = 0, PRO_NORM = 1, PRO_CODES = 2 };
 
 // What happens to each finished output row (the "epilogue").
 enum Epi {
@@ -44,6 +48,8 @@ struct GemvParams {
     int32_t gs;
     const float* x;     // input vector [K], fp32
     const float* gain;  // RMSNorm gain [K] (PRO_NORM)
+    const int8_t* xq;   // PRO_CODES: Q8_0 codes of the input [K], plain order
+    const float* xs;    //            and its group scales [K/gs]
     double eps;
     float* out;
     // EPI_QKV
@@ -54,6 +60,14 @@ struct GemvParams {
     const int32_t* step;  // device step record (kStep*)
     // EPI_LOGITS
     unsigned long long* argmax;  // [2][kArgmaxSlots][kArgmaxStride], parity pos & 1
+    // EPI_SWIGLU: when oq is set, the output is also quantised to Q8_0 with
+    // groups of ogs (codes oq [M/2], scales os [M/2/ogs]) for the next matvec,
+    // each group once, by the wave that completes it (counters octr, zero
+    // between launches, kGroupCtrStride apart)
+    int8_t* oq;
+    float* os;
+    uint32_t* octr;
+    int32_t ogs;
     // diagnostics
     int32_t* group_dots;  // [M][K/gs] exact int32 group dots (Q8_0, Q4_0; test hook)
     int8_t* trace_q;      // workgroup 0 copies its quantised input here

@@ -56,6 +56,9 @@ struct l2d_ctx {
     float* q = nullptr;       // [d]
     float* o = nullptr;       // attention output [d]
     float* hb = nullptr;      // [h]
+    int8_t* hb_q = nullptr;   // Q8_0 / Q4_0 models: codes of hb [h], its scales [h/gs],
+    float* hb_s = nullptr;    // written by the w1/w3 matvec for the w2 matvec
+    uint32_t* hb_ctr = nullptr;  // [h/gs][kGroupCtrStride] group completion counters
     float* logits = nullptr;  // [V]
     int32_t* step = nullptr;  // {token, pos}
     unsigned long long* argmax = nullptr;  // [2][kArgmaxSlots][kArgmaxStride]
