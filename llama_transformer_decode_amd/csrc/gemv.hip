@@ -12,10 +12,14 @@
 //   3. prologue: the input vector is prepared in LDS while those loads are in
 //      flight: x as is, or RMSNorm(x) (pomoai.com hub page, architecture
 //      list), and for Q8_0 the int8 codes and group scales of that vector
-//      (gitcode porting guide, INT8 quantisation section; group max by DPP);
+//      (gitcode porting guide, INT8 quantisation section; group max by DPP),
+//      or codes and scales the producing kernel already made (PRO_CODES). A
+//      scheduling barrier and register holds keep steps 1 and 2 in this
+//      order, so the prologue waits for its own loads only;
 //   4. main loop over a contiguous, balanced range of row tiles (RPW rows
 //      each), as a ring of NBUF chunk buffers: consume a chunk, refill its
-//      buffer with the chunk NBUF ahead. Every load is unconditional (indices
+//      buffer with the chunk NBUF ahead, then (at a tile's end) reduce and
+//      run the epilogue. Every load is unconditional (indices
 //      past the end are clamped onto valid memory and their contribution is
 //      masked), so each iteration issues the same loads and the compiler's
 //      wait counts stay exact: NBUF-1 chunks remain in flight while one is
@@ -689,11 +693,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
         for (int k = 0; k < NBUF; k++) {
             const bool valid = it + k < iters;
             use_chunk<DT, RPW, U, DBG>(buf[k], acc, p, smem, tile * RPW, ch, lane, valid);
+            // refill the buffer as soon as its data is consumed: the tile's
+            // reduction and epilogue then run with NBUF chunks in flight
+            float res[RPW];
+#pragma unroll
+            for (int r = 0; r < RPW; r++) res[r] = EPI == EPI_RESID ? buf[k].res[r] : 0.0f;
+            load_next(buf[k]);
             if (valid && ch == nch - 1) {
 #pragma unroll
                 for (int r = 0; r < RPW; r++) acc[r] = wave_sum_to_last(acc[r]);
                 if (lane == kWave - 1) {
-                    const EpiIn ein{pos, buf[k].res, rcos, rsin, temp, seed};
+                    const EpiIn ein{pos, res, rcos, rsin, temp, seed};
                     if constexpr (PAIR1) {
                         if ((tile & 1) == 0) {
                             pend = acc[0];
@@ -708,7 +718,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 #pragma unroll
                 for (int r = 0; r < RPW; r++) acc[r] = 0.0;
             }
-            load_next(buf[k]);
             if (++ch == nch) {
                 ch = 0;
                 ++tile;
