@@ -95,6 +95,20 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     __shared__ double wsh[kMaxG][64];
     __shared__ double lsh[kMaxG];
     const size_t base = (size_t)g * NS;
+    const int sub = tid & 3;
+    constexpr int KMAX = 16;  // ranges per lane: NS <= 64
+    const int kk = (nact + 3) / 4;  // ranges this lane's loads actually need
+    // the partial values of the first two passes go out together with the
+    // (m, l) loads below: the merge then costs one round trip, not two
+    constexpr int PRE = 2;
+    double pre[PRE][KMAX];
+#pragma unroll
+    for (int ps = 0; ps < PRE; ps++) {
+        const int ec = min(ps * (kAThreads / 4) + (tid >> 2), G * hs - 1);
+#pragma unroll
+        for (int k = 0; k < KMAX; k++)
+            pre[ps][k] = k < kk ? ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec) : 0.0;
+    }
     for (int t = tid; t < G * 64; t += kAThreads) {
         const int h = t / 64, c = t % 64;
         const bool ok = c < nact;
@@ -107,15 +121,19 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
         if ((t & 63) == 0) lsh[h] = Ls;
     }
     __syncthreads();
-    const int sub = tid & 3;
-    constexpr int KMAX = 16;  // ranges per lane: NS <= 64
-    for (int e0 = 0; e0 < G * hs; e0 += kAThreads / 4) {
+    for (int e0 = 0, ps = 0; e0 < G * hs; e0 += kAThreads / 4, ps++) {
         const int e = e0 + (tid >> 2);
         const int ec = e < G * hs ? e : G * hs - 1;
         const int h = ec / hs;
         double o[KMAX];
+        if (ps < PRE) {
 #pragma unroll
-        for (int k = 0; k < KMAX; k++) o[k] = ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec);
+            for (int k = 0; k < KMAX; k++) o[k] = ps == 0 ? pre[0][k] : pre[1][k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; k++)
+                o[k] = k < kk ? ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec) : 0.0;
+        }
         double O = 0.0;
 #pragma unroll
         for (int k = 0; k < KMAX; k++)
