@@ -36,9 +36,20 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags. The matvec kernel holds its input vector in arrays
+# of float4 across the weight prefetch; with two or more chunks per thread
+# (hidden sizes above 4096) LLVM's SROA leaves those arrays on the stack.
+# The AMDGPU alloca-to-vector promotion, given a larger budget, moves them
+# back into registers.
+EXTRA = {
+    "gemv.hip": ["-mllvm", "-amdgpu-promote-alloca-to-vector-limit=1024",
+                 "-mllvm", "-amdgpu-promote-alloca-to-vector-max-regs=64"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS
+    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS + EXTRA.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

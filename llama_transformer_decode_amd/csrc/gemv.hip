@@ -144,8 +144,12 @@ struct InputF32 {
     }
 };
 
-__device__ __forceinline__ void unpack16(float* v, const f32x4* a)
+// The four vectors come by value: a pointer into the held input arrays
+// lets the optimiser merge their loads across elements, which pins the
+// arrays to the stack.
+__device__ __forceinline__ void unpack16(float* v, f32x4 a0, f32x4 a1, f32x4 a2, f32x4 a3)
 {
+    const f32x4 a[4] = {a0, a1, a2, a3};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         v[4 * k] = a[k].x;
@@ -186,6 +190,9 @@ __device__ __forceinline__ void trace_input(const GemvParams& p, const unsigned 
 template <int DT, int PRO, int NC>
 struct InputQ8 {
     static constexpr int N = NC > 0 ? NC : 1;
+    // the RMSNorm gain is held across the weight prefetch only for one chunk
+    // per thread; longer inputs load it in the prologue (registers)
+    static constexpr bool kHoldGain = PRO == PRO_NORM && NC == 1;
     f32x4 x[N][4], g[N][4];
 
     __device__ __forceinline__ void fence()
@@ -196,7 +203,7 @@ struct InputQ8 {
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 hold(x[j][k]);
-                if (PRO == PRO_NORM) hold(g[j][k]);
+                if (kHoldGain) hold(g[j][k]);
             }
     }
 
@@ -210,7 +217,7 @@ struct InputQ8 {
 #pragma unroll
             for (int k = 0; k < 4; k++) {
                 x[j][k] = ld4(p.x + 16 * c + 4 * k);
-                if (PRO == PRO_NORM) g[j][k] = ld4(p.gain + 16 * c + 4 * k);
+                if (kHoldGain) g[j][k] = ld4(p.gain + 16 * c + 4 * k);
             }
         }
     }
@@ -237,6 +244,14 @@ struct InputQ8 {
         const int64_t nq = p.K / 16;
         const int lpg = p.gs / 16;
         if (NC > 0) {
+            if (PRO == PRO_NORM && !kHoldGain) {
+#pragma unroll
+                for (int j = 0; j < N; j++) {
+                    const int64_t c = imin((int64_t)j * kThreads + threadIdx.x, nq - 1);
+#pragma unroll
+                    for (int k = 0; k < 4; k++) g[j][k] = ld4(p.gain + 16 * c + 4 * k);
+                }
+            }
             double r = 1.0;
             if (PRO == PRO_NORM) {
                 double ss = 0.0;
@@ -255,16 +270,17 @@ struct InputQ8 {
             }
 #pragma unroll
             for (int j = 0; j < N; j++) {
-                if ((int64_t)j * kThreads >= nq) break;  // uniform
-                float v[16];
-                unpack16(v, x[j]);
-                if (PRO == PRO_NORM) {
-                    float gg[16];
-                    unpack16(gg, g[j]);
+                if ((int64_t)j * kThreads < nq) {  // uniform
+                    float v[16];
+                    unpack16(v, x[j][0], x[j][1], x[j][2], x[j][3]);
+                    if (PRO == PRO_NORM) {
+                        float gg[16];
+                        unpack16(gg, g[j][0], g[j][1], g[j][2], g[j][3]);
 #pragma unroll
-                    for (int i = 0; i < 16; i++) v[i] = (float)((double)gg[i] * ((double)v[i] * r));
+                        for (int i = 0; i < 16; i++) v[i] = (float)((double)gg[i] * ((double)v[i] * r));
+                    }
+                    store(p, smem, (int64_t)j * kThreads + threadIdx.x, v, lpg);
                 }
-                store(p, smem, (int64_t)j * kThreads + threadIdx.x, v, lpg);
             }
         } else {
             // long plain inputs: batches of 4 chunks per thread
@@ -278,10 +294,11 @@ struct InputQ8 {
                 }
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    if (base + (int64_t)j * kThreads >= nq) break;  // uniform
-                    float v[16];
-                    unpack16(v, a[j]);
-                    store(p, smem, base + (int64_t)j * kThreads + threadIdx.x, v, lpg);
+                    if (base + (int64_t)j * kThreads < nq) {  // uniform
+                        float v[16];
+                        unpack16(v, a[j][0], a[j][1], a[j][2], a[j][3]);
+                        store(p, smem, base + (int64_t)j * kThreads + threadIdx.x, v, lpg);
+                    }
                 }
             }
         }
@@ -343,10 +360,8 @@ struct InputCodes {
         const int lpg = p.gs / 16;
         if (NC > 0) {
 #pragma unroll
-            for (int j = 0; j < N; j++) {
-                if ((int64_t)j * kThreads >= nq) break;  // uniform
-                put(p, smem, (int64_t)j * kThreads + threadIdx.x, c[j], sc[j], lpg);
-            }
+            for (int j = 0; j < N; j++)
+                if ((int64_t)j * kThreads < nq) put(p, smem, (int64_t)j * kThreads + threadIdx.x, c[j], sc[j], lpg);
         } else {
             for (int64_t base = 0; base < nq; base += 4 * kThreads) {
                 i32x4 a[4];
@@ -358,10 +373,8 @@ struct InputCodes {
                     b[j] = p.xs[k / lpg];
                 }
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    if (base + (int64_t)j * kThreads >= nq) break;  // uniform
-                    put(p, smem, base + (int64_t)j * kThreads + threadIdx.x, a[j], b[j], lpg);
-                }
+                for (int j = 0; j < 4; j++)
+                    if (base + (int64_t)j * kThreads < nq) put(p, smem, base + (int64_t)j * kThreads + threadIdx.x, a[j], b[j], lpg);
             }
         }
         __syncthreads();
@@ -615,7 +628,7 @@ __device__ __forceinline__ void use_chunk(const Chunk<DT, RPW, U>& ch, double* a
 }
 
 template <int DT, int PRO, int EPI, int RPW, int U, int NC, int NBUF, bool DBG>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
+__global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ double red[kWaves];
