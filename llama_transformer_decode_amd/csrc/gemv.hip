@@ -628,7 +628,7 @@ __device__ __forceinline__ void use_chunk(const Chunk<DT, RPW, U>& ch, double* a
 }
 
 template <int DT, int PRO, int EPI, int RPW, int U, int NC, int NBUF, bool DBG>
-__global__ __launch_bounds__(kThreads, 2) void gemv_kernel(GemvParams p)
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ double red[kWaves];
