@@ -1,7 +1,9 @@
 // attn.hip - the attention kernel of the kernel-by-kernel step: grid
-// (n_kv_heads, NS), workgroup (g, c) runs the attention of kv head g over a
-// contiguous range of about (pos+1)/NS positions (rounded up to whole
-// sub-chunks; see attn_core.hpp for the computation). One active range: o is
+// (n_kv_heads * gsplit, NS), workgroup (vg, c) runs the attention of G/gsplit
+// of the query heads of kv head vg / gsplit over a contiguous range of about
+// (pos+1)/NS positions (rounded up to whole sub-chunks; see attn_core.hpp for
+// the computation). gsplit > 1 (used for 8 query heads per kv head) reads
+// the kv head's K/V rows once per workgroup but halves each merge. One active range: o is
 // written directly. Several: each range stores its (m, l, acc) with
 // device-scope stores, waits for them to complete and counts itself done on
 // its kv head's counter; the range that completes the count merges all of
@@ -34,7 +36,11 @@ template <int KG>
 __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int g = blockIdx.x, split = blockIdx.y;
+    // workgroup (vg, c): kv head g = vg / gsplit, its query heads
+    // [hsub * KG, (hsub + 1) * KG), positions of range c
+    const int vg = blockIdx.x, split = blockIdx.y;
+    const int g = vg / p.gsplit, hsub = vg % p.gsplit;
+    const size_t qoff = ((size_t)g * p.G + (size_t)hsub * KG) * p.hs;
     const int T = p.step[1] + 1;
     const int NS = p.nsplit;
     int nact;
@@ -46,7 +52,7 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     const int tid = threadIdx.x;
 
     AttnRange r;
-    r.q = p.q + (size_t)g * G * hs;
+    r.q = p.q + qoff;
     r.kc = p.kc;
     r.vc = p.vc;
     r.kvd = p.kvd;
@@ -63,13 +69,13 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
 
     if (nact == 1) {
         for (int e = tid; e < G * hs; e += kAThreads)
-            p.o[(size_t)g * G * hs + e] =
+            p.o[qoff + e] =
                 (float)(attn_value<kAThreads>(smem, G, hs, e) / attn_l<kAThreads>(smem, G, hs, e / hs));
         return;
     }
     // Several ranges: store (acc, m, l) at the device coherence point, then
     // count this range done; the last one merges
-    const size_t pbase = ((size_t)g * NS + split) * G;
+    const size_t pbase = ((size_t)vg * NS + split) * G;
     for (int e = tid; e < G * hs; e += kAThreads) st_dev(p.part_o + pbase * hs + e, attn_value<kAThreads>(smem, G, hs, e));
     if (tid < G) {
         st_dev(p.part_ml + (pbase + tid) * 2, attn_m<kAThreads>(smem, G, hs, tid));
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     __syncthreads();
     __shared__ int last;
     if (tid == 0) {
-        uint32_t* ctr = p.ctr + (size_t)g * 32;
+        uint32_t* ctr = p.ctr + (size_t)vg * 32;
         const uint32_t done = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = done + 1 == (uint32_t)nact;
         if (last) st_dev(ctr, 0u);  // the next use is a later launch
@@ -94,21 +100,26 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     // DPP in a fixed order. Every lane of a wave joins the DPP steps.
     __shared__ double wsh[kMaxG][64];
     __shared__ double lsh[kMaxG];
-    const size_t base = (size_t)g * NS;
+    const size_t base = (size_t)vg * NS;
     const int sub = tid & 3;
     constexpr int KMAX = 16;  // ranges per lane: NS <= 64
     const int kk = (nact + 3) / 4;  // ranges this lane's loads actually need
-    // the partial values of the first two passes go out together with the
-    // (m, l) loads below: the merge then costs one round trip, not two
-    constexpr int PRE = 2;
-    double pre[PRE][KMAX];
-#pragma unroll
-    for (int ps = 0; ps < PRE; ps++) {
+    // Output passes of 64 elements (4 lanes each). The partial values of PB
+    // passes are loaded together; the first batch goes out with the (m, l)
+    // loads below, so for G <= 2 (two passes at head size 128) the merge
+    // costs one device round trip, and for G = 8 four instead of sixteen.
+    constexpr int PB = KG >= 4 ? 4 : 2;
+    const int npass = (G * hs + kAThreads / 4 - 1) / (kAThreads / 4);
+    double buf[PB][KMAX];
+    auto load_pass = [&](double* o, int ps) {
         const int ec = min(ps * (kAThreads / 4) + (tid >> 2), G * hs - 1);
 #pragma unroll
         for (int k = 0; k < KMAX; k++)
-            pre[ps][k] = k < kk ? ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec) : 0.0;
-    }
+            o[k] = (k < kk && ps < npass) ? ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec)
+                                          : 0.0;
+    };
+#pragma unroll
+    for (int q = 0; q < PB; q++) load_pass(buf[q], q);
     for (int t = tid; t < G * 64; t += kAThreads) {
         const int h = t / 64, c = t % 64;
         const bool ok = c < nact;
@@ -121,26 +132,26 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
         if ((t & 63) == 0) lsh[h] = Ls;
     }
     __syncthreads();
-    for (int e0 = 0, ps = 0; e0 < G * hs; e0 += kAThreads / 4, ps++) {
-        const int e = e0 + (tid >> 2);
-        const int ec = e < G * hs ? e : G * hs - 1;
-        const int h = ec / hs;
-        double o[KMAX];
-        if (ps < PRE) {
+    for (int b0 = 0; b0 < npass; b0 += PB) {
+        if (b0 > 0) {
 #pragma unroll
-            for (int k = 0; k < KMAX; k++) o[k] = ps == 0 ? pre[0][k] : pre[1][k];
-        } else {
-#pragma unroll
-            for (int k = 0; k < KMAX; k++)
-                o[k] = k < kk ? ld_dev(p.part_o + ((base + min(sub + 4 * k, nact - 1)) * G) * hs + ec) : 0.0;
+            for (int q = 0; q < PB; q++) load_pass(buf[q], b0 + q);
         }
-        double O = 0.0;
 #pragma unroll
-        for (int k = 0; k < KMAX; k++)
-            if (sub + 4 * k < nact) O += wsh[h][sub + 4 * k] * o[k];
-        O += __hiloint2double(dpp_xor1(__double2hiint(O)), dpp_xor1(__double2loint(O)));
-        O += __hiloint2double(dpp_xor2(__double2hiint(O)), dpp_xor2(__double2loint(O)));
-        if (sub == 0 && e < G * hs) p.o[(size_t)g * G * hs + e] = (float)(O / lsh[h]);
+        for (int q = 0; q < PB; q++) {
+            if (b0 + q < npass) {  // uniform
+                const int e = (b0 + q) * (kAThreads / 4) + (tid >> 2);
+                const int ec = e < G * hs ? e : G * hs - 1;
+                const int h = ec / hs;
+                double O = 0.0;
+#pragma unroll
+                for (int k = 0; k < KMAX; k++)
+                    if (sub + 4 * k < nact) O += wsh[h][sub + 4 * k] * buf[q][k];
+                O += __hiloint2double(dpp_xor1(__double2hiint(O)), dpp_xor1(__double2loint(O)));
+                O += __hiloint2double(dpp_xor2(__double2hiint(O)), dpp_xor2(__double2loint(O)));
+                if (sub == 0 && e < G * hs) p.o[qoff + e] = (float)(O / lsh[h]);
+            }
+        }
     }
 }
 
@@ -148,14 +159,15 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEven
 {
     if (p.nsplit > 64) return hipErrorInvalidValue;  // the merge takes at most 64 ranges
     const size_t lds = attention_lds_bytes(p.G, p.hs, 0);
-    const dim3 grid(p.nkv, p.nsplit);
+    if (p.gsplit < 1 || p.G % p.gsplit) return hipErrorInvalidValue;
+    const dim3 grid(p.nkv * p.gsplit, p.nsplit);
 #define L2D_ATT(GG)                                                                                \
     if (ev)                                                                                        \
         hipExtLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), (uint32_t)lds, s,       \
                               ev->start, ev->stop, 0u, p);                                         \
     else                                                                                           \
         hipLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), lds, s, p);
-    switch (p.G) {
+    switch (p.G / p.gsplit) {
     case 1: L2D_ATT(1) break;
     case 2: L2D_ATT(2) break;
     case 4: L2D_ATT(4) break;

@@ -268,6 +268,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         a.kvd = (int32_t)kvd;
         a.G = (int32_t)ctx->G;
         a.nsplit = ctx->nsplit;
+        a.gsplit = ctx->gsplit;
         if (kt) HIP_TRY(ctx, kt->next(KC_ATTN));
         HIP_TRY(ctx, launch_attention(a, s, kt ? &kt->cur : nullptr));
 
@@ -434,7 +435,16 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     // inactive splits exit), at most 64 splits to merge per head
     {
         const int64_t sc = attention_positions_per_subchunk((int)ctx->hs);
-        int64_t ns = ((int64_t)3 * cus + ctx->nkv / 2) / ctx->nkv;
+        // 8 query heads per kv head: two workgroups share each kv head (4
+        // heads each), so the merge that follows the last range reads half
+        // as much per workgroup, and two run at once
+        ctx->gsplit = ctx->G == 8 ? 2 : 1;
+        if (const char* e = getenv("L2D_ATTN_GSPLIT")) {
+            const int v = atoi(e);
+            if (v >= 1 && ctx->G % v == 0 && ctx->G / v >= 1) ctx->gsplit = v;
+        }
+        const int64_t nv = ctx->nkv * ctx->gsplit;
+        int64_t ns = ((int64_t)3 * cus + nv / 2) / nv;
         if (ns > 64) ns = 64;
         if (ns > (ctx->S + sc - 1) / sc) ns = (ctx->S + sc - 1) / sc;
         ctx->nsplit = (int)(ns < 1 ? 1 : ns);
@@ -442,7 +452,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     const size_t nparts = (size_t)ctx->nkv * ctx->nsplit * ctx->G;
     ALLOC(ctx->part_o, nparts * ctx->hs * 8);
     ALLOC(ctx->part_ml, nparts * 2 * 8);
-    ALLOC(ctx->attn_ctr, (size_t)ctx->nkv * 32 * 4);
+    ALLOC(ctx->attn_ctr, (size_t)ctx->nkv * ctx->gsplit * 32 * 4);
     for (int i = 0; i < 4; i++) {
         const int64_t n = i == 3 ? h : d;
         ALLOC(ctx->trace_q[i], (size_t)n);
@@ -549,7 +559,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->argmax, 0, (size_t)kArgmaxWords * 8, ctx->stream));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * ctx->gsplit * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->hb_ctr, 0, (size_t)(ctx->h / ctx->gs + 1) * kGroupCtrStride * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
@@ -825,7 +835,7 @@ int l2d_reset_kv(l2d_ctx* ctx)
     const size_t kvbytes = (size_t)(ctx->L * ctx->S * ctx->kvd) * 4;
     HIP_TRY(ctx, hipMemsetAsync(ctx->kc, 0, kvbytes, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->vc, 0, kvbytes, ctx->stream));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * ctx->gsplit * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->hb_ctr, 0, (size_t)(ctx->h / ctx->gs + 1) * kGroupCtrStride * 4, ctx->stream));
     ctx->last_pos = -1;
     return L2D_OK;

@@ -95,9 +95,10 @@ struct AttnParams {
     float* o;          // [n_heads * hs]
     double* part_o;    // [nkv][nsplit][G][hs]
     double* part_ml;   // [nkv][nsplit][G][2]
-    uint32_t* ctr;     // [nkv][32]: ranges of each kv head done this launch (zero between launches)
+    uint32_t* ctr;     // [nkv * gsplit][32]: ranges done this launch per (kv head, head subset); zero between launches
     const int32_t* step;
     int32_t S, nkv, hs, kvd, G, nsplit;
+    int32_t gsplit;    // workgroups sharing one kv head's G query heads (G / gsplit heads each)
 };
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEvents* ev = nullptr);

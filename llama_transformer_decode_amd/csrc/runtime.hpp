@@ -66,6 +66,7 @@ struct l2d_ctx {
     double* part_ml = nullptr;
     uint32_t* attn_ctr = nullptr;  // [nkv][32] ranges done per kv head (attention merge)
     int nsplit = 0;
+    int gsplit = 1;  // workgroups per kv head in decode attention
 
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
