@@ -187,7 +187,10 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
     if (nsub > 1) load_kv<NT>(B, r, a, r0 + a.sc, min(a.sc, n - a.sc));
     for (int i = tid; i < G * hs; i += NT) {
         const int h = i / hs;
-        L.qs[i] = ld_dev(r.q + (size_t)(h / r.Gt) * r.qstride + (size_t)(h % r.Gt) * hs + i % hs);
+        // q written in this launch (fresh >= 0: the persistent step) needs a
+        // device-scope load; one written by an earlier launch does not
+        const float* qp = r.q + (size_t)(h / r.Gt) * r.qstride + (size_t)(h % r.Gt) * hs + i % hs;
+        L.qs[i] = r.fresh >= 0 ? ld_dev(qp) : *qp;
     }
     if (tid < G) {
         L.m_run[tid] = -INFINITY;
