@@ -246,7 +246,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.d = (int32_t)d;
         p.kvd = (int32_t)kvd;
         p.hs = (int32_t)ctx->hs;
-        p.freqs = ctx->freqs;
+        p.rope = ctx->rope;
         p.trace_q = tr ? ctx->trace_q[0] : nullptr;
         p.trace_s = tr ? ctx->trace_s[0] : nullptr;
         if (kt) HIP_TRY(ctx, kt->next(KC_QKV));
@@ -415,6 +415,7 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ALLOC(ctx->rms_ffn, (size_t)(L * d) * 4);
     ALLOC(ctx->rms_final, (size_t)d * 4);
     ALLOC(ctx->freqs, (size_t)(ctx->hs / 2) * 4);
+    ALLOC(ctx->rope, (size_t)ctx->hs * 4);
     const size_t kvbytes = (size_t)(L * ctx->S * kvd) * 4;
     ALLOC(ctx->kc, kvbytes);
     ALLOC(ctx->vc, kvbytes);
@@ -704,6 +705,9 @@ hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy,
     b.greedy = greedy ? 1 : 0;
     b.temperature = ctx->temperature;
     b.seed = ctx->seed;
+    b.freqs = ctx->freqs;
+    b.rope = ctx->rope;
+    b.hs = (int32_t)ctx->hs;
     return launch_begin(b, ctx->stream, ev);
 }
 

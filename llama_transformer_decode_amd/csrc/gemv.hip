@@ -660,9 +660,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     typename std::conditional<PRO == PRO_CODES, InputCodes<DT, NC>,
         typename std::conditional<DT == DT_F32, InputF32<PRO, NC>, InputQ8<DT, PRO, NC>>::type>::type in;
     in.issue(p);
-    // the RoPE frequency of this thread's pair (q/k/v epilogue)
-    float freq = 0.0f;
-    if (EPI == EPI_QKV && (int)threadIdx.x < p.hs / 2) freq = p.freqs[threadIdx.x];
+    // this step's RoPE cos / sin of this thread's pair (q/k/v epilogue),
+    // made once per step by the step-start kernel
+    float rc = 0.0f, rs = 0.0f;
+    if (EPI == EPI_QKV && (int)threadIdx.x < p.hs / 2) {
+        rc = p.rope[threadIdx.x];
+        rs = p.rope[p.hs / 2 + threadIdx.x];
+    }
     // keep every input load ahead of the weight prefetch: the prologue then
     // waits only for its own loads, not for the weights in flight behind them
     __builtin_amdgcn_sched_barrier(0);
@@ -681,16 +685,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p)
     for (int k = 0; k < NBUF; k++) load_next(buf[k]);
     __builtin_amdgcn_sched_barrier(0);
     in.fence();
-    hold(freq);
+    hold(rc);
+    hold(rs);
 
-    // 3. prologue. RoPE table of this pos first: fp32 cosine / sine of the
-    //    fp32 angle pos*freq_j, correctly rounded (fp64 value rounded once)
+    // 3. prologue: this step's RoPE table into LDS, then the input vector
     float* rcos = (float*)(smem + gemv_input_bytes(DT, p.K, p.gs));
     float* rsin = rcos + p.hs / 2;
     if (EPI == EPI_QKV && (int)threadIdx.x < p.hs / 2) {
-        const float ang = (float)pos * freq;
-        rcos[threadIdx.x] = (float)cos((double)ang);
-        rsin[threadIdx.x] = (float)sin((double)ang);
+        rcos[threadIdx.x] = rc;
+        rsin[threadIdx.x] = rs;
     }
     in.finish(p, smem, red);
 

@@ -56,7 +56,7 @@ struct GemvParams {
     float* kcache;  // this layer's [seq_len][kv_dim]
     float* vcache;
     int32_t d, kvd, hs;
-    const float* freqs;   // [hs/2] RoPE frequencies
+    const float* rope;    // [hs]: fp32 cos, then sin, of pos * freq_j for this step's pos
     const int32_t* step;  // device step record (kStep*)
     // EPI_LOGITS
     unsigned long long* argmax;  // [2][kArgmaxSlots][kArgmaxStride], parity pos & 1
@@ -178,6 +178,11 @@ struct BeginParams {
     int32_t token, pos, greedy;
     double temperature;  // 0: the classifier's argmax picks the token
     uint64_t seed;
+    // RoPE table of this step: rope[j] = cos, rope[hs/2 + j] = sin of the
+    // fp32 angle pos * freqs[j], each the fp64 value rounded once
+    const float* freqs;
+    float* rope;
+    int32_t hs;
 };
 
 hipError_t launch_begin(const BeginParams& p, hipStream_t s, const LaunchEvents* ev = nullptr);

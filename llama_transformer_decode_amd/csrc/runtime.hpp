@@ -48,6 +48,7 @@ struct l2d_ctx {
     float* rms_ffn = nullptr;
     float* rms_final = nullptr;
     float* freqs = nullptr;   // [hs/2]
+    float* rope = nullptr;    // [hs]: this step's RoPE cos / sin (step-start kernel)
 
     // state
     float* kc = nullptr;      // [L][S][kvd]

@@ -59,6 +59,11 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
     }
     if (blockIdx.x == 0 && threadIdx.x < kArgmaxSlots)
         p.argmax[((size_t)(p.pos & 1) * kArgmaxSlots + threadIdx.x) * kArgmaxStride] = 0ull;
+    if (blockIdx.x == 0 && (int)threadIdx.x < p.hs / 2) {
+        const float ang = (float)p.pos * p.freqs[threadIdx.x];
+        p.rope[threadIdx.x] = (float)cos((double)ang);
+        p.rope[p.hs / 2 + threadIdx.x] = (float)sin((double)ang);
+    }
 }
 
 hipError_t launch_begin(const BeginParams& p, hipStream_t s, const LaunchEvents* ev)
