@@ -19,8 +19,12 @@
 //   prefill_prep_kernel    RMSNorm (optional) + Q8_0 quantisation per token row
 //   prefill_gemm_kernel    int8 MFMA product + epilogue (q/k/v with RoPE and the
 //                          cache write, residual add, SwiGLU)
+//   prefill_attn_mfma_kernel  causal attention of 16 tokens of one head on the
+//                          fp64 matrix cores (one query head per kv head)
 //   prefill_attn_kernel    causal GQA attention of a block of tokens per kv head
+//                          (the other shapes)
 #include <hip/hip_ext.h>
+#include <stdlib.h>
 
 #include "attn_core.hpp"
 #include "device.hpp"
@@ -673,8 +677,250 @@ static int prefill_attn_rows(int G, int hs)
 
 bool prefill_attn_supported(int G, int hs) { return G >= 1 && prefill_attn_rows(G, hs) > 0; }
 
+// ---------------------------------------------------------------- attention on fp64 MFMA
+// One query head per kv head and a head size that is a multiple of 16 (up to
+// 128): a workgroup holds 16 query tokens of one head; its four wavefronts
+// take every fourth chunk of 16 positions each (so the long, late blocks are
+// spread over four SIMDs), each with S = Q K^T and O += P V on
+// v_mfma_f64_16x16x4f64 and the online softmax of the vector path in fp64
+// (scaled fp64 scores, running maximum, fp64 exp, fixed-order row sums). The
+// four partial (m, l, O) are merged at the end in a fixed order, as the decode
+// step merges position ranges. q is converted to fp64 once per token; K and
+// V rows are staged through each wavefront's own LDS, the next chunk's rows
+// loaded while the current one is used. Operand rows are fed in the order
+// 4*(i%4) + i/4, so register r of lane l ends up with token 4*(l/16) + r (as
+// in the fp64 prefill matmul).
+constexpr int kPMT = 16;            // query tokens per workgroup
+constexpr int kPMC = 16;            // positions per chunk
+constexpr int kPMW = 4;             // wavefronts per workgroup, chunks dealt round-robin
+constexpr int kPMHs = 128;          // largest head size
+constexpr int kPMSK = kPMHs + 4;    // K row stride in LDS: the B-operand reads hit distinct banks
+constexpr int kPMSV = kPMHs + 16;   // V row stride
+constexpr int kPMSP = kPMC + 1;     // P row stride (doubles)
+
+struct PrefillMfmaWaveLds {
+    float k[kPMC][kPMSK];
+    float v[kPMC][kPMSV];
+    double pt[kPMT][kPMSP];
+};
+// after the chunk loop the same bytes hold the wavefront's partial result
+struct PrefillMfmaMerge {
+    double o[64][kPMHs / 16 * 4];  // [lane][4 * tile + register]
+    double m[kPMT], l[kPMT];       // per token
+};
+static_assert(sizeof(PrefillMfmaMerge) <= sizeof(PrefillMfmaWaveLds), "merge area");
+
+static bool prefill_attn_mfma_ok(int G, int hs) { return G == 1 && hs % 16 == 0 && hs >= 16 && hs <= kPMHs; }
+
+// maximum / sum over each aligned group of 16 lanes, identical in every lane
+// of the group (quad swaps, half-row mirror, row mirror: each step combines
+// a pair of lanes symmetrically, so all lanes see the same operations)
+__device__ __forceinline__ double row16_max(double v)
+{
+    v = fmax(v, dpp_f64<0xB1>(v));
+    v = fmax(v, dpp_f64<0x4E>(v));
+    v = fmax(v, dpp_f64<0x141>(v));
+    return fmax(v, dpp_f64<0x140>(v));
+}
+
+__device__ __forceinline__ double row16_sum(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    return v + dpp_f64<0x140>(v);
+}
+
+// this wavefront's LDS writes complete before its lanes read them (each
+// wavefront owns its staging area; the waves run different chunk counts, so
+// no workgroup barrier inside the loop)
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAttnParams p)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    PrefillMfmaWaveLds& L = ((PrefillMfmaWaveLds*)smem)[w];
+    const int rl = lane % 16, ql = lane / 16;
+    const int perm = 4 * (rl % 4) + rl / 4;
+    const int g = blockIdx.x;
+    const int t0 = (gridDim.y - 1 - blockIdx.y) * kPMT;  // the longest blocks first
+    const int hs = p.hs, nks = hs / 4, ntile = hs / 16;
+    const int tlast = min(t0 + kPMT, p.m) - 1;
+    const int plast = p.pos0 + tlast;  // the last position any token of the block sees
+    const int nch = plast / kPMC + 1;
+    const double scale = 1.0 / sqrt((double)hs);
+
+    // Q operand of step ks: row rl, k ql = token t0 + perm, dimension 4 ks + ql.
+    // Tokens past the chunk read the query buffer's zeroed spare rows.
+    double qa[kPMHs / 4];
+    {
+        const float* qrow = p.q + (size_t)(t0 + perm) * p.d + (size_t)g * hs;
+#pragma unroll
+        for (int ks = 0; ks < kPMHs / 4; ks++) qa[ks] = ks < nks ? (double)qrow[4 * ks + ql] : 0.0;
+    }
+    v4d acc[kPMHs / 16];
+#pragma unroll
+    for (int j = 0; j < kPMHs / 16; j++) acc[j] = v4d{0.0, 0.0, 0.0, 0.0};
+    double mrun[4], lrun[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        mrun[r] = -INFINITY;
+        lrun[r] = 0.0;
+    }
+
+    // staging: the chunk's 16 K rows and 16 V rows, hs/16 float4 of each per lane
+    const int f4row = hs / 4;
+    const int nf4 = kPMC * f4row / 64;
+    f32x4 kr[kPMHs / 16], vr[kPMHs / 16];
+    auto stage_load = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < kPMHs / 16; i++) {
+            if (i < nf4) {
+                const int idx = lane + 64 * i, row = idx / f4row, col = idx % f4row;
+                const int pp = min(c * kPMC + row, plast);  // rows past the last one repeat it (masked)
+                const size_t off = (size_t)pp * p.kvd + (size_t)g * hs + 4 * col;
+                kr[i] = *(const f32x4*)(p.kc + off);
+                vr[i] = *(const f32x4*)(p.vc + off);
+            }
+        }
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < kPMHs / 16; i++) {
+            if (i < nf4) {
+                const int idx = lane + 64 * i, row = idx / f4row, col = idx % f4row;
+                *(f32x4*)&L.k[row][4 * col] = kr[i];
+                *(f32x4*)&L.v[row][4 * col] = vr[i];
+            }
+        }
+    };
+
+    if (w < nch) stage_load(w);
+    for (int c = w; c < nch; c += kPMW) {
+        stage_store();
+        lds_wave_sync();
+        if (c + kPMW < nch) stage_load(c + kPMW);
+
+        // S = Q K^T: operand B[k ql][col rl] = K[position rl][4 ks + ql]; two
+        // interleaved accumulators halve the dependent chain
+        v4d s0 = v4d{0.0, 0.0, 0.0, 0.0}, s1 = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int ks = 0; ks < kPMHs / 4; ks += 2) {
+            if (ks < nks) s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], (double)L.k[rl][4 * ks + ql], s0, 0, 0, 0);
+            if (ks + 1 < nks)
+                s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks + 1], (double)L.k[rl][4 * ks + 4 + ql], s1, 0, 0, 0);
+        }
+        const v4d sacc = s0 + s1;
+
+        // causal mask, online softmax; register r is token t0 + 4 ql + r,
+        // lane rl is position c*16 + rl
+        const int pp = c * kPMC + rl;
+        double pr[4], alpha[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int tpos = p.pos0 + t0 + 4 * ql + r;
+            const double sv = pp <= tpos ? sacc[r] * scale : -INFINITY;
+            const double mn = fmax(mrun[r], row16_max(sv));
+            // a token may see none of this wavefront's positions so far (its
+            // first chunks lie past it): then every term is 0, not e^(-inf + inf)
+            const double ms = mn == -INFINITY ? 0.0 : mn;
+            const double e = exp(sv - ms);
+            const double sum = row16_sum(e);
+            alpha[r] = exp(mrun[r] - ms);  // 0 on the first chunk the token sees
+            lrun[r] = lrun[r] * alpha[r] + sum;
+            mrun[r] = mn;
+            pr[r] = e;
+        }
+#pragma unroll
+        for (int j = 0; j < kPMHs / 16; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[j][r] *= alpha[r];
+
+        // O += P V: P through LDS into operand order, B[k ql][col rl] = V[4 ks + ql][16 j + rl]
+#pragma unroll
+        for (int r = 0; r < 4; r++) L.pt[4 * ql + r][rl] = pr[r];
+        lds_wave_sync();
+#pragma unroll
+        for (int ks = 0; ks < kPMC / 4; ks++) {
+            const double a = L.pt[perm][4 * ks + ql];
+#pragma unroll
+            for (int j = 0; j < kPMHs / 16; j++)
+                if (j < ntile)
+                    acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)L.v[4 * ks + ql][16 * j + rl], acc[j], 0, 0, 0);
+        }
+        lds_wave_sync();
+    }
+
+    // merge the wavefronts' partial results in a fixed order (wave 0..3): a
+    // wavefront without chunks contributes m = -inf, l = 0, O = 0
+    __syncthreads();
+    {
+        PrefillMfmaMerge& M = *(PrefillMfmaMerge*)&L;
+#pragma unroll
+        for (int j = 0; j < kPMHs / 16; j++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) M.o[lane][4 * j + r] = acc[j][r];
+        if (rl == 0)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                M.m[4 * ql + r] = mrun[r];
+                M.l[4 * ql + r] = lrun[r];
+            }
+    }
+    __syncthreads();
+    // wave w finishes tiles w, w + 4, ...
+    for (int j = w; j < ntile; j += kPMW) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int tk = 4 * ql + r;
+            double mw[kPMW], mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < kPMW; u++) {
+                mw[u] = ((PrefillMfmaMerge*)&((PrefillMfmaWaveLds*)smem)[u])->m[tk];
+                mx = fmax(mx, mw[u]);
+            }
+            double O = 0.0, Lsum = 0.0;
+#pragma unroll
+            for (int u = 0; u < kPMW; u++) {
+                const PrefillMfmaMerge* Mu = (const PrefillMfmaMerge*)&((PrefillMfmaWaveLds*)smem)[u];
+                const double f = exp(mw[u] - mx);  // 0 for a wavefront without chunks
+                O += f * Mu->o[lane][4 * j + r];
+                Lsum += f * Mu->l[tk];
+            }
+            const int t = t0 + tk;
+            if (t <= tlast) p.o[(size_t)t * p.d + (size_t)g * hs + 16 * j + rl] = (float)(O / Lsum);
+        }
+    }
+}
+
+static hipError_t prefill_mfma_lds_attr()
+{
+    static bool done = false;
+    if (!done) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_attn_mfma_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(kPMW * sizeof(PrefillMfmaWaveLds)));
+        if (e != hipSuccess) return e;
+        done = true;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_prefill_attn(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
+    if (prefill_attn_mfma_ok(p.G, p.hs) && !getenv("L2D_PREFILL_ATTN_VALU")) {
+        const hipError_t e = prefill_mfma_lds_attr();
+        if (e != hipSuccess) return e;
+        const dim3 grid((unsigned)p.nkv, (unsigned)((p.m + kPMT - 1) / kPMT));
+        const size_t lds = kPMW * sizeof(PrefillMfmaWaveLds);
+        if (ev)
+            hipExtLaunchKernelGGL(prefill_attn_mfma_kernel, grid, dim3(64 * kPMW), (uint32_t)lds, s, ev->start,
+                                  ev->stop, 0u, p);
+        else
+            hipLaunchKernelGGL(prefill_attn_mfma_kernel, grid, dim3(64 * kPMW), lds, s, p);
+        return hipGetLastError();
+    }
     const int kg = prefill_attn_rows(p.G, p.hs);
     if (kg == 0) return hipErrorInvalidValue;
     const int TB = kg / p.G;
