@@ -680,19 +680,18 @@ bool prefill_attn_supported(int G, int hs) { return G >= 1 && prefill_attn_rows(
 // ---------------------------------------------------------------- attention on fp64 MFMA
 // One query head per kv head and a head size that is a multiple of 16 (up to
 // 128): a workgroup holds 16 query tokens of one head; its four wavefronts
-// take every fourth chunk of 16 positions each (so the long, late blocks are
-// spread over four SIMDs), each with S = Q K^T and O += P V on
-// v_mfma_f64_16x16x4f64 and the online softmax of the vector path in fp64
-// (scaled fp64 scores, running maximum, fp64 exp, fixed-order row sums). The
-// four partial (m, l, O) are merged at the end in a fixed order, as the decode
-// step merges position ranges. q is converted to fp64 once per token; K and
-// V rows are staged through each wavefront's own LDS, the next chunk's rows
-// loaded while the current one is used. Operand rows are fed in the order
-// 4*(i%4) + i/4, so register r of lane l ends up with token 4*(l/16) + r (as
-// in the fp64 prefill matmul).
+// take every fourth chunk of 16 positions (so the long, late blocks are
+// spread over four SIMDs; two workgroups share a CU). Each computes
+// S = Q K^T and O += P V on v_mfma_f64_16x16x4f64 with the online softmax of
+// the vector path in fp64 (scaled fp64 scores, running maximum, fp64 exp,
+// fixed-order row sums). The four partial (m, l, O) are merged at the end in
+// a fixed order, as the decode step merges position ranges. q is converted to
+// fp64 once per token; K and V rows are staged through each wavefront's own
+// LDS. Operand rows are fed in the order 4*(i%4) + i/4, so register r of
+// lane l ends up with token 4*(l/16) + r (as in the fp64 prefill matmul).
 constexpr int kPMT = 16;            // query tokens per workgroup
 constexpr int kPMC = 16;            // positions per chunk
-constexpr int kPMW = 4;             // wavefronts per workgroup, chunks dealt round-robin
+constexpr int kPMW = 4;             // wavefronts per workgroup (8 measured slower)
 constexpr int kPMHs = 128;          // largest head size
 constexpr int kPMSK = kPMHs + 4;    // K row stride in LDS: the B-operand reads hit distinct banks
 constexpr int kPMSV = kPMHs + 16;   // V row stride
@@ -736,8 +735,15 @@ __device__ __forceinline__ double row16_sum(double v)
 // no workgroup barrier inside the loop)
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAttnParams p)
+// NT = head size / 16: every loop below has a compile-time trip count. W
+// wavefronts per workgroup. A chunk's K/V rows are loaded when it starts:
+// two wavefronts per SIMD (at most 256 registers each) cover each other's
+// load latency, where holding the next chunk's rows in registers (one
+// wavefront per SIMD) measured slower.
+template <int NT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_mfma_kernel(PrefillAttnParams p)
 {
+    constexpr int HS = 16 * NT, NKS = HS / 4, F4ROW = HS / 4;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     PrefillMfmaWaveLds& L = ((PrefillMfmaWaveLds*)smem)[w];
@@ -745,23 +751,22 @@ __global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAtt
     const int perm = 4 * (rl % 4) + rl / 4;
     const int g = blockIdx.x;
     const int t0 = (gridDim.y - 1 - blockIdx.y) * kPMT;  // the longest blocks first
-    const int hs = p.hs, nks = hs / 4, ntile = hs / 16;
     const int tlast = min(t0 + kPMT, p.m) - 1;
     const int plast = p.pos0 + tlast;  // the last position any token of the block sees
     const int nch = plast / kPMC + 1;
-    const double scale = 1.0 / sqrt((double)hs);
+    const double scale = 1.0 / sqrt((double)HS);
 
     // Q operand of step ks: row rl, k ql = token t0 + perm, dimension 4 ks + ql.
     // Tokens past the chunk read the query buffer's zeroed spare rows.
-    double qa[kPMHs / 4];
+    double qa[NKS];
     {
-        const float* qrow = p.q + (size_t)(t0 + perm) * p.d + (size_t)g * hs;
+        const float* qrow = p.q + (size_t)(t0 + perm) * p.d + (size_t)g * HS;
 #pragma unroll
-        for (int ks = 0; ks < kPMHs / 4; ks++) qa[ks] = ks < nks ? (double)qrow[4 * ks + ql] : 0.0;
+        for (int ks = 0; ks < NKS; ks++) qa[ks] = (double)qrow[4 * ks + ql];
     }
-    v4d acc[kPMHs / 16];
+    v4d acc[NT];
 #pragma unroll
-    for (int j = 0; j < kPMHs / 16; j++) acc[j] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < NT; j++) acc[j] = v4d{0.0, 0.0, 0.0, 0.0};
     double mrun[4], lrun[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -769,46 +774,39 @@ __global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAtt
         lrun[r] = 0.0;
     }
 
-    // staging: the chunk's 16 K rows and 16 V rows, hs/16 float4 of each per lane
-    const int f4row = hs / 4;
-    const int nf4 = kPMC * f4row / 64;
-    f32x4 kr[kPMHs / 16], vr[kPMHs / 16];
+    // staging: the chunk's 16 K rows and 16 V rows, NT float4 of each per lane
+    f32x4 kr[NT], vr[NT];
     auto stage_load = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < kPMHs / 16; i++) {
-            if (i < nf4) {
-                const int idx = lane + 64 * i, row = idx / f4row, col = idx % f4row;
-                const int pp = min(c * kPMC + row, plast);  // rows past the last one repeat it (masked)
-                const size_t off = (size_t)pp * p.kvd + (size_t)g * hs + 4 * col;
-                kr[i] = *(const f32x4*)(p.kc + off);
-                vr[i] = *(const f32x4*)(p.vc + off);
-            }
+        for (int i = 0; i < NT; i++) {
+            const int idx = lane + 64 * i, row = idx / F4ROW, col = idx % F4ROW;
+            const int pp = min(c * kPMC + row, plast);  // rows past the last one repeat it (masked)
+            const size_t off = (size_t)pp * p.kvd + (size_t)g * HS + 4 * col;
+            kr[i] = *(const f32x4*)(p.kc + off);
+            vr[i] = *(const f32x4*)(p.vc + off);
         }
     };
     auto stage_store = [&]() {
 #pragma unroll
-        for (int i = 0; i < kPMHs / 16; i++) {
-            if (i < nf4) {
-                const int idx = lane + 64 * i, row = idx / f4row, col = idx % f4row;
-                *(f32x4*)&L.k[row][4 * col] = kr[i];
-                *(f32x4*)&L.v[row][4 * col] = vr[i];
-            }
+        for (int i = 0; i < NT; i++) {
+            const int idx = lane + 64 * i, row = idx / F4ROW, col = idx % F4ROW;
+            *(f32x4*)&L.k[row][4 * col] = kr[i];
+            *(f32x4*)&L.v[row][4 * col] = vr[i];
         }
     };
 
-    if (w < nch) stage_load(w);
-    for (int c = w; c < nch; c += kPMW) {
+    for (int c = w; c < nch; c += W) {
+        stage_load(c);
         stage_store();
         lds_wave_sync();
-        if (c + kPMW < nch) stage_load(c + kPMW);
 
         // S = Q K^T: operand B[k ql][col rl] = K[position rl][4 ks + ql]; two
         // interleaved accumulators halve the dependent chain
         v4d s0 = v4d{0.0, 0.0, 0.0, 0.0}, s1 = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int ks = 0; ks < kPMHs / 4; ks += 2) {
-            if (ks < nks) s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], (double)L.k[rl][4 * ks + ql], s0, 0, 0, 0);
-            if (ks + 1 < nks)
+        for (int ks = 0; ks < NKS; ks += 2) {
+            s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], (double)L.k[rl][4 * ks + ql], s0, 0, 0, 0);
+            if (ks + 1 < NKS)
                 s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks + 1], (double)L.k[rl][4 * ks + 4 + ql], s1, 0, 0, 0);
         }
         const v4d sacc = s0 + s1;
@@ -816,24 +814,36 @@ __global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAtt
         // causal mask, online softmax; register r is token t0 + 4 ql + r,
         // lane rl is position c*16 + rl
         const int pp = c * kPMC + rl;
-        double pr[4], alpha[4];
+        double pr[4], mn[4], ms[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int tpos = p.pos0 + t0 + 4 * ql + r;
             const double sv = pp <= tpos ? sacc[r] * scale : -INFINITY;
-            const double mn = fmax(mrun[r], row16_max(sv));
+            mn[r] = fmax(mrun[r], row16_max(sv));
             // a token may see none of this wavefront's positions so far (its
             // first chunks lie past it): then every term is 0, not e^(-inf + inf)
-            const double ms = mn == -INFINITY ? 0.0 : mn;
-            const double e = exp(sv - ms);
-            const double sum = row16_sum(e);
-            alpha[r] = exp(mrun[r] - ms);  // 0 on the first chunk the token sees
-            lrun[r] = lrun[r] * alpha[r] + sum;
-            mrun[r] = mn;
-            pr[r] = e;
+            ms[r] = mn[r] == -INFINITY ? 0.0 : mn[r];
+            pr[r] = exp(sv - ms[r]);
+        }
+        // the rescale factor of token 4 ql + r is the same in all 16 lanes of
+        // the row: lane rl computes the one of r = rl % 4 and each quad of
+        // lanes shares its four by DPP broadcast
+        const int ro = rl & 3;
+        const double mo = ro == 0 ? mrun[0] : ro == 1 ? mrun[1] : ro == 2 ? mrun[2] : mrun[3];
+        const double so = ro == 0 ? ms[0] : ro == 1 ? ms[1] : ro == 2 ? ms[2] : ms[3];
+        const double ao = exp(mo - so);  // 0 on the first chunk the token sees
+        double alpha[4];
+        alpha[0] = dpp_f64<0x00>(ao);
+        alpha[1] = dpp_f64<0x55>(ao);
+        alpha[2] = dpp_f64<0xAA>(ao);
+        alpha[3] = dpp_f64<0xFF>(ao);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            lrun[r] = lrun[r] * alpha[r] + row16_sum(pr[r]);
+            mrun[r] = mn[r];
         }
 #pragma unroll
-        for (int j = 0; j < kPMHs / 16; j++)
+        for (int j = 0; j < NT; j++)
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[j][r] *= alpha[r];
 
@@ -845,9 +855,8 @@ __global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAtt
         for (int ks = 0; ks < kPMC / 4; ks++) {
             const double a = L.pt[perm][4 * ks + ql];
 #pragma unroll
-            for (int j = 0; j < kPMHs / 16; j++)
-                if (j < ntile)
-                    acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)L.v[4 * ks + ql][16 * j + rl], acc[j], 0, 0, 0);
+            for (int j = 0; j < NT; j++)
+                acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)L.v[4 * ks + ql][16 * j + rl], acc[j], 0, 0, 0);
         }
         lds_wave_sync();
     }
@@ -858,7 +867,7 @@ __global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAtt
     {
         PrefillMfmaMerge& M = *(PrefillMfmaMerge*)&L;
 #pragma unroll
-        for (int j = 0; j < kPMHs / 16; j++)
+        for (int j = 0; j < NT; j++)
 #pragma unroll
             for (int r = 0; r < 4; r++) M.o[lane][4 * j + r] = acc[j][r];
         if (rl == 0)
@@ -869,57 +878,79 @@ __global__ __launch_bounds__(64 * kPMW) void prefill_attn_mfma_kernel(PrefillAtt
             }
     }
     __syncthreads();
-    // wave w finishes tiles w, w + 4, ...
-    for (int j = w; j < ntile; j += kPMW) {
+    // wave w finishes tiles w, w + W, ...
+    for (int j = w; j < NT; j += W) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int tk = 4 * ql + r;
-            double mw[kPMW], mx = -INFINITY;
+            double mw[W], mx = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < kPMW; u++) {
+            for (int u = 0; u < W; u++) {
                 mw[u] = ((PrefillMfmaMerge*)&((PrefillMfmaWaveLds*)smem)[u])->m[tk];
                 mx = fmax(mx, mw[u]);
             }
             double O = 0.0, Lsum = 0.0;
 #pragma unroll
-            for (int u = 0; u < kPMW; u++) {
+            for (int u = 0; u < W; u++) {
                 const PrefillMfmaMerge* Mu = (const PrefillMfmaMerge*)&((PrefillMfmaWaveLds*)smem)[u];
                 const double f = exp(mw[u] - mx);  // 0 for a wavefront without chunks
                 O += f * Mu->o[lane][4 * j + r];
                 Lsum += f * Mu->l[tk];
             }
             const int t = t0 + tk;
-            if (t <= tlast) p.o[(size_t)t * p.d + (size_t)g * hs + 16 * j + rl] = (float)(O / Lsum);
+            if (t <= tlast) p.o[(size_t)t * p.d + (size_t)g * HS + 16 * j + rl] = (float)(O / Lsum);
         }
     }
 }
 
+template <int NT, int W>
 static hipError_t prefill_mfma_lds_attr()
 {
     static bool done = false;
     if (!done) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_attn_mfma_kernel,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_attn_mfma_kernel<NT, W>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kPMW * sizeof(PrefillMfmaWaveLds)));
+                                           (int)(W * sizeof(PrefillMfmaWaveLds)));
         if (e != hipSuccess) return e;
         done = true;
     }
     return hipSuccess;
 }
 
+template <int NT, int W>
+static hipError_t launch_prefill_mfma(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev)
+{
+    if (hipError_t e = prefill_mfma_lds_attr<NT, W>(); e != hipSuccess) return e;
+    const dim3 grid((unsigned)p.nkv, (unsigned)((p.m + kPMT - 1) / kPMT));
+    const size_t lds = W * sizeof(PrefillMfmaWaveLds);
+    if (ev)
+        hipExtLaunchKernelGGL((prefill_attn_mfma_kernel<NT, W>), grid, dim3(64 * W), (uint32_t)lds, s, ev->start,
+                              ev->stop, 0u, p);
+    else
+        hipLaunchKernelGGL((prefill_attn_mfma_kernel<NT, W>), grid, dim3(64 * W), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int W>
+static hipError_t launch_prefill_mfma_w(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev)
+{
+    switch (p.hs / 16) {
+    case 1: return launch_prefill_mfma<1, W>(p, s, ev);
+    case 2: return launch_prefill_mfma<2, W>(p, s, ev);
+    case 3: return launch_prefill_mfma<3, W>(p, s, ev);
+    case 4: return launch_prefill_mfma<4, W>(p, s, ev);
+    case 5: return launch_prefill_mfma<5, W>(p, s, ev);
+    case 6: return launch_prefill_mfma<6, W>(p, s, ev);
+    case 7: return launch_prefill_mfma<7, W>(p, s, ev);
+    case 8: return launch_prefill_mfma<8, W>(p, s, ev);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_prefill_attn(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     if (prefill_attn_mfma_ok(p.G, p.hs) && !getenv("L2D_PREFILL_ATTN_VALU")) {
-        const hipError_t e = prefill_mfma_lds_attr();
-        if (e != hipSuccess) return e;
-        const dim3 grid((unsigned)p.nkv, (unsigned)((p.m + kPMT - 1) / kPMT));
-        const size_t lds = kPMW * sizeof(PrefillMfmaWaveLds);
-        if (ev)
-            hipExtLaunchKernelGGL(prefill_attn_mfma_kernel, grid, dim3(64 * kPMW), (uint32_t)lds, s, ev->start,
-                                  ev->stop, 0u, p);
-        else
-            hipLaunchKernelGGL(prefill_attn_mfma_kernel, grid, dim3(64 * kPMW), lds, s, p);
-        return hipGetLastError();
+        return launch_prefill_mfma_w<kPMW>(p, s, ev);
     }
     const int kg = prefill_attn_rows(p.G, p.hs);
     if (kg == 0) return hipErrorInvalidValue;
