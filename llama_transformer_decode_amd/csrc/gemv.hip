@@ -808,7 +808,7 @@ static hipError_t launch_nc(const GemvParams& p, int max_blocks, hipStream_t s, 
 // (fp32), or U = gs/16 loads per group (Q8_0); every wave gets a contiguous
 // share of the tiles; the grid is capped at max_blocks workgroups.
 // Measured on MI355X (7B shapes, back-to-back launches): two chunks in the
-// ring beat three or four (fewer registers, more waves); Q8_0 rows are best
+// ring beat three or four (fewer registers, more waves); fp32 and Q8_0 rows are best
 // one per tile when the matrix gives a wave fewer than three two-row tiles
 // (output projection, w2), two per tile otherwise. Epilogues that combine a
 // row pair (RoPE, SwiGLU) get an even number of rows per tile, or one-row
@@ -817,6 +817,13 @@ template <int DT, int PRO, int EPI, bool DBG>
 static hipError_t launch_shape(const GemvParams& p, int max_blocks, hipStream_t s, const LaunchEvents* ev)
 {
     if constexpr (DT == DT_F32) {
+        // one-row tiles on the same rule as Q8_0 (7B output projection and
+        // w2: 0.2 and 1.1 us faster than two-row tiles; two-row tiles with
+        // 2 or 8 loads and four-row tiles were slower on every shape)
+        if constexpr (EPI != EPI_QKV && EPI != EPI_SWIGLU) {
+            const int64_t waves = (int64_t)(max_blocks > 0 ? max_blocks : 512) * kWaves;
+            if (p.M < 6 * waves) return launch_nc<DT, PRO, EPI, 1, 4, DBG>(p, max_blocks, s, ev);
+        }
         return launch_nc<DT, PRO, EPI, 2, 4, DBG>(p, max_blocks, s, ev);
     } else if constexpr (DT == DT_Q4) {
         // four rows of one group per lane: the fastest of RPW 1-8 x U 1-4
