@@ -234,6 +234,15 @@ __device__ __forceinline__ void prefill_epilogue(const PrefillGemmParams& p, int
 constexpr int kGR = 64, kGT = 128, kGParts = 8;
 constexpr int kTR = 2, kTT = 4;  // 16 x 16 tiles per wavefront: rows, tokens
 
+// Staged weight rows are stored at row ^ gemm_swz(part, quarter). The XOR
+// stays within an aligned block of 16 rows, so the 16 lanes of one operand
+// read still hit 16 distinct 16-byte bank groups, and the staging writes
+// (adjacent lanes: different parts and quarters of the same row) spread over
+// 16 bank groups instead of landing on one. Only for one 64-value part per
+// group: with 2 or 4 the index arithmetic made those instances spill.
+template <int U>
+__device__ __forceinline__ int gemm_swz(int part, int quarter) { return U == 1 ? ((part & 3) << 2) | quarter : 0; }
+
 struct GemmLds {
     v4i w[2][kGParts][4][kGR];    // [buffer][part][quarter][row], 16 bytes each
     float sw[2][kGParts][kGR];    // weight scales [buffer][group of the step][row]
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
         for (int k = 0; k < kPieces; k++) {
             const int id2 = tid + 256 * k;
             const int jg = id2 % GPS, Q = (id2 / GPS) % (4 * U), r = id2 / (GPS * 4 * U);
-            L.w[bf][jg * U + Q / 4][Q % 4][r] = wreg[k];
+            L.w[bf][jg * U + Q / 4][Q % 4][r ^ gemm_swz<U>(jg * U + Q / 4, Q % 4)] = wreg[k];
         }
 #pragma unroll
         for (int k = 0; k < (kGR * GPS + 255) / 256; k++) {
@@ -370,7 +379,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
             const double sw[4] = {(double)sw4.x, (double)sw4.y, (double)sw4.z, (double)sw4.w};
             v4i a[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) a[u] = L.w[bf][gl * U + u][ql][32 * wr + 16 * i + rl];
+            for (int u = 0; u < U; u++)
+                a[u] = L.w[bf][gl * U + u][ql][(32 * wr + 16 * i + rl) ^ gemm_swz<U>(gl * U + u, ql)];
 #pragma unroll
             for (int j = 0; j < kTT; j++) {
                 v4i c = {0, 0, 0, 0};
