@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
 {
 #pragma clang fp contract(off)
     constexpr int GPS = kGParts / U;  // groups per step
-    constexpr int kGRing = U == 1 ? 3 : U == 2 ? 2 : 1;
+    constexpr int kGRing = U == 1 ? 2 : U == 2 ? 2 : 1;
     extern __shared__ __align__(16) unsigned char gsmem[];
     GemmLds& L = *(GemmLds*)gsmem;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -370,17 +370,32 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
 
     auto use_group = [&](const GemmOps<U>& o, int g) {
         const int bf = (g / GPS) & 1, gl = g % GPS;
-        double sx[kTT];
-#pragma unroll
-        for (int j = 0; j < kTT; j++) sx[j] = (double)L.sx[bf][gl][64 * wt + 16 * j + rl];
-#pragma unroll
-        for (int i = 0; i < kTR; i++) {
-            const f32x4 sw4 = *(const f32x4*)&L.sw[bf][gl][32 * wr + 16 * i + 4 * ql];
-            const double sw[4] = {(double)sw4.x, (double)sw4.y, (double)sw4.z, (double)sw4.w};
-            v4i a[U];
+        // with one part per group every LDS read of the group is issued
+        // first, so one wait covers them all (with 2 or 4 parts the extra
+        // operands would spill: their reads stay per row tile)
+        float sxf[kTT];
+        f32x4 sw4[kTR];
+        v4i av[kTR][U];
+        auto read_rows = [&](int i) {
+            sw4[i] = *(const f32x4*)&L.sw[bf][gl][32 * wr + 16 * i + 4 * ql];
 #pragma unroll
             for (int u = 0; u < U; u++)
-                a[u] = L.w[bf][gl * U + u][ql][(32 * wr + 16 * i + rl) ^ gemm_swz<U>(gl * U + u, ql)];
+                av[i][u] = L.w[bf][gl * U + u][ql][(32 * wr + 16 * i + rl) ^ gemm_swz<U>(gl * U + u, ql)];
+        };
+#pragma unroll
+        for (int j = 0; j < kTT; j++) sxf[j] = L.sx[bf][gl][64 * wt + 16 * j + rl];
+        if constexpr (U == 1) {
+#pragma unroll
+            for (int i = 0; i < kTR; i++) read_rows(i);
+        }
+        double sx[kTT];
+#pragma unroll
+        for (int j = 0; j < kTT; j++) sx[j] = (double)sxf[j];
+#pragma unroll
+        for (int i = 0; i < kTR; i++) {
+            if constexpr (U != 1) read_rows(i);
+            const double sw[4] = {(double)sw4[i].x, (double)sw4[i].y, (double)sw4[i].z, (double)sw4[i].w};
+            const v4i* a = av[i];
 #pragma unroll
             for (int j = 0; j < kTT; j++) {
                 v4i c = {0, 0, 0, 0};
