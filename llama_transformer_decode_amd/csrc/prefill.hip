@@ -245,9 +245,14 @@ __device__ __forceinline__ int gemm_swz(int part, int quarter) { return U == 1 ?
 
 struct GemmLds {
     v4i w[2][kGParts][4][kGR];    // [buffer][part][quarter][row], 16 bytes each
-    float sw[2][kGParts][kGR];    // weight scales [buffer][group of the step][row]
-    float sx[2][kGParts][kGT];    // input scales [buffer][group of the step][token]
+    // scales [buffer][group of the step][row or token]; rows padded by 8
+    // floats so that a staging write (8 groups of 8 rows or tokens) hits 64
+    // distinct banks
+    float sw[2][kGParts][kGR + 8];
+    float sx[2][kGParts][kGT + 8];
 };
+// two workgroups per CU (launch bounds) must fit the CU's 160 KiB of LDS
+static_assert(2 * sizeof(GemmLds) <= 160 * 1024, "GemmLds");
 
 template <int U>
 struct GemmOps {
