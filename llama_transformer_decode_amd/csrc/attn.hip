@@ -32,7 +32,9 @@ bool attention_supported(int G, int hs)
 
 size_t attention_lds_bytes(int G, int hs, int) { return attn_core_lds_bytes<kAThreads>(G, hs); }
 
-template <int KG>
+// HS > 0: the head size as a compile-time constant (every shape of the range
+// computation folds, with no branches on it); HS = 0: read from p.hs
+template <int KG, int HS>
 __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -40,15 +42,15 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     // [hsub * KG, (hsub + 1) * KG), positions of range c
     const int vg = blockIdx.x, split = blockIdx.y;
     const int g = vg / p.gsplit, hsub = vg % p.gsplit;
-    const size_t qoff = ((size_t)g * p.G + (size_t)hsub * KG) * p.hs;
+    const size_t qoff = ((size_t)g * p.G + (size_t)hsub * KG) * (HS > 0 ? HS : p.hs);
     const int T = p.step[1] + 1;
     const int NS = p.nsplit;
     int nact;
-    const int per = attn_split(T, NS, attn_shape<kAThreads>(p.hs).sc, &nact);
+    const int hs = HS > 0 ? HS : p.hs;
+    const int per = attn_split(T, NS, attn_shape<kAThreads>(hs).sc, &nact);
     if (split >= nact) return;
     const int r0 = split * per;
     constexpr int G = KG;
-    const int hs = p.hs;
     const int tid = threadIdx.x;
 
     AttnRange r;
@@ -161,12 +163,20 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEven
     const size_t lds = attention_lds_bytes(p.G, p.hs, 0);
     if (p.gsplit < 1 || p.G % p.gsplit) return hipErrorInvalidValue;
     const dim3 grid(p.nkv * p.gsplit, p.nsplit);
-#define L2D_ATT(GG)                                                                                \
+#define L2D_ATT2(GG, HH)                                                                           \
     if (ev)                                                                                        \
-        hipExtLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), (uint32_t)lds, s,       \
+        hipExtLaunchKernelGGL((attention_kernel<GG, HH>), grid, dim3(kAThreads), (uint32_t)lds, s, \
                               ev->start, ev->stop, 0u, p);                                         \
     else                                                                                           \
-        hipLaunchKernelGGL(attention_kernel<GG>, grid, dim3(kAThreads), lds, s, p);
+        hipLaunchKernelGGL((attention_kernel<GG, HH>), grid, dim3(kAThreads), lds, s, p);
+#define L2D_ATT(GG)                                                                                \
+    if (p.hs == 128) {                                                                             \
+        L2D_ATT2(GG, 128)                                                                          \
+    } else if (p.hs == 64) {                                                                       \
+        L2D_ATT2(GG, 64)                                                                           \
+    } else {                                                                                       \
+        L2D_ATT2(GG, 0)                                                                            \
+    }
     switch (p.G / p.gsplit) {
     case 1: L2D_ATT(1) break;
     case 2: L2D_ATT(2) break;
@@ -175,6 +185,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEven
     default: return hipErrorInvalidValue;
     }
 #undef L2D_ATT
+#undef L2D_ATT2
     return hipGetLastError();
 }
 
