@@ -445,7 +445,9 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
             if (v >= 1 && ctx->G % v == 0 && ctx->G / v >= 1) ctx->gsplit = v;
         }
         const int64_t nv = ctx->nkv * ctx->gsplit;
-        int64_t ns = ((int64_t)3 * cus + nv / 2) / nv;
+        int64_t per_cu = 3;
+        if (const char* e = getenv("L2D_ATTN_WG_PER_CU")) per_cu = atoi(e) > 0 ? atoi(e) : per_cu;
+        int64_t ns = (per_cu * cus + nv / 2) / nv;
         if (ns > 64) ns = 64;
         if (ns > (ctx->S + sc - 1) / sc) ns = (ctx->S + sc - 1) / sc;
         ctx->nsplit = (int)(ns < 1 ? 1 : ns);
