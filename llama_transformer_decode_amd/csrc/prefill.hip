@@ -734,7 +734,10 @@ struct PrefillMfmaWaveLds {
 };
 // after the chunk loop the same bytes hold the wavefront's partial result
 struct PrefillMfmaMerge {
-    double o[64][kPMHs / 16 * 4];  // [lane][4 * tile + register]
+    // [lane][4 * tile + register]; the row is padded by one double so that
+    // the lanes of a wavefront hit distinct banks (unpadded, every lane of a
+    // store or load fell on the same bank pair)
+    double o[64][kPMHs / 16 * 4 + 1];
     double m[kPMT], l[kPMT];       // per token
 };
 static_assert(sizeof(PrefillMfmaMerge) <= sizeof(PrefillMfmaWaveLds), "merge area");
