@@ -238,8 +238,8 @@ constexpr int kTR = 2, kTT = 4;  // 16 x 16 tiles per wavefront: rows, tokens
 // stays within an aligned block of 16 rows, so the 16 lanes of one operand
 // read still hit 16 distinct 16-byte bank groups, and each 16 lanes of a
 // staging write (8 parts times 2 quarters of the same row) hit 16 distinct
-// bank groups instead of one. Only for one 64-value part per
-// group: with 2 or 4 the index arithmetic made those instances spill.
+// bank groups instead of one. Only for one 64-value part per group: with 2
+// or 4 parts the index arithmetic made those instances spill.
 template <int U>
 __device__ __forceinline__ int gemm_swz(int part, int quarter) { return U == 1 ? ((quarter & 1) << 3) | (part & 7) : 0; }
 
