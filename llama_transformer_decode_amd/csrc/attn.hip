@@ -157,6 +157,34 @@ __global__ __launch_bounds__(kAThreads) void attention_kernel(AttnParams p)
     }
 }
 
+template <int KG, int HS>
+static int blocks_per_cu(size_t lds)
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_kernel<KG, HS>, kAThreads, lds) != hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int KG>
+static int blocks_per_cu_hs(int hs, size_t lds)
+{
+    return hs == 128 ? blocks_per_cu<KG, 128>(lds) : hs == 64 ? blocks_per_cu<KG, 64>(lds) : blocks_per_cu<KG, 0>(lds);
+}
+
+int attention_blocks_per_cu(int G, int gsplit, int hs)
+{
+    if (gsplit < 1 || G % gsplit) return 0;
+    const size_t lds = attention_lds_bytes(G, hs, 0);
+    switch (G / gsplit) {
+    case 1: return blocks_per_cu_hs<1>(hs, lds);
+    case 2: return blocks_per_cu_hs<2>(hs, lds);
+    case 4: return blocks_per_cu_hs<4>(hs, lds);
+    case 8: return blocks_per_cu_hs<8>(hs, lds);
+    default: return 0;
+    }
+}
+
 hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     if (p.nsplit > 64) return hipErrorInvalidValue;  // the merge takes at most 64 ranges

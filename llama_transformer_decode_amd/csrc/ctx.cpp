@@ -445,7 +445,12 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
             if (v >= 1 && ctx->G % v == 0 && ctx->G / v >= 1) ctx->gsplit = v;
         }
         const int64_t nv = ctx->nkv * ctx->gsplit;
+        // no more than can be resident at once: the 4-head instance (70B)
+        // fits two per CU, and sizing for three left a second round of
+        // workgroups (attention at pos 4095: 41.0 -> 33.3 us per layer)
         int64_t per_cu = 3;
+        const int resident = attention_blocks_per_cu((int)ctx->G, ctx->gsplit, (int)ctx->hs);
+        if (resident > 0 && resident < per_cu) per_cu = resident;
         if (const char* e = getenv("L2D_ATTN_WG_PER_CU")) per_cu = atoi(e) > 0 ? atoi(e) : per_cu;
         int64_t ns = (per_cu * cus + nv / 2) / nv;
         if (ns > 64) ns = 64;

@@ -105,6 +105,9 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s, const LaunchEven
 size_t attention_lds_bytes(int G, int hs, int unused);
 bool attention_supported(int G, int hs);
 int attention_positions_per_subchunk(int hs);
+// attention workgroups that can be resident on one CU for this shape (the
+// instance the launch would pick), or 0 if the runtime cannot tell
+int attention_blocks_per_cu(int G, int gsplit, int hs);
 
 // ---- batched prefill (prefill.hip)
 
