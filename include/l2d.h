@@ -110,6 +110,18 @@ int l2d_blob_parse(const void* blob, uint64_t nbytes, int32_t dtype, int32_t gro
  * Supported: dim and hidden_dim multiples of 4 (fp32: at most 16000);
  * head_size a multiple of 4 and <= 256; n_heads / n_kv_heads in {1, 2, 4, 8};
  * Q8_0 group size a power of two in [16, 256] dividing dim and hidden_dim.
+ * Launch-shape settings read from the environment here (tuning only; the
+ * results do not depend on them beyond the rounding noted):
+ *   L2D_GEMV_WG_PER_CU   matvec workgroups per CU (default 2; bit-identical)
+ *   L2D_ATTN_WG_PER_CU   attention workgroups per CU that size the position
+ *                        splits (default 3, capped by how many fit on a CU;
+ *                        another split changes the fp64 merge order)
+ *   L2D_ATTN_GSPLIT      workgroups sharing one kv head's query heads
+ *                        (default 2 when 8 query heads share one, else 1;
+ *                        bit-identical)
+ *   L2D_PREFILL_ATTN_VALU=1  batched prefill uses the vector attention kernel
+ *                        for every shape (comparison only; read at each
+ *                        prefill launch, not here)
  * Errors: L2D_EINVAL, L2D_ENOMEM (device memory), L2D_EHIP.
  */
 int l2d_init(const l2d_config* cfg, const l2d_weights* w, void* stream, l2d_ctx** out);
