@@ -19,10 +19,11 @@
 //   prefill_prep_kernel    RMSNorm (optional) + Q8_0 quantisation per token row
 //   prefill_gemm_kernel    int8 MFMA product + epilogue (q/k/v with RoPE and the
 //                          cache write, residual add, SwiGLU)
-//   prefill_attn_mfma_kernel  causal attention of 16 tokens of one head on the
-//                          fp64 matrix cores (one query head per kv head)
+//   prefill_attn_mfma_kernel  causal attention of 16 query rows (token, head)
+//                          of one kv head on the fp64 matrix cores (head
+//                          sizes that are multiples of 16, up to 128)
 //   prefill_attn_kernel    causal GQA attention of a block of tokens per kv head
-//                          (the other shapes)
+//                          (the other head sizes)
 #include <hip/hip_ext.h>
 #include <stdlib.h>
 
@@ -708,18 +709,20 @@ static int prefill_attn_rows(int G, int hs)
 bool prefill_attn_supported(int G, int hs) { return G >= 1 && prefill_attn_rows(G, hs) > 0; }
 
 // ---------------------------------------------------------------- attention on fp64 MFMA
-// One query head per kv head and a head size that is a multiple of 16 (up to
-// 128): a workgroup holds 16 query tokens of one head; its four wavefronts
+// A head size that is a multiple of 16 (up to 128): a workgroup holds 16
+// query rows of one kv head, each a (token, query head) pair of the G query
+// heads sharing it (16 tokens when G = 1, 2 tokens of all 8 heads when
+// G = 8); its four wavefronts
 // take every fourth chunk of 16 positions (so the long, late blocks are
 // spread over four SIMDs; two workgroups share a CU). Each computes
 // S = Q K^T and O += P V on v_mfma_f64_16x16x4f64 with the online softmax of
 // the vector path in fp64 (scaled fp64 scores, running maximum, fp64 exp,
 // fixed-order row sums). The four partial (m, l, O) are merged at the end in
 // a fixed order, as the decode step merges position ranges. q is converted to
-// fp64 once per token; K and V rows are staged through each wavefront's own
-// LDS. Operand rows are fed in the order 4*(i%4) + i/4, so register r of
-// lane l ends up with token 4*(l/16) + r (as in the fp64 prefill matmul).
-constexpr int kPMT = 16;            // query tokens per workgroup
+// fp64 once per query row; K and V rows are staged through each wavefront's
+// own LDS. Operand rows are fed in the order 4*(i%4) + i/4, so register r of
+// lane l ends up with query row 4*(l/16) + r (as in the fp64 prefill matmul).
+constexpr int kPMT = 16;            // query rows per workgroup
 constexpr int kPMC = 16;            // positions per chunk
 constexpr int kPMW = 4;             // wavefronts per workgroup (8 measured slower)
 constexpr int kPMHs = 128;          // largest head size
@@ -742,7 +745,10 @@ struct PrefillMfmaMerge {
 };
 static_assert(sizeof(PrefillMfmaMerge) <= sizeof(PrefillMfmaWaveLds), "merge area");
 
-static bool prefill_attn_mfma_ok(int G, int hs) { return G == 1 && hs % 16 == 0 && hs >= 16 && hs <= kPMHs; }
+static bool prefill_attn_mfma_ok(int G, int hs)
+{
+    return (G == 1 || G == 2 || G == 4 || G == 8) && hs % 16 == 0 && hs >= 16 && hs <= kPMHs;
+}
 
 // maximum / sum over each aligned group of 16 lanes, identical in every lane
 // of the group (quad swaps, half-row mirror, row mirror: each step combines
@@ -782,21 +788,30 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     PrefillMfmaWaveLds& L = ((PrefillMfmaWaveLds*)smem)[w];
     const int rl = lane % 16, ql = lane / 16;
     const int perm = 4 * (rl % 4) + rl / 4;
-    const int g = blockIdx.x;
-    const int t0 = (gridDim.y - 1 - blockIdx.y) * kPMT;  // the longest blocks first
-    const int tlast = min(t0 + kPMT, p.m) - 1;
-    const int plast = p.pos0 + tlast;  // the last position any token of the block sees
+    // the block's 16 operand rows are query rows R0 .. R0 + 15 of kv head g;
+    // row R is query head g * G + R % G of token R / G (all G query heads of
+    // a kv head share its K/V rows)
+    const int g = blockIdx.x, G = p.G;
+    const int R0 = (gridDim.y - 1 - blockIdx.y) * kPMT;  // the longest blocks first
+    const int tlast = min((R0 + kPMT - 1) / G, p.m - 1);
+    const int plast = p.pos0 + tlast;  // the last position any row of the block sees
     const int nch = plast / kPMC + 1;
     const double scale = 1.0 / sqrt((double)HS);
 
-    // Q operand of step ks: row rl, k ql = token t0 + perm, dimension 4 ks + ql.
-    // Tokens past the chunk read the query buffer's zeroed spare rows.
+    // Q operand of step ks: row rl, k ql = query row R0 + perm, dimension
+    // 4 ks + ql. Tokens past the chunk read the query buffer's zeroed spare
+    // rows (it holds whole 16-token tiles, and R0 + 15 < 16 * ceil(m / 16) * G).
     double qa[NKS];
     {
-        const float* qrow = p.q + (size_t)(t0 + perm) * p.d + (size_t)g * HS;
+        const int R = R0 + perm;
+        const float* qrow = p.q + (size_t)(R / G) * p.d + ((size_t)g * G + R % G) * HS;
 #pragma unroll
         for (int ks = 0; ks < NKS; ks++) qa[ks] = (double)qrow[4 * ks + ql];
     }
+    // causal limit of the rows this lane's registers hold: row R0 + 4 ql + r
+    int tpos[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) tpos[r] = p.pos0 + (R0 + 4 * ql + r) / G;
     v4d acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; j++) acc[j] = v4d{0.0, 0.0, 0.0, 0.0};
@@ -844,14 +859,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         const v4d sacc = s0 + s1;
 
-        // causal mask, online softmax; register r is token t0 + 4 ql + r,
+        // causal mask, online softmax; register r is query row R0 + 4 ql + r,
         // lane rl is position c*16 + rl
         const int pp = c * kPMC + rl;
         double pr[4], mn[4], ms[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int tpos = p.pos0 + t0 + 4 * ql + r;
-            const double sv = pp <= tpos ? sacc[r] * scale : -INFINITY;
+            const double sv = pp <= tpos[r] ? sacc[r] * scale : -INFINITY;
             mn[r] = fmax(mrun[r], row16_max(sv));
             // a token may see none of this wavefront's positions so far (its
             // first chunks lie past it): then every term is 0, not e^(-inf + inf)
@@ -930,8 +944,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 O += f * Mu->o[lane][4 * j + r];
                 Lsum += f * Mu->l[tk];
             }
-            const int t = t0 + tk;
-            if (t <= tlast) p.o[(size_t)t * p.d + (size_t)g * HS + 16 * j + rl] = (float)(O / Lsum);
+            const int R = R0 + tk, t = R / G;
+            if (t < p.m)
+                p.o[(size_t)t * p.d + ((size_t)g * G + R % G) * HS + 16 * j + rl] = (float)(O / Lsum);
         }
     }
 }
@@ -954,7 +969,7 @@ template <int NT, int W>
 static hipError_t launch_prefill_mfma(const PrefillAttnParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     if (hipError_t e = prefill_mfma_lds_attr<NT, W>(); e != hipSuccess) return e;
-    const dim3 grid((unsigned)p.nkv, (unsigned)((p.m + kPMT - 1) / kPMT));
+    const dim3 grid((unsigned)p.nkv, (unsigned)(((int64_t)p.m * p.G + kPMT - 1) / kPMT));
     const size_t lds = W * sizeof(PrefillMfmaWaveLds);
     if (ev)
         hipExtLaunchKernelGGL((prefill_attn_mfma_kernel<NT, W>), grid, dim3(64 * W), (uint32_t)lds, s, ev->start,
