@@ -25,6 +25,7 @@ pytestmark = pytest.mark.gpu
 
 TINY_Q8 = synth.Config("tinyq8", 128, 256, 3, 4, 2, 320, 64, 11, (synth.Q8_0,))
 GQA8_Q8 = synth.Config("gqa8q8", 256, 512, 2, 8, 1, 320, 96, 12, (synth.Q8_0,))
+GQA8_H128 = synth.Config("gqa8h128", 1024, 512, 2, 8, 1, 320, 96, 14, (synth.Q8_0,))  # head size 128, G = 8
 
 
 def _check_cache(ctx, orc, lo: int, hi: int, st: Stats):
@@ -78,7 +79,8 @@ def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0):
     (TINY_Q8, 64, [(0, 1)]),             # a single token
     (GQA8_Q8, 64, [(0, 50)]),            # G = 8: one token per block
     (GQA8_Q8, 256, [(0, 33), (33, 20)]),  # four parts per group; second call at pos 33
-], ids=["tiny-g2-gs64", "tiny-gs128", "tiny-one-token", "gqa8-gs64", "gqa8-gs256-two-calls"])
+    (GQA8_H128, 64, [(0, 45), (45, 20)]),  # the 70B attention shape: head size 128, G = 8
+], ids=["tiny-g2-gs64", "tiny-gs128", "tiny-one-token", "gqa8-gs64", "gqa8-gs256-two-calls", "gqa8-hs128-two-calls"])
 def test_prefill_small(cfg, gs, calls):
     cache_st, _ = _run(cfg, gs, calls)
     assert cache_st.exact / cache_st.n > 0.99
