@@ -108,7 +108,9 @@ int l2d_blob_parse(const void* blob, uint64_t nbytes, int32_t dtype, int32_t gro
  * HIP graph. stream: a hipStream_t to run on, or NULL for a stream the
  * context creates and owns. The host weights may be freed after return.
  * Supported: dim and hidden_dim multiples of 4 (fp32: at most 16000);
- * head_size a multiple of 4 and <= 256; n_heads / n_kv_heads in {1, 2, 4, 8};
+ * head_size one of 4, 8, 12, 16, 24, 32, 48, 64, 96, 128 (the attention
+ * kernel holds at most four float4 of a key row per lane);
+ * n_heads / n_kv_heads in {1, 2, 4, 8};
  * Q8_0 group size a power of two in [16, 256] dividing dim and hidden_dim.
  * Launch-shape settings read from the environment here (tuning only; the
  * results do not depend on them beyond the rounding noted):

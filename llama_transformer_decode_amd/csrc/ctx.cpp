@@ -63,13 +63,18 @@ static int check_supported(l2d_ctx* ctx, const l2d_config* c)
     const int hs = c->dim / c->n_heads;
     if (c->dim % 4 || c->hidden_dim % 4)
         return fail(ctx, L2D_EINVAL, "init: dim and hidden_dim must be multiples of 4");
-    if (hs % 4 || hs > 256) return fail(ctx, L2D_EINVAL, "init: head_size must be a multiple of 4 and <= 256");
+    if (hs % 4 || hs > 128) return fail(ctx, L2D_EINVAL, "init: head_size must be a multiple of 4 and <= 128");
     if (c->dtype == L2D_F32 && (c->dim > 16000 || c->hidden_dim > 16000))
         return fail(ctx, L2D_EINVAL, "init: fp32 matvec inputs are limited to 16000 values (64 KiB of LDS)");
     if (c->dim > 65536 || c->hidden_dim > 65536)
         return fail(ctx, L2D_EINVAL, "init: matvec inputs are limited to 65536 values");
-    if (!attention_supported(c->n_heads / c->n_kv_heads, hs))
-        return fail(ctx, L2D_EINVAL, "init: attention supports at most 8 query heads per kv head");
+    const int G = c->n_heads / c->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(ctx, L2D_EINVAL, "init: n_heads / n_kv_heads must be 1, 2, 4 or 8");
+    if (!attention_supported(G, hs))
+        return fail(ctx, L2D_EINVAL,
+                    "init: attention supports head sizes 4, 8, 12, 16, 24, 32, 48, 64, 96 and 128 "
+                    "(at most 4 float4 of a key row per lane)");
     return L2D_OK;
 }
 

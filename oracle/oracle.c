@@ -269,35 +269,45 @@ int or_threads(void)
 /* ---------------------------------------------------------- the method */
 
 /*
- * Q8_0 quantisation of a vector, group by group, as the quantize listing of
- * the gitcode porting guide (section "1. INT8 quantisation") computes it:
- * the group's largest |x| in float, scale = that max / 127 as a float
- * division, code = the float quotient x/scale rounded half away from zero
- * (C round) and cast to int8. A group whose max is 0 (the listing would
- * divide 0 by 0) gets scale 0 and codes 0. n must be a multiple of gs.
+ * Q8_0 (definition from the gitcode porting guide, section "1. INT8
+ * quantisation", and the hub page's quantisation section): a vector is cut
+ * into groups of gs consecutive values; a group stores one fp32 scale and gs
+ * int8 codes, and value i of the group stands for code_i * scale.
+ *
+ * The scale is the group's largest magnitude divided by 127 (an fp32
+ * division), so the largest value maps to +-127.
  */
+static float q80_scale_of(const float* v, int gs)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < gs; i++)
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+    return amax / 127.0f;
+}
+
+/*
+ * A code is the nearest integer to the fp32 quotient value / scale, halves
+ * rounded away from zero (C's round). A group of zeros has scale 0; its codes
+ * are 0 (the quotient would be 0/0).
+ */
+static int8_t q80_code_of(float v, float scale)
+{
+    if (scale == 0.0f) return 0;
+    const float quotient = v / scale;
+    return (int8_t)roundf(quotient);
+}
+
+/* Quantise n values (n a multiple of gs): codes q[n], scales s[n/gs]. */
 int or_quantize(const float* x, int64_t n, int gs, int8_t* q, float* s)
 {
     if (gs <= 0 || n < 0 || n % gs) return OR_EINVAL;
-    int64_t ng = n / gs;
+    const int64_t groups = n / gs;
     #pragma omp parallel for schedule(static)
-    for (int64_t g = 0; g < ng; g++) {
-        const float* xg = x + g * gs;
-        float wmax = 0.0f;
-        for (int i = 0; i < gs; i++) {
-            float a = fabsf(xg[i]);
-            if (a > wmax) wmax = a;
-        }
-        float scale = wmax / 127.0f;
+    for (int64_t g = 0; g < groups; g++) {
+        const float* v = x + g * gs;
+        const float scale = q80_scale_of(v, gs);
         s[g] = scale;
-        for (int i = 0; i < gs; i++) {
-            if (scale == 0.0f) {
-                q[g * gs + i] = 0;
-            } else {
-                float r = xg[i] / scale;
-                q[g * gs + i] = (int8_t)roundf(r);
-            }
-        }
+        for (int i = 0; i < gs; i++) q[g * gs + i] = q80_code_of(v[i], scale);
     }
     return OR_OK;
 }

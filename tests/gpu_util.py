@@ -2,6 +2,7 @@
 same seeded inputs and compare them element by element."""
 from __future__ import annotations
 
+import os
 import sys
 import time
 
@@ -16,8 +17,18 @@ RTOL = 1e-4
 MARGIN = 1e-3
 
 
+_PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+
+
 def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+    """Progress line to stderr and, when a gpurun_out/ folder exists at the
+    repository root, to gpurun_out/gpu_tests_progress.log (pytest captures
+    stderr; the file shows a long test's steps while it runs)."""
+    msg = " ".join(str(x) for x in a)
+    print(msg, file=sys.stderr, flush=True)
+    if os.path.isdir(_PROGRESS):
+        with open(os.path.join(_PROGRESS, "gpu_tests_progress.log"), "a") as f:
+            f.write(msg + "\n")
 
 
 def need_gpu():
@@ -40,10 +51,6 @@ def set_mode(ctx, mode: str):
     of per-phase kernels. Skips when the persistent kernel is unavailable."""
     if mode == "persistent":
         pytest.skip(PERSISTENT_SKIP)
-        try:
-            ctx.use_persistent(True)
-        except Exception as e:  # noqa: BLE001 - the library's error names the reason
-            pytest.skip(f"persistent step kernel unavailable: {e}")
     else:
         ctx.use_persistent(False)
         ctx.use_graph(True)

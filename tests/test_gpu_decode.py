@@ -6,14 +6,15 @@ to both, so one near-tie cannot fork the two runs; the GPU's own fused argmax
 is checked at every step whose oracle top-2 margin exceeds 1e-3. Logits must
 satisfy |gpu - oracle| <= 1e-3 + 1e-4 |oracle| everywhere.
 
-Full-size 7B and 70B shapes run a few steps from pos 0 and one step at a deep
-position whose cache slots 0..pos-1 hold the same synthetic keys and values
-on both sides (the KV-cache hook), so long-context attention, its position
-split and its merge are checked at the real shapes and launch configuration.
-
-Every check runs in both execution modes of the library: the persistent step
-kernel (one launch per step, the default) and the captured graph of
-per-phase kernels.
+Full-size workloads run the lengths the workloads state: the 7B Q8_0 model
+decodes pos 0..2048 and the 7B fp32 model pos 0..255, teacher-forced by the
+oracle's greedy trajectory computed in the same pass (one oracle step per
+position); the 70B Q8_0 model decodes pos 0..63 and then one step at each of
+pos 1024, 2048 and 4095 whose cache slots 0..pos-1 hold the same synthetic
+keys and values on both sides (the KV-cache hook), so long-context GQA
+attention, its position split and its merge are checked at the real shapes
+and launch configuration. The 13B shape and the 4-bit 7B step run a few
+steps plus injected deep positions.
 """
 import gc
 import time
@@ -235,12 +236,64 @@ def _full_size(name, dtype, deep_positions, steps=3):
         torch.cuda.empty_cache()
 
 
-def test_decode_7b_fp32_full_size():
-    _full_size("7B", synth.F32, [512, 2048])
+def _long_trajectory(name, dtype, n_steps, deep_positions=(), modes=("graph",)):
+    """Teacher-forced greedy decode of pos 0..n_steps-1 at full size: at each
+    pos the oracle's step gives the logits to compare and, by its argmax, the
+    token both sides take next (one oracle pass; the GPU step is enqueued
+    before the oracle's so the two overlap). Then one step at each deep
+    position over identical synthetic cache slots 0..pos-1."""
+    torch = need_gpu()
+    from gpu_util import Stats
+    cfg = synth.CONFIGS[name]
+    t = time.time()
+    blob = synth.make_blob(cfg, dtype)
+    log(f"  {name} dt{dtype}: blob {blob.size / 1e9:.2f} GB in {time.time() - t:.1f}s")
+    orc = oracle.Model(blob, dtype)
+    ctx = l2d.Context(blob, dtype)
+    try:
+        for mode in modes:
+            set_mode(ctx, mode)
+            ctx.reset_kv()
+            orc.reset_kv()
+            st = Stats()
+            tok = 1
+            t0 = t1 = time.time()
+            for p in range(n_steps):
+                ctx.forward(tok, p)
+                r = orc.forward(tok, p)
+                st.add(p, ctx.logits(), r, ctx.last_token())
+                tok = int(np.argmax(r))
+                if time.time() - t1 > 30:
+                    log(f"  [{name} dt{dtype} {mode}] pos {p} ({time.time() - t0:.0f}s): {st.summary()}")
+                    t1 = time.time()
+            log(f"  [{name} dt{dtype} {mode}] pos 0..{n_steps - 1}: {st.summary()}")
+            st.assert_ok()
+            assert st.steps == n_steps and st.argmax_checked > 0
+            for P in deep_positions:
+                _fill_kv_both(ctx, orc, P, seed=77 + P)
+                r = orc.forward(tok, P)
+                ctx.forward(tok, P)
+                sd = Stats()
+                sd.add(P, ctx.logits(), r, ctx.last_token())
+                log(f"  [{name} dt{dtype} {mode}] deep pos {P}: {sd.summary()}")
+                sd.assert_ok()
+    finally:
+        ctx.close()
+        orc.close()
+        del blob
+        gc.collect()
+        torch.cuda.empty_cache()
 
 
-def test_decode_7b_q8_full_size():
-    _full_size("7B", synth.Q8_0, [512, 2048])
+def test_decode_7b_fp32_trajectory():
+    """7B fp32: pos 0..255 (the logits tolerance after 256 steps), then deep
+    positions 512 and 2048 over injected caches."""
+    _long_trajectory("7B", synth.F32, 256, [512, 2048])
+
+
+def test_decode_7b_q8_trajectory():
+    """7B Q8_0: pos 0..2048, the decode length of the workload."""
+    _long_trajectory("7B", synth.Q8_0, 2049)
 
 
 def test_decode_7b_q4_full_size():
@@ -266,5 +319,7 @@ def test_decode_13b_fp32_full_size():
     _full_size("13B", synth.F32, [1024], steps=2)
 
 
-def test_decode_70b_q8_full_size():
-    _full_size("70B", synth.Q8_0, [4095], steps=2)
+def test_decode_70b_q8_trajectory():
+    """70B Q8_0 (GQA, 8 query heads per kv head): pos 0..63, then pos 1024,
+    2048 and 4095 over injected caches."""
+    _long_trajectory("70B", synth.Q8_0, 64, [1024, 2048, 4095])

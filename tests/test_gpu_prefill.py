@@ -4,14 +4,18 @@ token-by-token decode, through the C ABI: the K/V cache rows the prefill
 writes, the last token's logits and argmax, and the decode that continues
 from it on the device.
 
-Small models cover group sizes 64, 128 and 256, GQA ratios 1, 2 and 8 (token
-blocks of 4, 2 and 1 per attention workgroup), head sizes 8 to 128, ragged
-token counts, prompts longer than one 512-token chunk and prefill in two
-calls at pos0 > 0; the 7B shape runs at full size in both dtypes. Q8_0 is
+Small models cover group sizes 64, 128 and 256, GQA ratios 1, 2, 4 and 8,
+head sizes 8 to 128, ragged token counts, prompts longer than one 512-token
+chunk and prefill in two calls at pos0 > 0; the 7B shape runs at full size
+in both dtypes. Head sizes that are multiples of 16 take the matrix-core
+attention kernel (blocks of 16 (token, query head) rows); the others take
+the vector kernel, which L2D_PREFILL_ATTN_VALU=1 also selects for every
+shape, so both kernels are checked at every GQA ratio. Q8_0 is
 bit-identical by construction (same exact group dots, same fp64 order); fp32
 sums the same exact products in another fp64 order, like the decode step's
 fp32 GEMV, and is held to the logits tolerance."""
 import gc
+import os
 
 import numpy as np
 import pytest
@@ -26,6 +30,9 @@ pytestmark = pytest.mark.gpu
 TINY_Q8 = synth.Config("tinyq8", 128, 256, 3, 4, 2, 320, 64, 11, (synth.Q8_0,))
 GQA8_Q8 = synth.Config("gqa8q8", 256, 512, 2, 8, 1, 320, 96, 12, (synth.Q8_0,))
 GQA8_H128 = synth.Config("gqa8h128", 1024, 512, 2, 8, 1, 320, 96, 14, (synth.Q8_0,))  # head size 128, G = 8
+GQA4_H64 = synth.Config("gqa4h64", 512, 512, 2, 8, 2, 320, 96, 15, (synth.Q8_0,))  # head size 64, G = 4
+GQA4_H32 = synth.Config("gqa4h32", 256, 512, 2, 8, 2, 320, 80, 16, (synth.Q8_0,))  # head size 32, G = 4
+MHA_H64 = synth.Config("mhah64", 256, 512, 2, 4, 4, 320, 80, 17, (synth.Q8_0,))  # head size 64, G = 1
 
 
 def _check_cache(ctx, orc, lo: int, hi: int, st: Stats):
@@ -34,10 +41,21 @@ def _check_cache(ctx, orc, lo: int, hi: int, st: Stats):
     st.add("v", vc[:, lo:hi].cpu().numpy(), orc.value_cache()[:, lo:hi])
 
 
-def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0):
+def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0, valu: bool = False):
     """calls: list of (start, n) prefill calls over one prompt; then `cont`
-    greedy decode steps on the device, teacher-checked against the oracle."""
+    greedy decode steps on the device, teacher-checked against the oracle.
+    valu: run the prefill with the vector attention kernel for every shape
+    (L2D_PREFILL_ATTN_VALU=1, read at each prefill launch)."""
     torch = need_gpu()
+    if valu:
+        os.environ["L2D_PREFILL_ATTN_VALU"] = "1"
+    try:
+        return _run_inner(cfg, gs, calls, cont, dtype, torch)
+    finally:
+        os.environ.pop("L2D_PREFILL_ATTN_VALU", None)
+
+
+def _run_inner(cfg, gs, calls, cont, dtype, torch):
     total = sum(n for _, n in calls)
     tokens = synth.prompt(cfg.seed + 500, total, abs(cfg.vocab))
     blob = synth.make_blob(cfg, dtype, gs=gs)
@@ -80,9 +98,25 @@ def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0):
     (GQA8_Q8, 64, [(0, 50)]),            # G = 8: one token per block
     (GQA8_Q8, 256, [(0, 33), (33, 20)]),  # four parts per group; second call at pos 33
     (GQA8_H128, 64, [(0, 45), (45, 20)]),  # the 70B attention shape: head size 128, G = 8
-], ids=["tiny-g2-gs64", "tiny-gs128", "tiny-one-token", "gqa8-gs64", "gqa8-gs256-two-calls", "gqa8-hs128-two-calls"])
+    (GQA4_H64, 64, [(0, 38), (38, 21)]),  # G = 4 on the matrix cores: 4 tokens x 4 heads per block
+    (GQA4_H32, 64, [(0, 29), (29, 18)]),  # G = 4, head size 32
+], ids=["tiny-g2-gs64", "tiny-gs128", "tiny-one-token", "gqa8-gs64", "gqa8-gs256-two-calls", "gqa8-hs128-two-calls",
+        "gqa4-hs64-two-calls", "gqa4-hs32-two-calls"])
 def test_prefill_small(cfg, gs, calls):
     cache_st, _ = _run(cfg, gs, calls)
+    assert cache_st.exact / cache_st.n > 0.99
+
+
+@pytest.mark.parametrize("cfg,calls", [
+    (MHA_H64, [(0, 33), (33, 14)]),       # G = 1: blocks of 4 tokens
+    (TINY_Q8, [(0, 41)]),                 # G = 2: blocks of 2 tokens
+    (GQA4_H64, [(0, 38), (38, 21)]),      # G = 4: one token of 4 heads per block
+    (GQA8_H128, [(0, 45), (45, 20)]),     # G = 8: one token per block
+], ids=["g1-hs64", "g2-hs32", "g4-hs64", "g8-hs128"])
+def test_prefill_vector_attention(cfg, calls):
+    """The vector attention kernel at every GQA ratio, on shapes the
+    matrix-core kernel would otherwise take (L2D_PREFILL_ATTN_VALU=1)."""
+    cache_st, _ = _run(cfg, 64, calls, valu=True)
     assert cache_st.exact / cache_st.n > 0.99
 
 

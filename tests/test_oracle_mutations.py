@@ -30,8 +30,9 @@ MUTATIONS = {
                                "for (int64_t t = 0; t < pos; t++) {\n            const float* kt"),
     "rmsnorm_eps_dropped": ("ss / (double)n + 1e-5", "ss / (double)n"),
     "rmsnorm_sum_not_mean": ("ss / (double)n + 1e-5", "ss + 1e-5"),
-    "quant_half_even": ("q[g * gs + i] = (int8_t)roundf(r);", "q[g * gs + i] = (int8_t)rintf(r);"),
-    "quant_scale_255": ("float scale = wmax / 127.0f;", "float scale = wmax / 255.0f;"),
+    "quant_half_even": ("return (int8_t)roundf(quotient);", "return (int8_t)rintf(quotient);"),
+    "quant_scale_255": ("return amax / 127.0f;", "return amax / 255.0f;"),
+    "quant_truncates": ("return (int8_t)roundf(quotient);", "return (int8_t)quotient;"),
     "q8_act_scale_dropped": ("acc += (double)dot * (double)sr[g] * (double)as[g];",
                              "acc += (double)dot * (double)sr[g];"),
     "swiglu_branches_swapped": ("double z = m->h1[i];", "double z = m->h3[i];"),
