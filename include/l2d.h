@@ -309,24 +309,56 @@ int l2d_use_graph(l2d_ctx* ctx, int32_t enable);
 
 /*
  * The same step as one persistent kernel: a single cooperative launch per
- * l2d_forward / l2d_forward_greedy, its phases separated by grid barriers
- * (the toy forward pass of the mht18 essay, section 2.3, computed as above;
- * results agree with the per-phase kernels within fp64 summation order).
- * Available only when the environment variable L2D_PERSISTENT=1 is set at
- * l2d_init (its first run on MI355X faulted and the cause is not yet found),
- * for Q8_0 with group size 64 or fp32, head_size <= 256, at most 8 query
- * heads per kv head, and a device that can hold one 512-thread workgroup per
- * CU with the step's LDS. enable = 1 where it is not available returns
- * L2D_EINVAL. A grid barrier that waits beyond a bounded
- * number of polls (seconds) gives up: every workgroup then ends, and the next
- * l2d_sync, l2d_last_token or l2d_read_logits returns L2D_EHIP and resets the
- * barrier state. Tracing (l2d_trace_layer) uses the per-phase kernels.
+ * l2d_forward / l2d_forward_greedy (the toy forward pass of the mht18 essay,
+ * section 2.3, every phase computed as above, with the same arithmetic and
+ * order, so the results equal the per-phase kernels' bit for bit). Worker
+ * waves stream the weights through all matvec phases without a break;
+ * control waves run the grid barriers, prologues, epilogues and attention.
+ * Available for Q8_0 with group size 64 on a device with cooperative launch
+ * that can hold one workgroup per CU (dim <= 16384, hidden_dim <= 65536,
+ * the head sizes l2d_init takes); enable = 1 elsewhere returns L2D_EINVAL.
+ * A grid barrier that waits beyond a bounded number of polls (seconds)
+ * gives up: every workgroup then ends, and the next l2d_sync,
+ * l2d_last_token or l2d_read_logits returns L2D_EHIP and resets the barrier
+ * state. Tracing (l2d_trace_layer) uses the per-phase kernels. Off by
+ * default.
  */
 int l2d_use_persistent(l2d_ctx* ctx, int32_t enable);
+
+/*
+ * Diagnostics of the persistent step kernel: run one step at (token, pos)
+ * with it, recording the device's real-time clock (100 MHz ticks) at each
+ * workgroup's control events and at each worker's phase reports. *events
+ * receives E = 1 + 6 (4 n_layers + 1), the control events per workgroup.
+ * host (n uint64) receives, for G workgroups (one per CU) and W worker
+ * waves each: [G][E] control stamps (event 0: step start; for phase p, in
+ * step order q/k/v, output, w1/w3, w2 per layer, then the classifier:
+ * 1 + 6p input preparation starts, 2 + 6p input published, 3 + 6p all
+ * workers done, 4 + 6p results stored, 5 + 6p grid barrier passed, 6 + 6p
+ * (q/k/v phases) attention done), then [G][W][4 n_layers + 1] worker report
+ * stamps; 0 where an event did not occur. host NULL: only *events is set.
+ * Synchronous; L2D_EINVAL when n is too small or the kernel is not
+ * available.
+ */
+int l2d_stream_trace(l2d_ctx* ctx, int32_t token, int32_t pos, uint64_t* host, int64_t n, int64_t* events);
 
 /* 1 when l2d_forward runs the persistent step kernel, 0 when the per-phase
  * kernels run, L2D_EINVAL for a null context. */
 int l2d_persistent(const l2d_ctx* ctx);
+
+/*
+ * Test hook, host only (no device is touched): run the persistent step
+ * kernel's plan for the model cfg (Q8_0, group size 64) and a launch of nwg
+ * workgroups on the host, with the same functions the kernel computes its
+ * addresses with: every worker wave's weight stream (phase order, rows,
+ * chunks, code and scale offsets inside their arrays), every row of every
+ * matrix streamed exactly once, workgroup row ranges tiling each matrix,
+ * attention position ranges covering 0..pos exactly for every pos, partial
+ * slots inside their allocation, LDS within 160 KiB. Returns 0 ("ok" in
+ * msg) or L2D_EINVAL with the first problem in msg (msglen bytes, NUL
+ * terminated).
+ */
+int l2d_stream_plan_check(const l2d_config* cfg, int32_t nwg, char* msg, int32_t msglen);
 
 #ifdef __cplusplus
 }

@@ -98,6 +98,10 @@ def lib():
             "l2d_stream": (_vp, [_vp]),
             "l2d_profile_step": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.POINTER(ctypes.c_double)]),
+            "l2d_stream_plan_check": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_char_p,
+                                                     ctypes.c_int32]),
+            "l2d_stream_trace": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
+                                                ctypes.POINTER(ctypes.c_int64)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -112,7 +116,8 @@ EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l
            "l2d_last_token", "l2d_read_logits", "l2d_quantize_q80", "l2d_reset_kv", "l2d_free",
            "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
-           "l2d_set_sampling", "l2d_prefill", "l2d_profile_prefill")
+           "l2d_set_sampling", "l2d_prefill", "l2d_profile_prefill", "l2d_stream_plan_check",
+           "l2d_stream_trace")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
 PREFILL_CLASSES = ("prep", "qkv", "attn", "wo", "w13", "w2", "start", "cls")
@@ -275,9 +280,23 @@ class Context:
         _check(lib().l2d_set_sampling(self._h, float(temperature), int(seed) & (2**64 - 1)), self._h)
 
     def use_persistent(self, enable: bool):
-        """Run each step as the one persistent kernel (True) or as the
-        per-phase kernels (False)."""
+        """Run each step as the one persistent step kernel (True; Q8_0 with
+        group size 64) or as the captured graph of per-phase kernels (False)."""
         _check(lib().l2d_use_persistent(self._h, 1 if enable else 0), self._h)
+
+    def stream_trace(self, token: int, pos: int, workgroups: int, workers: int):
+        """One persistent-kernel step with clock stamps: (control [G][E],
+        worker reports [G][W][phases]) in 100 MHz ticks."""
+        ev = ctypes.c_int64()
+        _check(lib().l2d_stream_trace(self._h, 0, 0, None, 0, ctypes.byref(ev)), self._h)
+        E = ev.value
+        NP = 4 * self.n_layers + 1
+        n = workgroups * (E + workers * NP)
+        buf = np.zeros(n, dtype=np.uint64)
+        _check(lib().l2d_stream_trace(self._h, int(token), int(pos), _np_ptr(buf), n, ctypes.byref(ev)), self._h)
+        ctl = buf[:workgroups * E].reshape(workgroups, E)
+        wk = buf[workgroups * E:].reshape(workgroups, workers, NP)
+        return ctl, wk
 
     @property
     def persistent(self) -> bool:
@@ -294,6 +313,20 @@ class Context:
         s = np.empty(n // self.group_size, dtype=np.float32)
         _check(lib().l2d_trace_read(self._h, slot, _np_ptr(q), _np_ptr(s)), self._h)
         return q, s
+
+
+def stream_plan_check(header, nwg: int, group_size: int = 64) -> str:
+    """Run the persistent step kernel's plan (every worker's weight stream,
+    row ownership, attention ranges, LDS size) on the host for a launch of
+    nwg workgroups; returns "ok" or raises L2DError naming the first problem.
+    header: the seven blob-header fields. Host only: no device is touched."""
+    cfg = Config(*header, 1, group_size, 10000.0, 1e-5)
+    buf = ctypes.create_string_buffer(512)
+    rc = lib().l2d_stream_plan_check(ctypes.byref(cfg), int(nwg), buf, 512)
+    msg = buf.value.decode()
+    if rc != OK:
+        raise L2DError(rc, msg)
+    return msg
 
 
 def quantize_q80(x, gs: int = 64, stream=None):

@@ -66,7 +66,7 @@ __host__ __device__ inline AttnShape attn_shape(int hs)
 }
 
 template <int NT>
-inline size_t attn_core_lds_bytes(int G, int hs)
+__host__ __device__ inline size_t attn_core_lds_bytes(int G, int hs)
 {
     const AttnShape a = attn_shape<NT>(hs);
     const size_t q = (((size_t)G * hs * 4) + 15) & ~(size_t)15;
@@ -167,11 +167,16 @@ struct AttnLds {
     }
 };
 
-// The range computation; ends with a __syncthreads after which red, m_run
-// and l_run hold the result. KV rows of the first two sub-chunks come from
-// pre (loaded by the caller with load_kv when has_pre, else here).
-template <int KG, int NT>
-__device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* smem)
+// Barrier of the NT threads running a range: the whole workgroup by default.
+struct BlockSync {
+    __device__ __forceinline__ void operator()() const { __syncthreads(); }
+};
+
+// The range computation; ends with a barrier (sync) after which red, m_run
+// and l_run hold the result. sync synchronises the NT threads that run it
+// (the workgroup, or a group of its waves).
+template <int KG, int NT, class Sync = BlockSync>
+__device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* smem, Sync sync = Sync())
 {
     constexpr int G = KG;
     const int hs = r.hs;
@@ -196,7 +201,7 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
         L.m_run[tid] = -INFINITY;
         L.l_run[tid] = 0.0;
     }
-    __syncthreads();
+    sync();
 
     const double scale = 1.0 / sqrt((double)hs);
     const int vf = tid % a.F, vslot = tid / a.F;
@@ -233,7 +238,7 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
                 for (int h = 0; h < KG; h++)
                     L.sc[(size_t)h * a.sc + tl] = t0 + tl <= r.last0 + h / r.Gt ? sv[h] * scale : -INFINITY;
         }
-        __syncthreads();
+        sync();
         for (int h = wave; h < G; h += NT / kWave) {
             double mx = -INFINITY;
             for (int t = lane; t < m; t += kWave) mx = fmax(mx, L.sc[(size_t)h * a.sc + t]);
@@ -254,7 +259,7 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
                 L.m_run[h] = mn;
             }
         }
-        __syncthreads();
+        sync();
         // values
         if (vslot < a.slots) {
 #pragma unroll
@@ -281,7 +286,7 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
                 }
             }
         }
-        __syncthreads();
+        sync();
         // refill the buffer just consumed with the sub-chunk after next
         if (s + 2 < nsub) load_kv<NT>(cur, r, a, t0 + 2 * a.sc, min(a.sc, n - (s + 2) * a.sc));
     };
@@ -320,7 +325,7 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
             rr[3] = aw[h];
         }
     }
-    __syncthreads();
+    sync();
 }
 
 // unnormalised value sum of element e (of G*hs) after attn_range, in a fixed order

@@ -12,6 +12,7 @@
 #include "internal.hpp"
 #include "l2d.h"
 #include "runtime.hpp"
+#include "stream_plan.hpp"
 
 namespace {
 
@@ -334,7 +335,7 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
     return enqueue_classifier(ctx, kt, KC_CLS);
 }
 
-int setup_mega(l2d_ctx* ctx, int cus);
+int setup_stream(l2d_ctx* ctx, int cus);
 
 int capture(l2d_ctx* ctx)
 {
@@ -578,57 +579,61 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     rc = capture(ctx);
     if (rc != L2D_OK) return rc;
-    return setup_mega(ctx, cus);
+    return setup_stream(ctx, cus);
 }
 
-// The persistent step kernel: one workgroup per CU, all resident
-// (cooperative launch), LDS for the largest matvec input or attention
-// range. It is built but not enabled: its first run on MI355X ended in a
-// memory access fault whose cause has not been found, so the library runs
-// the captured graph of per-phase kernels unless L2D_PERSISTENT=1 is set in
-// the environment at l2d_init.
-int setup_mega(l2d_ctx* ctx, int cus)
+// The persistent step kernel (Q8_0, group size 64): one workgroup per CU,
+// all resident (cooperative launch). Its attention items: the query heads of
+// a kv head split over gsplit items when 8 share one (as in the per-phase
+// attention kernel), and about one item per workgroup over the position
+// splits.
+int setup_stream(l2d_ctx* ctx, int cus)
 {
-    ctx->mega_ok = false;
-    ctx->use_mega = false;
-    const char* e = getenv("L2D_PERSISTENT");
-    if (!e || atoi(e) != 1) return L2D_OK;
-    if (!mega_supported(ctx->dt, ctx->gs, ctx->d, ctx->h, (int)ctx->G, (int)ctx->hs)) return L2D_OK;
+    ctx->stream_ok = false;
+    ctx->use_stream = false;
+    const int gsplit = ctx->G == 8 ? 2 : 1;
+    if (!stream_supported(ctx->dt, ctx->gs, ctx->d, ctx->h, (int)ctx->G, gsplit, (int)ctx->hs)) return L2D_OK;
     int coop = 0;
     HIP_TRY(ctx, hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, ctx->device));
     if (!coop) return L2D_OK;
-    const size_t lds = mega_lds_bytes(ctx->dt, ctx->d, ctx->h, (int)ctx->G, (int)ctx->hs);
-    if (mega_blocks_per_cu(ctx->dt, (int)ctx->G, lds) < 1) return L2D_OK;
-    ALLOC(ctx->msync, sizeof(MegaSync));
-    ALLOC(ctx->head_ctr, (size_t)ctx->nkv * 32 * 4);
-    const size_t nparts = (size_t)ctx->nkv * kMegaSplits * ctx->G;
-    ALLOC(ctx->mpart_o, nparts * ctx->hs * 8);
-    ALLOC(ctx->mpart_ml, nparts * 2 * 8);
-    HIP_TRY(ctx, hipMemsetAsync(ctx->msync, 0, sizeof(MegaSync), ctx->stream));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->head_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    const int kg = (int)ctx->G / gsplit;
+    SPlan sp{ctx->d, ctx->h, ctx->L, ctx->kvd, ctx->V, cus, stream_workers(), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const size_t lds = stream_lds_bytes(sp, kg, (int)ctx->hs);
+    if (stream_blocks_per_cu(kg, (int)ctx->hs, lds) < 1) return L2D_OK;
+    const int64_t cols = ctx->nkv * gsplit;
+    const int64_t ns = stream_splits(ctx->nkv, gsplit, cus, ctx->S, (int)ctx->hs);
+    ALLOC(ctx->ssync, sizeof(StreamSync));
+    ALLOC(ctx->shead_ctr, (size_t)cols * 32 * 4);
+    ALLOC(ctx->spart_o, (size_t)cols * ns * kg * ctx->hs * 8);
+    ALLOC(ctx->spart_ml, (size_t)cols * ns * kg * 2 * 8);
+    ALLOC(ctx->sdummy, 8192);
+    HIP_TRY(ctx, hipMemsetAsync(ctx->ssync, 0, sizeof(StreamSync), ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->shead_ctr, 0, (size_t)cols * 32 * 4, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->sdummy, 0, 8192, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    ctx->mega_grid = cus;
-    ctx->mega_lds = lds;
-    ctx->mega_epoch = 0;
-    ctx->mega_ok = true;
-    ctx->use_mega = true;
+    ctx->stream_grid = cus;
+    ctx->stream_kg = kg;
+    ctx->stream_gsplit = gsplit;
+    ctx->stream_nsplit = (int)ns;
+    ctx->stream_ymax = (int)sp_max_wg_rows(sp);
+    ctx->stream_lds = lds;
+    ctx->stream_epoch = 0;
+    ctx->stream_ok = true;
     return L2D_OK;
 }
 
 // One launch of the persistent step kernel for (token, pos).
 hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
 {
-    const uint32_t nb = mega_barriers((int)ctx->L);
-    if (ctx->mega_epoch > (1u << 25) - nb) {
+    const uint32_t nb = stream_barriers((int)ctx->L);
+    if (ctx->stream_epoch > (1u << 25) - nb) {
         // the arrival counters count up across launches: restart them from zero
-        hipError_t e = hipMemsetAsync(ctx->msync, 0, sizeof(MegaSync), ctx->stream);
+        hipError_t e = hipMemsetAsync(ctx->ssync, 0, sizeof(StreamSync), ctx->stream);
         if (e != hipSuccess) return e;
-        ctx->mega_epoch = 0;
+        ctx->stream_epoch = 0;
     }
-    MegaParams p;
+    StreamParams p;
     memset(&p, 0, sizeof(p));
-    p.dt = ctx->dt;
-    p.gs = ctx->gs;
     p.d = (int32_t)ctx->d;
     p.h = (int32_t)ctx->h;
     p.L = (int32_t)ctx->L;
@@ -638,18 +643,22 @@ hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool gre
     p.G = (int32_t)ctx->G;
     p.V = (int32_t)ctx->V;
     p.S = (int32_t)ctx->S;
+    p.nsplit = ctx->stream_nsplit;
+    p.gsplit = ctx->stream_gsplit;
+    p.ymax = ctx->stream_ymax;
+    p.kmax = (int32_t)(ctx->d > ctx->h ? ctx->d : ctx->h);
     p.eps = ctx->cfg.norm_eps;
-    p.emb = ctx->emb;
+    p.emb = (const int8_t*)ctx->emb;
     p.emb_s = ctx->emb_s;
-    p.wqkv = ctx->wqkv;
+    p.wqkv = (const int8_t*)ctx->wqkv;
     p.wqkv_s = ctx->wqkv_s;
-    p.wo = ctx->wo;
+    p.wo = (const int8_t*)ctx->wo;
     p.wo_s = ctx->wo_s;
-    p.w13 = ctx->w13;
+    p.w13 = (const int8_t*)ctx->w13;
     p.w13_s = ctx->w13_s;
-    p.w2 = ctx->w2;
+    p.w2 = (const int8_t*)ctx->w2;
     p.w2_s = ctx->w2_s;
-    p.wcls = ctx->wcls;
+    p.wcls = (const int8_t*)ctx->wcls;
     p.wcls_s = ctx->wcls_s;
     p.rms_att = ctx->rms_att;
     p.rms_ffn = ctx->rms_ffn;
@@ -664,38 +673,51 @@ hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool gre
     p.logits = ctx->logits;
     p.step = ctx->step;
     p.argmax = ctx->argmax;
-    p.part_o = ctx->mpart_o;
-    p.part_ml = ctx->mpart_ml;
-    p.head_ctr = ctx->head_ctr;
-    p.sync = ctx->msync;
+    p.part_o = ctx->spart_o;
+    p.part_ml = ctx->spart_ml;
+    p.head_ctr = ctx->shead_ctr;
+    p.sync = ctx->ssync;
+    p.dummy = ctx->sdummy;
+    {
+        const int8_t* const codes[5] = {p.wqkv, p.wo, p.w13, p.w2, p.wcls};
+        const float* const scales[5] = {p.wqkv_s, p.wo_s, p.w13_s, p.w2_s, p.wcls_s};
+        p.wbase = p.wqkv;
+        for (int k = 0; k < 5; k++) {
+            p.wofs[k] = (int64_t)((intptr_t)codes[k] - (intptr_t)p.wbase);
+            p.sofs[k] = (int64_t)((intptr_t)scales[k] - (intptr_t)p.wbase);
+        }
+    }
     p.token = token;
     p.pos = pos;
     p.greedy = greedy ? 1 : 0;
-    p.epoch0 = ctx->mega_epoch;
+    p.epoch0 = ctx->stream_epoch;
     p.temperature = ctx->temperature;
     p.seed = ctx->seed;
-    hipError_t e = launch_mega(p, ctx->mega_grid, ctx->mega_lds, ctx->stream);
+    p.trace = ctx->strace;
+    p.trace_n = stream_trace_events((int)ctx->L);
+    hipError_t e = launch_stream(p, ctx->stream_kg, ctx->stream_grid, ctx->stream_lds, ctx->stream);
     if (e == hipSuccess) {
-        ctx->mega_epoch += nb;
-        ctx->mega_pending = true;
+        ctx->stream_epoch += nb;
+        ctx->stream_pending = true;
     }
     return e;
 }
 
-// After a synchronisation: did a grid barrier of the step kernel give up?
-// Then the barrier state is reset and the error reported.
-int mega_check(l2d_ctx* ctx)
+// After a synchronisation: did a wait of the step kernel give up? Then the
+// barrier state is reset and the error reported.
+int stream_check(l2d_ctx* ctx)
 {
-    if (!ctx->mega_pending) return L2D_OK;
+    if (!ctx->stream_pending) return L2D_OK;
     uint32_t err = 0;
-    HIP_TRY(ctx, hipMemcpyAsync(&err, ctx->msync->err, 4, hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(ctx, hipMemcpyAsync(&err, ctx->ssync->err, 4, hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    ctx->mega_pending = false;
+    ctx->stream_pending = false;
     if (err == 0) return L2D_OK;
-    HIP_TRY(ctx, hipMemsetAsync(ctx->msync, 0, sizeof(MegaSync), ctx->stream));
-    HIP_TRY(ctx, hipMemsetAsync(ctx->head_ctr, 0, (size_t)ctx->nkv * 32 * 4, ctx->stream));
+    const int64_t cols = ctx->nkv * ctx->stream_gsplit;
+    HIP_TRY(ctx, hipMemsetAsync(ctx->ssync, 0, sizeof(StreamSync), ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->shead_ctr, 0, (size_t)cols * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    ctx->mega_epoch = 0;
+    ctx->stream_epoch = 0;
     return fail(ctx, L2D_EHIP, "step kernel: a grid barrier wait gave up; the step's results are invalid");
 }
 
@@ -742,7 +764,7 @@ const float* forward_impl(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
         return nullptr;
     }
     const bool tracing = ctx->trace_layer >= 0;
-    if (ctx->use_mega && ctx->mega_ok && !tracing) {
+    if (ctx->use_stream && ctx->stream_ok && !tracing) {
         hipError_t e = launch_step_kernel(ctx, token, pos, greedy);
         if (e != hipSuccess) {
             fail(ctx, L2D_EHIP, std::string("step kernel launch: ") + hipGetErrorString(e));
@@ -804,7 +826,7 @@ int l2d_sync(l2d_ctx* ctx)
 {
     if (!ctx) return fail(nullptr, L2D_EINVAL, "sync: null context");
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    return mega_check(ctx);
+    return stream_check(ctx);
 }
 
 int l2d_last_token(l2d_ctx* ctx, int32_t* token)
@@ -815,7 +837,7 @@ int l2d_last_token(l2d_ctx* ctx, int32_t* token)
     HIP_TRY(ctx, hipMemcpyAsync(slots, ctx->argmax + (size_t)(ctx->last_pos & 1) * kArgmaxSlots * kArgmaxStride,
                                 sizeof(slots), hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    int rc = mega_check(ctx);
+    int rc = stream_check(ctx);
     if (rc != L2D_OK) return rc;
     unsigned long long v = 0;
     for (int i = 0; i < kArgmaxSlots; i++)
@@ -830,7 +852,7 @@ int l2d_read_logits(l2d_ctx* ctx, float* host_dst)
     HIP_TRY(ctx, hipMemcpyAsync(host_dst, ctx->logits, (size_t)ctx->V * 4, hipMemcpyDeviceToHost,
                                 ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
-    return mega_check(ctx);
+    return stream_check(ctx);
 }
 
 int l2d_quantize_q80(const float* x, int64_t n, int32_t gs, int8_t* q, float* s, void* stream)
@@ -1254,16 +1276,46 @@ int l2d_set_sampling(l2d_ctx* ctx, double temperature, uint64_t seed)
 int l2d_use_persistent(l2d_ctx* ctx, int32_t enable)
 {
     if (!ctx) return fail(nullptr, L2D_EINVAL, "use_persistent: null context");
-    if (enable && !ctx->mega_ok)
-        return fail(ctx, L2D_EINVAL, "use_persistent: the persistent step kernel is not available for this model or device");
-    ctx->use_mega = enable != 0;
+    if (enable && !ctx->stream_ok)
+        return fail(ctx, L2D_EINVAL,
+                    "use_persistent: the persistent step kernel is built for Q8_0 with group size 64 "
+                    "on a device with cooperative launch; not available for this model or device");
+    ctx->use_stream = enable != 0;
     return L2D_OK;
 }
 
 int l2d_persistent(const l2d_ctx* ctx)
 {
     if (!ctx) return fail(nullptr, L2D_EINVAL, "persistent: null context");
-    return ctx->use_mega && ctx->mega_ok ? 1 : 0;
+    return ctx->use_stream && ctx->stream_ok ? 1 : 0;
+}
+
+int l2d_stream_trace(l2d_ctx* ctx, int32_t token, int32_t pos, uint64_t* host, int64_t n, int64_t* events)
+{
+    if (!ctx || !events) return fail(ctx, L2D_EINVAL, "stream_trace: null argument");
+    if (!ctx->stream_ok) return fail(ctx, L2D_EINVAL, "stream_trace: the persistent step kernel is not available");
+    const int64_t ne = stream_trace_events((int)ctx->L);
+    const int64_t NP = 4 * ctx->L + 1;
+    const int64_t total = (int64_t)ctx->stream_grid * (ne + stream_workers() * NP);
+    *events = ne;
+    if (!host) return L2D_OK;  // size query
+    if (n < total) return fail(ctx, L2D_EINVAL, "stream_trace: host buffer too small");
+    uint64_t* dev = nullptr;
+    HIP_TRY(ctx, hipMalloc(&dev, (size_t)total * 8));
+    hipError_t me = hipMemsetAsync(dev, 0, (size_t)total * 8, ctx->stream);
+    const bool was = ctx->use_stream;
+    ctx->use_stream = true;
+    ctx->strace = dev;
+    const float* r = me == hipSuccess ? forward_impl(ctx, token, pos, false) : nullptr;
+    ctx->strace = nullptr;
+    ctx->use_stream = was;
+    int rc = r ? l2d_sync(ctx) : L2D_EHIP;
+    if (rc == L2D_OK) {
+        hipError_t e = hipMemcpy(host, dev, (size_t)total * 8, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) rc = fail(ctx, L2D_EHIP, std::string("stream_trace: ") + hipGetErrorString(e));
+    }
+    hipFree(dev);
+    return rc;
 }
 
 int l2d_use_graph(l2d_ctx* ctx, int32_t enable)

@@ -197,34 +197,37 @@ hipError_t launch_quantize(const float* x, int64_t n, int32_t gs, int8_t* q, flo
                            hipStream_t st);
 
 // ---------------------------------------------------------------- step kernel
-// The whole decode step as one persistent cooperative kernel (mega.hip).
+// The whole Q8_0 decode step as one persistent cooperative kernel
+// (stream.hip): worker waves stream the weights, control waves run the grid
+// barriers, prologues, epilogues and attention.
 
-// Grid barrier state: arrival counters per XCD (workgroup b belongs to group
-// b % 8), each on its own 128-byte line, counting up across launches; and an
-// error word set when a wait gives up.
-struct MegaSync {
+// Grid barrier state: arrival counters per XCD (workgroup b counts on
+// counter b % 8), each on its own 128-byte line, counting up across
+// launches; and an error word set when a wait gives up.
+struct StreamSync {
     uint32_t arrive[8][32];
     uint32_t err[32];
 };
 
-// largest number of position ranges per kv head in the step kernel's attention
-constexpr int kMegaSplits = 64;
-
-struct MegaParams {
-    int32_t dt, gs, d, h, L, nkv, hs, kvd, G, V, S;
+struct StreamParams {
+    int32_t d, h, L, nkv, hs, kvd, G, V, S;
+    int32_t nsplit;  // attention position splits per kv head column
+    int32_t gsplit;  // attention items sharing one kv head's query heads
+    int32_t ymax;    // row results one workgroup holds in LDS
+    int32_t kmax;    // longest matvec input (max(dim, hidden_dim))
     double eps;
-    // weights, in the library's device layout
-    const void* emb;
+    // weights in the library's device layout (Q8_0, group size 64)
+    const int8_t* emb;
     const float* emb_s;
-    const void* wqkv;
+    const int8_t* wqkv;
     const float* wqkv_s;
-    const void* wo;
+    const int8_t* wo;
     const float* wo_s;
-    const void* w13;
+    const int8_t* w13;
     const float* w13_s;
-    const void* w2;
+    const int8_t* w2;
     const float* w2_s;
-    const void* wcls;
+    const int8_t* wcls;
     const float* wcls_s;
     const float* rms_att;
     const float* rms_ffn;
@@ -240,24 +243,42 @@ struct MegaParams {
     float* logits;
     int32_t* step;
     unsigned long long* argmax;
-    double* part_o;     // [nkv][kMegaSplits][G][hs]
-    double* part_ml;    // [nkv][kMegaSplits][G][2]
-    uint32_t* head_ctr; // [nkv][32]: ranges of the kv head finished (one 128-byte line each)
-    MegaSync* sync;
+    double* part_o;      // [nkv * gsplit][nsplit][G / gsplit][hs]
+    double* part_ml;     // [nkv * gsplit][nsplit][G / gsplit][2]
+    uint32_t* head_ctr;  // [nkv * gsplit][32]: ranges of the column finished (zero between uses)
+    StreamSync* sync;
+    const int8_t* dummy; // 8 KiB of zeroed device memory: the loads past the end of a worker's stream
+    // the workers' view of the five matrices (q/k/v, output, w1/w3, w2,
+    // classifier; SKind order): byte offsets of each one's codes and scales
+    // from wbase, read with scalar loads by kind
+    const int8_t* wbase;
+    int64_t wofs[5];
+    int64_t sofs[5];
     // this launch
     int32_t token, pos, greedy;
-    uint32_t epoch0;    // grid barriers completed by earlier launches
-    double temperature; // 0: argmax
+    uint32_t epoch0;     // grid barriers completed by earlier launches
+    double temperature;  // 0: argmax
     uint64_t seed;
+    // diagnostics: when set, clock stamps of each workgroup's control events
+    // ([nwg][trace_n]) and of each worker's phase reports ([nwg][workers][phases])
+    uint64_t* trace;
+    int64_t trace_n;
 };
 
-// grid barriers one launch of the step kernel performs
-inline uint32_t mega_barriers(int L) { return 1u + 5u * (uint32_t)L; }
+// control events per workgroup in a step kernel trace
+inline int64_t stream_trace_events(int L) { return 1 + 6 * (4 * (int64_t)L + 1); }
 
-bool mega_supported(int dt, int gs, int64_t d, int64_t h, int G, int hs);
-size_t mega_lds_bytes(int dt, int64_t d, int64_t h, int G, int hs);
+// grid barriers one launch of the step kernel performs
+inline uint32_t stream_barriers(int L) { return 5u * (uint32_t)L; }
+
+struct SPlan;
+bool stream_supported(int dt, int gs, int64_t d, int64_t h, int G, int gsplit, int hs);
+size_t stream_lds_bytes(const SPlan& s, int kg, int hs);
+int stream_threads();
+int stream_splits(int64_t nkv, int64_t gsplit, int64_t nwg, int64_t S, int hs);
+int stream_workers();
 // workgroups of the step kernel a CU can hold with this much LDS (0: none)
-int mega_blocks_per_cu(int dt, int G, size_t lds);
-hipError_t launch_mega(const MegaParams& p, int grid, size_t lds, hipStream_t s);
+int stream_blocks_per_cu(int kg, int hs, size_t lds);
+hipError_t launch_stream(const StreamParams& p, int kg, int grid, size_t lds, hipStream_t s);
 
 }  // namespace l2d

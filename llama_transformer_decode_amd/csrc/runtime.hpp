@@ -73,17 +73,23 @@ struct l2d_ctx {
     hipGraphExec_t exec = nullptr;
     bool use_graph = true;
 
-    // the persistent step kernel (one cooperative launch per step)
-    bool mega_ok = false;       // supported for this model on this device
-    bool use_mega = false;
-    bool mega_pending = false;  // launched since the error word was last read
-    int mega_grid = 0;
-    size_t mega_lds = 0;
-    uint32_t mega_epoch = 0;    // grid barriers completed so far
-    l2d::MegaSync* msync = nullptr;
-    uint32_t* head_ctr = nullptr;
-    double* mpart_o = nullptr;
-    double* mpart_ml = nullptr;
+    // the persistent step kernel (one cooperative launch per step, Q8_0)
+    bool stream_ok = false;       // supported for this model on this device
+    bool use_stream = false;
+    bool stream_pending = false;  // launched since the error word was last read
+    int stream_grid = 0;
+    int stream_kg = 1;            // query heads per attention item
+    int stream_gsplit = 1;
+    int stream_nsplit = 1;
+    int stream_ymax = 0;
+    size_t stream_lds = 0;
+    uint32_t stream_epoch = 0;    // grid barriers completed so far
+    l2d::StreamSync* ssync = nullptr;
+    uint32_t* shead_ctr = nullptr;
+    double* spart_o = nullptr;
+    double* spart_ml = nullptr;
+    int8_t* sdummy = nullptr;
+    uint64_t* strace = nullptr;   // diagnostics: clock stamps of the next launch (l2d_stream_trace)
 
     // batched prefill (allocated by the first l2d_prefill): chunk capacity
     // in tokens (a multiple of 16), token ids, residual rows, q rows,

@@ -38,19 +38,29 @@ def need_gpu():
     return torch
 
 
-MODES = ("persistent", "graph")
+MODES = ("persistent", "graph", "stream")
 
-# The persistent step kernel faulted on its first MI355X run (tiny fp32
-# model, first step) and the cause is not found; it stays off and its cases
-# are skipped until a cause is shown and fixed.
-PERSISTENT_SKIP = "persistent step kernel disabled: memory access fault on first run, cause not yet found"
+# The first persistent step kernel (one 512-thread workgroup per CU, fp32 and
+# Q8_0) faulted on its first MI355X run (tiny fp32 model, first step) and
+# the cause was not found; that kernel was removed. Its cases stay skipped.
+# The step kernel the library has now ("stream": worker waves streaming the
+# weights, control waves running barriers, prologues, epilogues and
+# attention) is a new design, Q8_0 with group size 64 only.
+PERSISTENT_SKIP = ("first persistent step kernel: memory access fault on its first run (tiny fp32, step 0), "
+                   "cause not found; the kernel was removed")
 
 
 def set_mode(ctx, mode: str):
-    """persistent: the whole step as one kernel; graph: the captured graph
-    of per-phase kernels. Skips when the persistent kernel is unavailable."""
+    """persistent: the removed first step kernel (skipped); graph: the
+    captured graph of per-phase kernels; stream: the persistent step kernel
+    (skips where the model is not Q8_0 with group size 64)."""
     if mode == "persistent":
         pytest.skip(PERSISTENT_SKIP)
+    elif mode == "stream":
+        try:
+            ctx.use_persistent(True)
+        except Exception as e:  # noqa: BLE001 - the library's error names the reason
+            pytest.skip(f"persistent step kernel not available: {e}")
     else:
         ctx.use_persistent(False)
         ctx.use_graph(True)

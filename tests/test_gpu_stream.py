@@ -1,0 +1,150 @@
+"""The persistent step kernel ("stream": one cooperative launch per decode
+step, worker waves streaming the weights through every matvec phase,
+control waves running the grid barriers, prologues, epilogues and
+attention) against the captured graph of per-phase kernels and the oracle.
+
+It keeps the per-phase kernels' arithmetic and order (same Q8_0 codes of
+every matvec input, same fp64 group combine and lane reduction, same
+attention range computation and merge); only the attention's position
+splits differ (about one work item per workgroup instead of about three per
+CU), which changes the fp64 merge order. The oracle comparison holds it to
+the logits tolerance and the argmax rule at every step; the count of steps
+whose logits equal the graph's bit for bit is reported. Shapes cover one, two, four and eight query heads
+per kv head (eight: two attention items per kv head of four heads each),
+head sizes 32, 64 and 128, an odd vocabulary, the 7B shape at full size with
+deep positions, and decoding with the token taken on the device.
+"""
+import gc
+
+import numpy as np
+import pytest
+
+import llama_transformer_decode_amd as l2d
+import oracle
+import synth
+from gpu_util import Stats, log, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+TINY_Q8 = synth.Config("tinyq8", 128, 256, 3, 4, 2, 320, 64, 11, (synth.Q8_0,))      # hs 32, G 2
+GQA4_Q8 = synth.Config("gsq8", 256, 512, 2, 8, 2, 320, 48, 13, (synth.Q8_0,))        # hs 32, G 4
+GQA8_H128 = synth.Config("gqa8h128", 1024, 512, 2, 8, 1, 320, 96, 14, (synth.Q8_0,))  # hs 128, G 8
+ODD_V = synth.Config("oddv", 128, 192, 2, 4, 4, 321, 40, 15, (synth.Q8_0,))          # hs 32, G 1, odd vocab
+
+
+def _teacher_forced(cfg, steps, label):
+    """Oracle trajectory fed to both execution modes; every step compared
+    with the oracle, and the two modes' logits compared with each other."""
+    need_gpu()
+    blob = synth.make_blob(cfg, synth.Q8_0)
+    orc = oracle.Model(blob, synth.Q8_0)
+    with l2d.Context(blob, synth.Q8_0) as ctx:
+        st = Stats()
+        graph_logits = []
+        fed = []
+        tok = 1
+        ctx.use_persistent(False)
+        for p in range(steps):
+            ctx.forward(tok, p)
+            r = orc.forward(tok, p)
+            graph_logits.append(ctx.logits())
+            fed.append(tok)
+            tok = int(np.argmax(r))
+        ctx.reset_kv()
+        orc.reset_kv()
+        ctx.use_persistent(True)
+        assert ctx.persistent
+        same = 0
+        for p, t in enumerate(fed):
+            log(f"  [{label}] stream step pos {p}")
+            ctx.forward(t, p)
+            g = ctx.logits()
+            r = orc.forward(t, p)
+            st.add(p, g, r, ctx.last_token())
+            same += int(np.array_equal(g, graph_logits[p]))
+        log(f"  [{label}] stream vs oracle: {st.summary()}; steps equal to the graph's bitwise: {same}/{steps}")
+    orc.close()
+    st.assert_ok()
+    return same
+
+
+@pytest.mark.parametrize("cfg,steps", [
+    (TINY_Q8, 8),
+    (TINY_Q8, 64),
+    (GQA4_Q8, 48),
+    (GQA8_H128, 96),
+    (ODD_V, 40),
+], ids=["tinyq8-8", "tinyq8-64", "gqa4-48", "gqa8-hs128-96", "odd-vocab-40"])
+def test_stream_small(cfg, steps):
+    _teacher_forced(cfg, steps, cfg.name)
+
+
+def test_stream_110m_trajectory():
+    """110M Q8_0 (12 heads of 64), 256 teacher-forced steps."""
+    _teacher_forced(synth.CONFIGS["110M"], 256, "110M")
+
+
+def test_stream_greedy_on_device():
+    """Decoding with the token taken on the device (the previous step's
+    argmax) gives the oracle's greedy trajectory."""
+    need_gpu()
+    cfg = TINY_Q8
+    blob = synth.make_blob(cfg, synth.Q8_0)
+    orc = oracle.Model(blob, synth.Q8_0)
+    fed, am, _ = oracle.trajectory(orc, np.array([1], np.int32), 40, keep_logits=False)
+    with l2d.Context(blob, synth.Q8_0) as ctx:
+        ctx.use_persistent(True)
+        ctx.forward(1, 0)
+        toks = [ctx.last_token()]
+        for p in range(1, 40):
+            ctx.forward_greedy(p)
+            toks.append(ctx.last_token())
+    orc.close()
+    np.testing.assert_array_equal(np.array(toks), am)
+
+
+def test_stream_not_available_for_fp32():
+    need_gpu()
+    blob = synth.make_blob(synth.CONFIGS["tiny"], synth.F32)
+    with l2d.Context(blob, synth.F32) as ctx:
+        assert not ctx.persistent
+        with pytest.raises(l2d.L2DError):
+            ctx.use_persistent(True)
+
+
+def test_stream_7b_full_size():
+    """7B Q8_0 at full size: pos 0..7 teacher-forced, then deep positions
+    512 and 2048 over identical synthetic caches; stream against the oracle
+    and the graph."""
+    torch = need_gpu()
+    from test_gpu_decode import _fill_kv_both
+    cfg = synth.CONFIGS["7B"]
+    blob = synth.make_blob(cfg, synth.Q8_0)
+    orc = oracle.Model(blob, synth.Q8_0)
+    ctx = l2d.Context(blob, synth.Q8_0)
+    try:
+        tok = 1
+        for p in list(range(8)) + [512, 2048]:
+            if p >= 512:
+                _fill_kv_both(ctx, orc, p, seed=77 + p)
+            r = orc.forward(tok, p)
+            outs = {}
+            for mode in ("graph", "stream"):
+                ctx.use_persistent(mode == "stream")
+                ctx.forward(tok, p)
+                st = Stats()
+                st.add(p, ctx.logits(), r, ctx.last_token())
+                log(f"  7B pos {p} {mode}: {st.summary()}")
+                st.assert_ok()
+                outs[mode] = ctx.logits()
+            sg = Stats()
+            sg.add(p, outs["stream"], outs["graph"])
+            log(f"  7B pos {p} stream vs graph: {sg.summary()}")
+            sg.assert_ok()
+            tok = int(np.argmax(r))
+    finally:
+        ctx.close()
+        orc.close()
+        del blob
+        gc.collect()
+        torch.cuda.empty_cache()
