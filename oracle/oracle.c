@@ -588,11 +588,15 @@ static void attention(or_model* m, int64_t l, int pos)
             sc[t] = exp(sc[t] - mx);
             z += sc[t];
         }
-        for (int64_t i = 0; i < hs; i++) {
-            double acc = 0.0;
-            for (int64_t t = 0; t <= pos; t++) acc += sc[t] * (double)vl[t * kvd + g * hs + i];
-            m->o[hd * hs + i] = (float)(acc / z);
+        /* o_i = sum over t = 0..pos of a_t v_t[i], each sum taken in
+           increasing t; the cached rows are read one at a time */
+        double* acc = (double*)calloc((size_t)hs, sizeof(double));
+        for (int64_t t = 0; t <= pos; t++) {
+            const float* vt = vl + t * kvd + g * hs;
+            for (int64_t i = 0; i < hs; i++) acc[i] += sc[t] * (double)vt[i];
         }
+        for (int64_t i = 0; i < hs; i++) m->o[hd * hs + i] = (float)(acc[i] / z);
+        free(acc);
         free(sc);
     }
 }
