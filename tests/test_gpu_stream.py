@@ -12,7 +12,9 @@ the logits tolerance and the argmax rule at every step; the count of steps
 whose logits equal the graph's bit for bit is reported. Shapes cover one, two, four and eight query heads
 per kv head (eight: two attention items per kv head of four heads each),
 head sizes 32, 64 and 128, an odd vocabulary, the 7B shape at full size with
-deep positions, and decoding with the token taken on the device.
+deep positions, and decoding with the token taken on the device. The
+longer Q8_0 trajectories (tiny 64 steps, 110M 1024 steps) run in this mode
+among the decode tests.
 """
 import gc
 
@@ -70,18 +72,12 @@ def _teacher_forced(cfg, steps, label):
 
 @pytest.mark.parametrize("cfg,steps", [
     (TINY_Q8, 8),
-    (TINY_Q8, 64),
     (GQA4_Q8, 48),
     (GQA8_H128, 96),
     (ODD_V, 40),
-], ids=["tinyq8-8", "tinyq8-64", "gqa4-48", "gqa8-hs128-96", "odd-vocab-40"])
+], ids=["tinyq8-8", "gqa4-48", "gqa8-hs128-96", "odd-vocab-40"])
 def test_stream_small(cfg, steps):
     _teacher_forced(cfg, steps, cfg.name)
-
-
-def test_stream_110m_trajectory():
-    """110M Q8_0 (12 heads of 64), 256 teacher-forced steps."""
-    _teacher_forced(synth.CONFIGS["110M"], 256, "110M")
 
 
 def test_stream_greedy_on_device():
