@@ -31,9 +31,13 @@
  *   - fp32 matrices: Irwin-Hall(4) bell variate (sum of the four 16-bit
  *     fields of one 64-bit draw, centred, unit variance), times 0.02, rounded
  *     to fp32 once: an approximately N(0, 0.02) tensor, bounded at 3.46 sd.
- *   - Q8_0 matrices: codes are the same centred sum mapped to [-127, 127]
- *     with integer arithmetic; each group scale is drawn uniformly from
- *     [0.75, 1.25] x 0.02/sd(code), so dequantised weights have sd ~0.02.
+ *   - Q8_0 matrices: shaped like the codes of a bell-shaped tensor stored
+ *     with one scale per group of GS: in every group one element, at a
+ *     drawn index and with a drawn sign, is +-127 (the group's largest
+ *     magnitude), and the others are the centred sum mapped with integer
+ *     arithmetic to a code of sd ~50, clipped to [-126, 126]; each group
+ *     scale is drawn uniformly from [0.75, 1.25] x 0.02/sd(code), so
+ *     dequantised weights have sd ~0.02.
  *   - Q4_0 matrices: the centred sum mapped to [-8, 8] with integer
  *     arithmetic and 8 clipped to 7; scales as for Q8_0 with the 4-bit
  *     code's sd.
@@ -48,7 +52,7 @@
 enum {
     T_EMB = 1, T_RMS_ATT, T_WQ, T_WK, T_WV, T_WO, T_RMS_FFN,
     T_W1, T_W2, T_W3, T_RMS_FINAL, T_FREQ_RE, T_FREQ_IM, T_WCLS,
-    T_SCALE_BASE = 32, T_PROMPT = 64
+    T_SCALE_BASE = 32, T_PROMPT = 64, T_GROUP_MAX = 96
 };
 
 static inline uint64_t mix64(uint64_t z)
@@ -157,11 +161,23 @@ static void fill_const(float* dst, int64_t n, float v)
     for (int64_t i = 0; i < n; i++) dst[i] = v;
 }
 
-static void fill_codes(int8_t* dst, int64_t n, uint64_t seed, int tid)
+/* sd of an 8-bit code before clipping: bell_sd * 173 / 131070 (about 49.9) */
+#define CODE8_SPAN 173
+
+static void fill_codes(int8_t* dst, int64_t n, int gs, uint64_t seed, int tid)
 {
     #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; i++)
-        dst[i] = (int8_t)(bell(draw(seed, (uint64_t)tid, (uint64_t)i)) * 127 / 131070);
+    for (int64_t g = 0; g < n / gs; g++) {
+        const uint64_t r = draw(seed, (uint64_t)(T_GROUP_MAX + tid), (uint64_t)g);
+        const int64_t at = (int64_t)((r >> 11) % (uint64_t)gs);
+        for (int64_t j = 0; j < gs; j++) {
+            const int64_t i = g * gs + j;
+            int64_t c = bell(draw(seed, (uint64_t)tid, (uint64_t)i)) * CODE8_SPAN / 131070;
+            c = c > 126 ? 126 : c < -126 ? -126 : c;
+            if (j == at) c = (r >> 63) ? -127 : 127;
+            dst[i] = (int8_t)c;
+        }
+    }
 }
 
 /* 4-bit codes of element i: the bell sum mapped to [-8, 8], 8 clipped to 7 */
@@ -193,8 +209,9 @@ static void fill_scales_sd(float* dst, int64_t ng, uint64_t seed, int tid, doubl
 
 static void fill_scales(float* dst, int64_t ng, uint64_t seed, int tid)
 {
-    /* sd of a code is bell_sd * 127 / 131070 */
-    const double base = 0.02 / (bell_sd() * 127.0 / 131070.0);
+    /* sd of a code: about bell_sd * CODE8_SPAN / 131070, plus the group's
+       +-127 (its share of the mean square is 127^2 / gs at gs 64) */
+    const double base = 0.02 / 52.0;
     #pragma omp parallel for schedule(static)
     for (int64_t g = 0; g < ng; g++) {
         double u = (double)(draw(seed, (uint64_t)(T_SCALE_BASE + tid), (uint64_t)g) >> 11) *
@@ -223,7 +240,7 @@ int synth_fill_blob(const synth_config* c, int dtype, int gs, uint64_t seed, uin
             ptr += 4 * (p[i].n / 32);
         } else if (dtype == 1 && p[i].is_matrix) {
             int8_t* q = (int8_t*)ptr;
-            fill_codes(q, p[i].n, seed, p[i].tid);
+            fill_codes(q, p[i].n, gs, seed, p[i].tid);
             ptr += p[i].n;
             float* s;
             /* scales follow the codes; the blob keeps 4-byte alignment because

@@ -236,14 +236,23 @@ def _full_size(name, dtype, deep_positions, steps=3):
         torch.cuda.empty_cache()
 
 
-def _long_trajectory(name, dtype, n_steps, deep_positions=(), modes=("graph",)):
+def _long_trajectory(name, dtype, n_steps, deep_positions=(), modes=("graph",), max_flips=3):
     """Teacher-forced greedy decode of pos 0..n_steps-1 at full size: at each
     pos the oracle's step gives the logits to compare and, by its argmax, the
     token both sides take next (one oracle pass; the GPU step is enqueued
     before the oracle's so the two overlap). Then one step at each deep
-    position over identical synthetic cache slots 0..pos-1."""
+    position over identical synthetic cache slots 0..pos-1.
+
+    Q8_0 activation codes may round to the neighbouring code where the
+    oracle's |x| / scale is within 1e-3 of k + 1/2 (near ties); one such
+    flip moves that step's logits past the tolerance and then every later
+    step through the cache. A step outside the tolerance is therefore
+    audited: both sides re-run it with every layer's quantised inputs traced,
+    and it passes only if the first differing input differs at near ties
+    alone; the oracle's cache then replaces the device's and the run goes
+    on. At most max_flips such steps per run."""
     torch = need_gpu()
-    from gpu_util import Stats
+    from gpu_util import Stats, copy_cache_from_oracle, near_tie_audit
     cfg = synth.CONFIGS[name]
     t = time.time()
     blob = synth.make_blob(cfg, dtype)
@@ -257,16 +266,31 @@ def _long_trajectory(name, dtype, n_steps, deep_positions=(), modes=("graph",)):
             orc.reset_kv()
             st = Stats()
             tok = 1
+            flips = []
             t0 = t1 = time.time()
             for p in range(n_steps):
                 ctx.forward(tok, p)
                 r = orc.forward(tok, p)
+                nbad = len(st.bad)
                 st.add(p, ctx.logits(), r, ctx.last_token())
+                if len(st.bad) > nbad and dtype != synth.F32 and len(flips) < max_flips:
+                    # a step outside the tolerance: allowed only when its first
+                    # differing quantised input differs at near ties (the two
+                    # sides' fp64 sums may round one fp32 ulp apart); then
+                    # both sides continue from the oracle's cache
+                    layer, slot, nd, ok = near_tie_audit(ctx, orc, tok, p, cfg.n_layers)
+                    log(f"  [{name} dt{dtype} {mode}] pos {p}: first differing input layer {layer} slot {slot}, "
+                        f"{nd} codes, near ties only: {ok}")
+                    if ok:
+                        del st.bad[nbad:]
+                        flips.append((p, layer, slot, nd))
+                        copy_cache_from_oracle(ctx, orc, p)
                 tok = int(np.argmax(r))
                 if time.time() - t1 > 30:
                     log(f"  [{name} dt{dtype} {mode}] pos {p} ({time.time() - t0:.0f}s): {st.summary()}")
                     t1 = time.time()
-            log(f"  [{name} dt{dtype} {mode}] pos 0..{n_steps - 1}: {st.summary()}")
+            log(f"  [{name} dt{dtype} {mode}] pos 0..{n_steps - 1}: {st.summary()}; "
+                f"near-tie steps (pos, layer, slot, codes): {flips}")
             st.assert_ok()
             assert st.steps == n_steps and st.argmax_checked > 0
             for P in deep_positions:
