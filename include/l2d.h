@@ -258,6 +258,22 @@ int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int
              int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream);
 
 /*
+ * l2d_gemv for callers that cannot allocate device memory (code under
+ * stream capture, serving loops and harnesses that forbid hipMalloc): same
+ * arguments, same kernels, same result bits, and no device allocation.
+ * Q8_0 codes are re-laid-out into a fixed scratch array of
+ * l2d_gemv_noalloc_max_bytes() bytes (32 MiB) that the library holds on each
+ * GPU it runs on until the process ends; rows * cols above that returns
+ * L2D_EINVAL (use l2d_gemv). Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and give
+ * undefined results; calls on one stream are ordered and safe. fp32 and
+ * Q4_0 need no scratch and run as l2d_gemv does. Asynchronous on stream.
+ */
+int l2d_gemv_noalloc(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
+                     int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream);
+int64_t l2d_gemv_noalloc_max_bytes(void);
+
+/*
  * Time the matvec kernel of l2d_gemv (dtype L2D_F32 or L2D_Q4_0; Q8_0 codes
  * need the device layout and are timed by l2d_profile_step): reps launches
  * on stream, launch r reading weight copy r % copies (W and W_s are host

@@ -86,6 +86,9 @@ def lib():
             "l2d_kv_cache": (ctypes.c_int, [_vp, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
             "l2d_gemv": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
+            "l2d_gemv_noalloc": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, _vp, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int32, _vp, _vp, _vp]),
+            "l2d_gemv_noalloc_max_bytes": (ctypes.c_int64, []),
             "l2d_gemv_profile": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp,
                                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _vp,
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _vp]),
@@ -114,7 +117,8 @@ def lib():
 # every symbol include/l2d.h declares
 EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l2d_sync",
            "l2d_last_token", "l2d_read_logits", "l2d_quantize_q80", "l2d_reset_kv", "l2d_free",
-           "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
+           "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_gemv_noalloc", "l2d_gemv_noalloc_max_bytes",
+           "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
            "l2d_set_sampling", "l2d_prefill", "l2d_profile_prefill", "l2d_stream_plan_check",
            "l2d_stream_trace")
@@ -350,6 +354,22 @@ def gemv(dtype: int, W, W_s, x, rows: int, cols: int, gs: int = 64, group_dots=N
                           x.data_ptr(), rows, cols, gs, out.data_ptr(),
                           group_dots.data_ptr() if group_dots is not None else None, st))
     return out
+
+
+def gemv_noalloc(dtype: int, W, W_s, x, out, rows: int, cols: int, gs: int = 64, group_dots=None, stream=None):
+    """l2d_gemv_noalloc: out = W x into the caller's tensor `out`, with no
+    device allocation by the library (torch CUDA tensors)."""
+    import torch
+    st = _stream_handle(stream if stream is not None else torch.cuda.current_stream())
+    _check(lib().l2d_gemv_noalloc(dtype, W.data_ptr(), W_s.data_ptr() if W_s is not None else None,
+                                  x.data_ptr(), rows, cols, gs, out.data_ptr(),
+                                  group_dots.data_ptr() if group_dots is not None else None, st))
+    return out
+
+
+def gemv_noalloc_max_bytes() -> int:
+    """Largest rows x cols of Q8_0 codes l2d_gemv_noalloc takes."""
+    return int(lib().l2d_gemv_noalloc_max_bytes())
 
 
 def gemv_profile(dtype: int, Ws, Ss, x, rows: int, cols: int, gs: int = 32, reps: int = 20, stream=None):

@@ -793,6 +793,47 @@ const float* forward_impl(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
 
 }  // namespace
 
+namespace l2d {
+
+// Argument checks shared by l2d_gemv, l2d_gemv_noalloc and l2d_gemv_profile; fills p (W, Ws
+// left to the caller) and the kernel dtype.
+int gemv_setup(int32_t dtype, const float* x, int64_t rows, int64_t cols, int32_t gs,
+               bool have_scales, float* out, GemvParams* p, int* dt)
+{
+    if (dtype != L2D_F32 && dtype != L2D_Q8_0 && dtype != L2D_Q4_0)
+        return fail(nullptr, L2D_EINVAL, "gemv: bad dtype");
+    if (rows <= 0 || cols <= 0 || rows % 2 || cols % 4 || !x || !out)
+        return fail(nullptr, L2D_EINVAL, "gemv: need rows even > 0, cols % 4 == 0, non-null pointers");
+    if (dtype == L2D_Q8_0) {
+        if (gs < 16 || gs > 256 || (gs & (gs - 1)) || cols % gs || !have_scales)
+            return fail(nullptr, L2D_EINVAL, "gemv: Q8_0 needs a power-of-two gs in [16,256] dividing cols");
+        if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
+    } else if (dtype == L2D_Q4_0) {
+        if (gs != 32 || cols % 32 || !have_scales) return fail(nullptr, L2D_EINVAL, "gemv: Q4_0 needs gs 32 dividing cols");
+        if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
+    } else if (cols > 16000) {
+        return fail(nullptr, L2D_EINVAL, "gemv: fp32 cols > 16000");
+    }
+    memset(p, 0, sizeof(*p));
+    p->M = rows;
+    p->K = cols;
+    p->gs = dtype == L2D_F32 ? 1 : gs;
+    p->x = x;
+    p->out = out;
+    *dt = dtype == L2D_F32 ? DT_F32 : dtype == L2D_Q8_0 ? DT_Q8 : DT_Q4;
+    return L2D_OK;
+}
+
+int gemv_grid()
+{
+    int dev = 0, cus = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus > 0 ? 2 * cus : 512;
+}
+
+}  // namespace l2d
+
 extern "C" {
 
 int l2d_init(const l2d_config* cfg, const l2d_weights* w, void* stream, l2d_ctx** out)
@@ -899,42 +940,6 @@ int l2d_kv_cache(l2d_ctx* ctx, float** key_cache, float** value_cache)
     return L2D_OK;
 }
 
-// Argument checks shared by l2d_gemv and l2d_gemv_profile; fills p (W, Ws
-// left to the caller) and the kernel dtype.
-static int gemv_setup(int32_t dtype, const float* x, int64_t rows, int64_t cols, int32_t gs,
-                      bool have_scales, float* out, GemvParams* p, int* dt)
-{
-    if (dtype != L2D_F32 && dtype != L2D_Q8_0 && dtype != L2D_Q4_0)
-        return fail(nullptr, L2D_EINVAL, "gemv: bad dtype");
-    if (rows <= 0 || cols <= 0 || rows % 2 || cols % 4 || !x || !out)
-        return fail(nullptr, L2D_EINVAL, "gemv: need rows even > 0, cols % 4 == 0, non-null pointers");
-    if (dtype == L2D_Q8_0) {
-        if (gs < 16 || gs > 256 || (gs & (gs - 1)) || cols % gs || !have_scales)
-            return fail(nullptr, L2D_EINVAL, "gemv: Q8_0 needs a power-of-two gs in [16,256] dividing cols");
-        if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
-    } else if (dtype == L2D_Q4_0) {
-        if (gs != 32 || cols % 32 || !have_scales) return fail(nullptr, L2D_EINVAL, "gemv: Q4_0 needs gs 32 dividing cols");
-        if (cols > 65536) return fail(nullptr, L2D_EINVAL, "gemv: cols > 65536");
-    } else if (cols > 16000) {
-        return fail(nullptr, L2D_EINVAL, "gemv: fp32 cols > 16000");
-    }
-    memset(p, 0, sizeof(*p));
-    p->M = rows;
-    p->K = cols;
-    p->gs = dtype == L2D_F32 ? 1 : gs;
-    p->x = x;
-    p->out = out;
-    *dt = dtype == L2D_F32 ? DT_F32 : dtype == L2D_Q8_0 ? DT_Q8 : DT_Q4;
-    return L2D_OK;
-}
-
-static int gemv_grid()
-{
-    int dev = 0, cus = 0;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    return cus > 0 ? 2 * cus : 512;
-}
 
 int l2d_gemv(int32_t dtype, const void* W, const float* W_s, const float* x, int64_t rows,
              int64_t cols, int32_t gs, float* out, int32_t* group_dots, void* stream)

@@ -19,6 +19,14 @@ int fail(l2d_ctx* ctx, int code, const std::string& msg);
 // check a config against what the kernels support; returns L2D_OK or L2D_EINVAL
 int validate_config(const l2d_config* c);
 
+// argument checks of l2d_gemv and its kernel parameters (weights unset);
+// returns L2D_OK or the error recorded for the calling thread
+int gemv_setup(int32_t dtype, const float* x, int64_t rows, int64_t cols, int32_t gs,
+               bool have_scales, float* out, GemvParams* p, int* dt);
+
+// workgroups of a standalone matvec launch on the current device
+int gemv_grid();
+
 }  // namespace l2d
 
 struct l2d_ctx {
