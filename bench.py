@@ -488,10 +488,10 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_path: str, title: str,
         return per
 
     fe, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
-    copy = [k for k in fe if "copyBuffer" in k]
+    copy = [k for k in fe if k == "__amd_rocclr_copyBuffer"]
     gib_kib = float(1 << 20)
     rf = gib_kib / sum(fe[copy[0]]) if copy else 1.0
-    copyw = [k for k in wr if "copyBuffer" in k]
+    copyw = [k for k in wr if k == "__amd_rocclr_copyBuffer"]
     wf = gib_kib / sum(wr[copyw[0]]) if copyw else 1.0
     cfg = synth.CONFIGS[cfg_name]
     b = step_bytes(cfg, 1, pos)

@@ -68,6 +68,9 @@ def bind(path: str):
         "or_trace_codes": (_vp, [_vp, ctypes.c_int]),
         "or_trace_scales": (_vp, [_vp, ctypes.c_int]),
         "or_trace_input": (_vp, [_vp, ctypes.c_int]),
+        "or_trace_codes_at": (_vp, [_vp, ctypes.c_int, ctypes.c_int]),
+        "or_trace_scales_at": (_vp, [_vp, ctypes.c_int, ctypes.c_int]),
+        "or_trace_input_at": (_vp, [_vp, ctypes.c_int, ctypes.c_int]),
         "or_forward": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int]),
         "or_matvec_f32": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp]),
         "or_matvec_q80": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
@@ -283,7 +286,19 @@ class Model:
         return self._view(_load().or_attn_out(self._h), self.dim, np.float32).copy()
 
     def trace_layer(self, layer: int):
+        """Record one layer's quantised matvec inputs on the next forwards
+        (-2: every layer, -1: stop)."""
         _load().or_trace_layer(self._h, layer)
+
+    def trace_at(self, layer: int, slot: int):
+        """(codes, scales, fp32 input) of `slot` of `layer` recorded while
+        every layer is traced (trace_layer(-2))."""
+        n = self.hidden_dim if slot == 3 else self.dim
+        lib = _load()
+        q = self._view(lib.or_trace_codes_at(self._h, layer, slot), n, np.int8).copy()
+        s = self._view(lib.or_trace_scales_at(self._h, layer, slot), n // self.gs, np.float32).copy()
+        f = self._view(lib.or_trace_input_at(self._h, layer, slot), n, np.float32).copy()
+        return q, s, f
 
     def trace(self, slot: int):
         """(codes, scales, fp32 input) of the traced layer's matvec input `slot`."""

@@ -77,6 +77,7 @@ typedef struct {
     float* as;
     /* trace of one layer's quantised matvec inputs (Q8_0 path) */
     int trace_layer;
+    int64_t trace_at; /* layer whose inputs the matvecs record */
     int8_t* tq[4];
     float* ts[4];
     float* tf[4];
@@ -381,9 +382,10 @@ static void matvec(or_model* m, float* out, const float* x, const or_mat* w, int
     int gs = m->gs;
     or_quantize(x, cols, gs, m->aq, m->as);
     if (trace_slot >= 0) {
-        memcpy(m->tq[trace_slot], m->aq, (size_t)cols);
-        memcpy(m->ts[trace_slot], m->as, (size_t)(cols / gs) * 4);
-        memcpy(m->tf[trace_slot], x, (size_t)cols * 4);
+        const int64_t off = m->trace_at * cols;
+        memcpy(m->tq[trace_slot] + off, m->aq, (size_t)cols);
+        memcpy(m->ts[trace_slot] + off / gs, m->as, (size_t)(cols / gs) * 4);
+        memcpy(m->tf[trace_slot] + off, x, (size_t)cols * 4);
     }
     matvec_q80_rows(out, m->aq, m->as, w->q + woff, w->s + woff / gs, rows, cols, gs);
 }
@@ -665,29 +667,47 @@ int or_sample(const float* logits, int64_t n, double temperature, uint64_t seed,
     return (int)best;
 }
 
+/* trace buffers hold every layer: slot s of layer l at offset l * size(s) */
+static int64_t trace_size(const or_model* m, int slot) { return slot == 3 ? m->h : m->d; }
+
 static void trace_alloc(or_model* m)
 {
-    int64_t sizes[4] = {m->d, m->d, m->d, m->h};
     for (int i = 0; i < 4; i++) {
         if (!m->tq[i]) {
-            m->tq[i] = (int8_t*)calloc(sizes[i], 1);
-            m->ts[i] = (float*)calloc(sizes[i], 4);
-            m->tf[i] = (float*)calloc(sizes[i], 4);
+            int64_t n = m->L * trace_size(m, i);
+            m->tq[i] = (int8_t*)calloc(n, 1);
+            m->ts[i] = (float*)calloc(n, 4);
+            m->tf[i] = (float*)calloc(n, 4);
         }
     }
 }
 
 /* record the quantised inputs of layer l's four matvecs (Q8_0 only):
-   slot 0 QKV input, 1 output-projection input, 2 W1/W3 input, 3 W2 input */
+   slot 0 QKV input, 1 output-projection input, 2 W1/W3 input, 3 W2 input;
+   l = -2 records every layer, l = -1 stops */
 void or_trace_layer(or_model* m, int l)
 {
     m->trace_layer = l;
-    if (l >= 0) trace_alloc(m);
+    if (l >= 0 || l == -2) trace_alloc(m);
 }
 
-int8_t* or_trace_codes(or_model* m, int slot) { return m->tq[slot]; }
-float* or_trace_scales(or_model* m, int slot) { return m->ts[slot]; }
-float* or_trace_input(or_model* m, int slot) { return m->tf[slot]; }
+static int64_t trace_off(const or_model* m, int layer, int slot)
+{
+    return (int64_t)(layer < 0 ? 0 : layer) * trace_size(m, slot);
+}
+
+int8_t* or_trace_codes(or_model* m, int slot) { return m->tq[slot] + trace_off(m, m->trace_layer, slot); }
+float* or_trace_scales(or_model* m, int slot)
+{
+    return m->ts[slot] + trace_off(m, m->trace_layer, slot) / m->gs;
+}
+float* or_trace_input(or_model* m, int slot) { return m->tf[slot] + trace_off(m, m->trace_layer, slot); }
+int8_t* or_trace_codes_at(or_model* m, int layer, int slot) { return m->tq[slot] + trace_off(m, layer, slot); }
+float* or_trace_scales_at(or_model* m, int layer, int slot)
+{
+    return m->ts[slot] + trace_off(m, layer, slot) / m->gs;
+}
+float* or_trace_input_at(or_model* m, int layer, int slot) { return m->tf[slot] + trace_off(m, layer, slot); }
 
 /*
  * One decode step: token at position pos -> logits[V]; writes KV slot pos.
@@ -723,7 +743,8 @@ int or_forward(or_model* m, int token, int pos)
     }
 
     for (int64_t l = 0; l < m->L; l++) {
-        int tr = (m->dtype == OR_Q8_0 && m->trace_layer == (int)l);
+        int tr = (m->dtype == OR_Q8_0 && (m->trace_layer == (int)l || m->trace_layer == -2));
+        m->trace_at = l;
         rmsnorm(m->xb, m->x, m->rms_att + l * d, d);
         matvec(m, m->q, m->xb, &m->wq, l * d * d, d, d, tr ? 0 : -1);
         matvec(m, m->k, m->xb, &m->wk, l * kvd * d, kvd, d, -1);

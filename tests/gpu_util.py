@@ -142,23 +142,24 @@ NEAR_TIE = 1e-3
 
 
 def near_tie_audit(ctx, orc, tok: int, pos: int, n_layers: int):
-    """Re-run step pos on both sides with each layer's quantised matvec
-    inputs traced, in layer and slot order, up to the first input whose
+    """Re-run step pos on both sides with the quantised matvec inputs
+    traced (the oracle every layer in one pass, the device one layer per
+    pass), compared in layer and slot order up to the first input whose
     codes or scales differ. Returns (layer, slot, n_codes_differing, ok):
     ok when every differing code sits at a near tie of the oracle's value
     and every scale agrees within 1e-5 relative; (None, None, 0, False)
     when nothing differs. Re-running a (token, pos) rewrites the same cache
     slot with the same values on both sides."""
     try:
+        orc.trace_layer(-2)  # one oracle pass records every layer
+        orc.forward(tok, pos)
         for layer in range(n_layers):
             ctx.trace_layer(layer)
-            orc.trace_layer(layer)
             ctx.forward(tok, pos)
             ctx.sync()
-            orc.forward(tok, pos)
             for slot in range(4):
                 gq, gsc = ctx.trace(slot)
-                oq, osc, of = orc.trace(slot)
+                oq, osc, of = orc.trace_at(layer, slot)
                 diff = gq != oq
                 sdiff = gsc != osc
                 if not diff.any() and not sdiff.any():
