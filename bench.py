@@ -628,6 +628,11 @@ def main():
                 detail["q8_0_stream"] = {"unavailable": str(e)}
         if not args.no_prefill and dt != 2:  # no batched prefill for 4-bit weights
             detail["prefill_" + name] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
+            if dt == 1:
+                # the same prefill with the group combine in fp32
+                ctx.prefill_combine(True)
+                detail["prefill_q8_0_fp32_combine"] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
+                ctx.prefill_combine(False)
         if head is None:
             head = (dt, res[hp], kt, step_bytes(cfg, dt, hp))
         ctx.close()

@@ -173,6 +173,19 @@ const float* l2d_forward_greedy(l2d_ctx* ctx, int32_t pos);
 const float* l2d_prefill(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t pos0);
 
 /*
+ * Group combine of the following prefills' Q8_0 matmuls. fp32 = 0 (the
+ * default): each output is the fp64 sum over groups of (exact int32 group
+ * dot x weight scale) x input scale, the single-token step's arithmetic, so
+ * prefill and token-by-token decoding give identical bits. fp32 = 1: the same
+ * sum accumulated in fp32, acc = fma(float(dot), weight scale x input scale,
+ * acc) (the pages' runq.c combines a group's integer dot with the two scales
+ * in float; hub page, quantisation support; gitcode guide section 1): fewer
+ * operations per group, results within the logits tolerance rather than bit
+ * for bit. fp32 weights are unaffected. Returns L2D_EINVAL for other values.
+ */
+int l2d_prefill_combine(l2d_ctx* ctx, int32_t fp32);
+
+/*
  * Next-token selection of the following forwards (mht18 essay, section 3.2:
  * the logits go through a softmax, the next token is a random draw from
  * that distribution, the temperature scaling the logits first).

@@ -95,6 +95,7 @@ def lib():
             "l2d_trace_layer": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_trace_read": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp]),
             "l2d_use_graph": (ctypes.c_int, [_vp, ctypes.c_int32]),
+            "l2d_prefill_combine": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_use_persistent": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_set_sampling": (ctypes.c_int, [_vp, ctypes.c_double, ctypes.c_uint64]),
             "l2d_persistent": (ctypes.c_int, [_vp]),
@@ -120,7 +121,7 @@ EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l
            "l2d_last_error", "l2d_kv_cache", "l2d_gemv", "l2d_gemv_noalloc", "l2d_gemv_noalloc_max_bytes",
            "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
-           "l2d_set_sampling", "l2d_prefill", "l2d_profile_prefill", "l2d_stream_plan_check",
+           "l2d_set_sampling", "l2d_prefill", "l2d_prefill_combine", "l2d_profile_prefill", "l2d_stream_plan_check",
            "l2d_stream_trace")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
@@ -274,6 +275,11 @@ class Context:
         out = (ctypes.c_double * len(KERNEL_CLASSES))()
         _check(lib().l2d_profile_step(self._h, int(token), int(pos), int(reps), out), self._h)
         return {k: float(out[i]) for i, k in enumerate(KERNEL_CLASSES)}
+
+    def prefill_combine(self, fp32: bool):
+        """Q8_0 group combine of the prefill matmuls: fp64 (False, the
+        default, bit-identical to token-by-token steps) or fp32 (True)."""
+        _check(lib().l2d_prefill_combine(self._h, 1 if fp32 else 0), self._h)
 
     def use_graph(self, enable: bool):
         _check(lib().l2d_use_graph(self._h, 1 if enable else 0), self._h)

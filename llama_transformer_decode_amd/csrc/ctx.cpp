@@ -1093,6 +1093,7 @@ int enqueue_prefill_chunk(l2d_ctx* ctx, int m, int pos, KernelTimer* kt)
         g.dtype = ctx->dt;
         g.gs = (int32_t)gs;
         g.m = m;
+        g.combine = ctx->pf_combine;
         g.aq = ctx->pf_aq;
         g.as = ctx->pf_as;
 
@@ -1321,6 +1322,14 @@ int l2d_stream_trace(l2d_ctx* ctx, int32_t token, int32_t pos, uint64_t* host, i
     }
     hipFree(dev);
     return rc;
+}
+
+int l2d_prefill_combine(l2d_ctx* ctx, int32_t fp32)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "prefill_combine: null context");
+    if (fp32 != 0 && fp32 != 1) return fail(ctx, L2D_EINVAL, "prefill_combine: 0 (fp64) or 1 (fp32)");
+    ctx->pf_combine = fp32;
+    return L2D_OK;
 }
 
 int l2d_use_graph(l2d_ctx* ctx, int32_t enable)

@@ -156,6 +156,8 @@ struct PrefillGemmParams {
     int32_t d, kvd, hs, pos0;
     const float* rcos;  // [m][hs/2]
     const float* rsin;
+    // Q8_0 group combine: 0 fp64 (bit-identical to single-token steps), 1 fp32
+    int32_t combine;
 };
 hipError_t launch_prefill_gemm(int epi, const PrefillGemmParams& p, hipStream_t s,
                                const LaunchEvents* ev = nullptr);

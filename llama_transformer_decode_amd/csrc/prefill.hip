@@ -260,7 +260,12 @@ struct GemmOps {
     v4i b[kTT][U];
 };
 
-template <int EPI, int U>
+// CMB 0: each output is the fp64 sum over groups of (dot x sw) x sx, the
+// oracle's arithmetic and order (bit-identical results). CMB 1: the same sum
+// in fp32, acc = fma(float(dot), sw x sx, acc): one conversion, one multiply
+// and one fused multiply-add per output and group instead of four fp64
+// operations, held to the logits tolerance instead of bit-identity.
+template <int EPI, int U, int CMB>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams p)
 {
 #pragma clang fp contract(off)
@@ -358,13 +363,14 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
             for (int j = 0; j < kTT; j++) o.b[j][u] = *(const v4i*)(xtile[j] + ((int64_t)gc * U + u) * 1024);
     };
 
-    double acc[kTR][kTT][4];
+    using Acc = typename std::conditional<CMB == 1, float, double>::type;
+    Acc acc[kTR][kTT][4];
 #pragma unroll
     for (int i = 0; i < kTR; i++)
 #pragma unroll
         for (int j = 0; j < kTT; j++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[i][j][r] = 0.0;
+            for (int r = 0; r < 4; r++) acc[i][j][r] = (Acc)0;
 
     GemmOps<U> ops[kGRing];
 #pragma unroll
@@ -401,6 +407,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
         for (int i = 0; i < kTR; i++) {
             if constexpr (U != 1) read_rows(i);
             const double sw[4] = {(double)sw4[i].x, (double)sw4[i].y, (double)sw4[i].z, (double)sw4[i].w};
+            const float swf[4] = {sw4[i].x, sw4[i].y, sw4[i].z, sw4[i].w};
             const v4i* a = av[i];
 #pragma unroll
             for (int j = 0; j < kTT; j++) {
@@ -409,8 +416,12 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(PrefillGemmParams 
                 for (int u = 0; u < U; u++) c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], o.b[j][u], c, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
-                    const double t = ((double)c[r] * sw[r]) * sx[j];
-                    acc[i][j][r] = acc[i][j][r] + t;
+                    if constexpr (CMB == 1) {
+                        acc[i][j][r] = __builtin_fmaf((float)c[r], swf[r] * sxf[j], acc[i][j][r]);
+                    } else {
+                        const double t = ((double)c[r] * sw[r]) * sx[j];
+                        acc[i][j][r] = acc[i][j][r] + t;
+                    }
                 }
             }
         }
@@ -579,12 +590,12 @@ size_t prefill_gemm_grid(int64_t N, int m)
 }
 
 // the staging buffers exceed the default 64 KiB of dynamic LDS
-template <int EPI, int U>
+template <int EPI, int U, int CMB>
 static hipError_t gemm_lds_attr()
 {
     static bool done = false;
     if (!done) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<EPI, U>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<EPI, U, CMB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmLds));
         if (e != hipSuccess) return e;
         done = true;
@@ -596,18 +607,27 @@ template <int EPI>
 static hipError_t launch_gemm_epi(const PrefillGemmParams& p, hipStream_t s, const LaunchEvents* ev)
 {
     const dim3 grid((unsigned)prefill_gemm_grid(p.N, p.m));
-#define L2D_PG(UU)                                                                                   \
-    if (hipError_t e_ = gemm_lds_attr<EPI, UU>(); e_ != hipSuccess) return e_;                      \
+#define L2D_PG(UU, CC)                                                                               \
+    if (hipError_t e_ = gemm_lds_attr<EPI, UU, CC>(); e_ != hipSuccess) return e_;                  \
     if (ev)                                                                                          \
-        hipExtLaunchKernelGGL((prefill_gemm_kernel<EPI, UU>), grid, dim3(256), (uint32_t)sizeof(GemmLds), \
-                              s, ev->start, ev->stop, 0u, p);                                        \
+        hipExtLaunchKernelGGL((prefill_gemm_kernel<EPI, UU, CC>), grid, dim3(256),                  \
+                              (uint32_t)sizeof(GemmLds), s, ev->start, ev->stop, 0u, p);             \
     else                                                                                             \
-        hipLaunchKernelGGL((prefill_gemm_kernel<EPI, UU>), grid, dim3(256), sizeof(GemmLds), s, p);
-    switch (p.gs) {
-    case 64: L2D_PG(1) break;
-    case 128: L2D_PG(2) break;
-    case 256: L2D_PG(4) break;
-    default: return hipErrorInvalidValue;
+        hipLaunchKernelGGL((prefill_gemm_kernel<EPI, UU, CC>), grid, dim3(256), sizeof(GemmLds), s, p);
+    if (p.combine == 1) {
+        switch (p.gs) {
+        case 64: L2D_PG(1, 1) break;
+        case 128: L2D_PG(2, 1) break;
+        case 256: L2D_PG(4, 1) break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.gs) {
+        case 64: L2D_PG(1, 0) break;
+        case 128: L2D_PG(2, 0) break;
+        case 256: L2D_PG(4, 0) break;
+        default: return hipErrorInvalidValue;
+        }
     }
 #undef L2D_PG
     return hipGetLastError();

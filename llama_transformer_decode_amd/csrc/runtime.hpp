@@ -103,6 +103,7 @@ struct l2d_ctx {
     // in tokens (a multiple of 16), token ids, residual rows, q rows,
     // attention outputs, FFN hidden rows, quantised matmul inputs, RoPE tables
     int pf_cap = 0;
+    int pf_combine = 0;      // Q8_0 group combine of the prefill matmuls: 0 fp64, 1 fp32
     int32_t* pf_tok = nullptr;
     float* pf_x = nullptr;   // [cap][d]
     float* pf_q = nullptr;   // [cap][d]

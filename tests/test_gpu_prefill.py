@@ -13,7 +13,9 @@ the vector kernel, which L2D_PREFILL_ATTN_VALU=1 also selects for every
 shape, so both kernels are checked at every GQA ratio. Q8_0 is
 bit-identical by construction (same exact group dots, same fp64 order); fp32
 sums the same exact products in another fp64 order, like the decode step's
-fp32 GEMV, and is held to the logits tolerance."""
+fp32 GEMV, and is held to the logits tolerance. The Q8_0 prefill with its
+group combine in fp32 is checked where its arithmetic alone decides (layer
+0); see its test for why not beyond."""
 import gc
 import os
 
@@ -41,29 +43,34 @@ def _check_cache(ctx, orc, lo: int, hi: int, st: Stats):
     st.add("v", vc[:, lo:hi].cpu().numpy(), orc.value_cache()[:, lo:hi])
 
 
-def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0, valu: bool = False):
+def _run(cfg, gs: int, calls, cont: int = 6, dtype: int = synth.Q8_0, valu: bool = False,
+         combine32: bool = False):
     """calls: list of (start, n) prefill calls over one prompt; then `cont`
     greedy decode steps on the device, teacher-checked against the oracle.
     valu: run the prefill with the vector attention kernel for every shape
-    (L2D_PREFILL_ATTN_VALU=1, read at each prefill launch)."""
+    (L2D_PREFILL_ATTN_VALU=1, read at each prefill launch).
+    combine32: the Q8_0 matmuls combine group dots in fp32."""
     torch = need_gpu()
     if valu:
         os.environ["L2D_PREFILL_ATTN_VALU"] = "1"
     try:
-        return _run_inner(cfg, gs, calls, cont, dtype, torch)
+        return _run_inner(cfg, gs, calls, cont, dtype, torch, combine32)
     finally:
         os.environ.pop("L2D_PREFILL_ATTN_VALU", None)
 
 
-def _run_inner(cfg, gs, calls, cont, dtype, torch):
+def _run_inner(cfg, gs, calls, cont, dtype, torch, combine32=False):
     total = sum(n for _, n in calls)
     tokens = synth.prompt(cfg.seed + 500, total, abs(cfg.vocab))
     blob = synth.make_blob(cfg, dtype, gs=gs)
     orc = oracle.Model(blob, dtype, gs=gs)
     cache_st, logit_st = Stats(), Stats()
     with l2d.Context(blob, dtype, group_size=gs) as ctx:
+        if combine32:
+            ctx.prefill_combine(True)
         for start, n in calls:
-            log(f"  {cfg.name} dt{dtype} gs{gs}: prefill {n} tokens at pos {start}")
+            log(f"  {cfg.name} dt{dtype} gs{gs}{' fp32 combine' if combine32 else ''}: "
+                f"prefill {n} tokens at pos {start}")
             ctx.prefill(tokens[start:start + n], start)
             for i in range(n):
                 ref = orc.forward(int(tokens[start + i]), start + i)
@@ -118,6 +125,44 @@ def test_prefill_vector_attention(cfg, calls):
     matrix-core kernel would otherwise take (L2D_PREFILL_ATTN_VALU=1)."""
     cache_st, _ = _run(cfg, 64, calls, valu=True)
     assert cache_st.exact / cache_st.n > 0.99
+
+
+@pytest.mark.parametrize("cfg,gs,n", [
+    (TINY_Q8, 64, 41),
+    (GQA8_Q8, 256, 53),
+    (GQA8_H128, 64, 65),
+    (synth.CONFIGS["110M"], 64, 300),
+], ids=["tiny-gs64", "gqa8-gs256", "gqa8-hs128", "110m-300"])
+def test_prefill_fp32_combine(cfg, gs, n):
+    """Q8_0 matmuls with the group combine in fp32 (l2d_prefill_combine).
+    Layer 0's inputs are exact (dequantised embedding rows), so its K/V
+    cache rows differ from the oracle's only by the combine: within 1e-5
+    relative (fp32 accumulation over at most 4096 / gs groups). Later layers
+    quantise inputs that already differ in low bits; a code that then rounds
+    the other way at a near tie moves everything after it, so the end-to-end
+    difference is logged, not held to the logits tolerance."""
+    torch = need_gpu()
+    tokens = synth.prompt(cfg.seed + 500, n, abs(cfg.vocab))
+    blob = synth.make_blob(cfg, synth.Q8_0, gs=gs)
+    orc = oracle.Model(blob, synth.Q8_0, gs=gs)
+    with l2d.Context(blob, synth.Q8_0, group_size=gs) as ctx:
+        ctx.prefill_combine(True)
+        ctx.prefill(tokens, 0)
+        for i in range(n):
+            ref = orc.forward(int(tokens[i]), i)
+        kc, vc = ctx.kv_cache()
+        for name, g, o in (("k", kc, orc.key_cache()), ("v", vc, orc.value_cache())):
+            g0 = g[0, :n].cpu().numpy().astype(np.float64)
+            o0 = o[0, :n].astype(np.float64)
+            d = np.abs(g0 - o0)
+            assert (d <= 1e-6 + 1e-5 * np.abs(o0)).all(), (name, float(d.max()))
+        st = Stats()
+        _check_cache(ctx, orc, 0, n, st)
+        lg = np.abs(ctx.logits().astype(np.float64) - ref).max()
+        log(f"  {cfg.name} gs{gs} fp32 combine, {n} tokens: layer 0 K/V within 1e-5 relative; "
+            f"all layers {st.summary()}; last logits max|d| {lg:.3g}")
+    orc.close()
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("name,calls", [
