@@ -1,7 +1,7 @@
 // attn_core.hpp - single-query GQA attention over one range of cached
 // positions of one kv head, for a workgroup of NT threads. Shared by the
 // standalone attention kernel (attn.hip) and the persistent step kernel
-// (mega.hip).
+// (stream.hip), and by the batched prefill's vector attention kernel.
 //
 // For query head h and its kv head g = h / G (G = n_heads / n_kv_heads query
 // heads share a kv head: Q&A page, GQA question), over cached positions
@@ -10,15 +10,19 @@
 //     s_t = q_h . k_t / sqrt(hs),  a = softmax(s),  o_h = sum_t a_t v_t.
 // The workgroup serves all G query heads of g, so every K/V row is read from
 // HBM once per step whatever G is. The range is walked in sub-chunks of SC
-// positions whose K and V rows are loaded two sub-chunks ahead (double
-// buffer), so a range of up to 2*SC positions costs one HBM round trip. Per
-// sub-chunk:
-//   scores  LPK lanes per position (16-byte loads, interleaved so the LPK
-//           lanes read LPK*16 contiguous bytes), G fp64 dots, DPP lane sums;
-//   softmax per head, online in fp64: running max m and sum l, rescale
-//           factor e^{m_old - m_new} for what was accumulated before;
-//   values  thread = (float4 column f, position slot), G fp64 double4
-//           accumulators.
+// positions, grouped into super-chunks of up to kSuperPos positions. K rows
+// stream two sub-chunks ahead across the whole range; the V rows of a
+// super-chunk's first two sub-chunks are loaded when its scores start, the
+// rest two ahead while its values accumulate. Per super-chunk:
+//   scores  per sub-chunk: LPK lanes per position (16-byte loads,
+//           interleaved so the LPK lanes read LPK*16 contiguous bytes), G fp64
+//           dots, DPP lane sums, into LDS;
+//   softmax per head, online in fp64 over super-chunks: the super-chunk's
+//           maximum, e^{s - m} for each of its positions, running max m and
+//           sum l, rescale factor e^{m_old - m_new} for what was accumulated
+//           before (one pass and three barriers per super-chunk);
+//   values  per sub-chunk: thread = (float4 column f, position slot), G fp64
+//           double4 accumulators.
 // On return the slot partial sums of the values sit in LDS (attn_value sums
 // them in a fixed order) with the running (m, l) of each head.
 //
@@ -39,6 +43,7 @@ namespace l2d {
 constexpr int kMaxG = 8;    // query heads per kv head held in registers
 constexpr int kMaxKPT = 4;  // K float4 per lane per sub-chunk
 constexpr int kMaxVPT = 4;  // V float4 per thread per sub-chunk
+constexpr int kSuperPos = 128;  // positions per softmax pass (a whole number of sub-chunks)
 
 struct AttnShape {
     int F;      // float4 per head row
@@ -65,12 +70,18 @@ __host__ __device__ inline AttnShape attn_shape(int hs)
     return a;
 }
 
+// positions per super-chunk: whole sub-chunks, at most kSuperPos (at least one)
+__host__ __device__ inline int attn_super_pos(const AttnShape& a)
+{
+    return a.sc >= kSuperPos ? a.sc : (kSuperPos / a.sc) * a.sc;
+}
+
 template <int NT>
 __host__ __device__ inline size_t attn_core_lds_bytes(int G, int hs)
 {
     const AttnShape a = attn_shape<NT>(hs);
     const size_t q = (((size_t)G * hs * 4) + 15) & ~(size_t)15;
-    const size_t sc = (size_t)G * a.sc * 8;
+    const size_t sc = (size_t)G * attn_super_pos(a) * 8;
     const size_t stats = (size_t)3 * kMaxG * 8;
     const size_t red = (size_t)a.nred * G * hs * 8;
     return q + sc + stats + red;
@@ -94,12 +105,24 @@ __device__ __forceinline__ double lanes_sum_f64(double v, int width)
         const int lo = dpp_xor2(__double2loint(v)), hi = dpp_xor2(__double2hiint(v));
         v += __hiloint2double(hi, lo);
     }
-    for (int m = 4; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    // every lane of a quad now holds the same partial sum: the half-row and
+    // row mirrors pair it with the other quad / half-row, as xor 4 / xor 8
+    if (width >= 8) {
+        const int lo = dpp_hmirror(__double2loint(v)), hi = dpp_hmirror(__double2hiint(v));
+        v += __hiloint2double(hi, lo);
+    }
+    if (width >= 16) {
+        const int lo = dpp_mirror(__double2loint(v)), hi = dpp_mirror(__double2hiint(v));
+        v += __hiloint2double(hi, lo);
+    }
+    for (int m = 16; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
     return v;
 }
 
-struct KVBuf {
+struct KBuf {
     f32x4 k[kMaxKPT];
+};
+struct VBuf {
     f32x4 v[kMaxVPT];
 };
 
@@ -116,34 +139,36 @@ struct AttnRange {
     int last0;        // last position the first token may see (causal limit)
 };
 
-// K and V rows of positions [t0, t0 + n) (n <= sc). Rows written in an
-// earlier launch take plain loads; the fresh row a device-scope load.
+// K rows, then V rows, of positions [t0, t0 + n) (n <= sc). Rows written in
+// an earlier launch take plain loads; the fresh row a device-scope load.
 template <int NT>
-__device__ __forceinline__ void load_kv(KVBuf& b, const AttnRange& r, const AttnShape& a, int t0, int n)
+__device__ __forceinline__ void load_k(KBuf& b, const AttnRange& r, const AttnShape& a, int t0, int n)
 {
     const int tid = threadIdx.x;
-    {
-        const int tl = tid / a.lpk, sub = tid % a.lpk;
-        const bool ok = tl < n;
-        const int t = t0 + (ok ? tl : 0);
-        const float* row = r.kc + (size_t)t * r.kvd + (size_t)r.g * r.hs;
+    const int tl = tid / a.lpk, sub = tid % a.lpk;
+    const bool ok = tl < n;
+    const int t = t0 + (ok ? tl : 0);
+    const float* row = r.kc + (size_t)t * r.kvd + (size_t)r.g * r.hs;
 #pragma unroll
-        for (int k = 0; k < kMaxKPT; k++) {
-            const bool use = ok && k < a.kpt;
-            const float* pk = row + 4 * (sub + a.lpk * k);
-            b.k[k] = use ? (t == r.fresh ? ld_dev4(pk) : *(const f32x4*)pk) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int k = 0; k < kMaxKPT; k++) {
+        const bool use = ok && k < a.kpt;
+        const float* pk = row + 4 * (sub + a.lpk * k);
+        b.k[k] = use ? (t == r.fresh ? ld_dev4(pk) : *(const f32x4*)pk) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    {
-        const int f = tid % a.F, slot = tid / a.F;
+}
+
+template <int NT>
+__device__ __forceinline__ void load_v(VBuf& b, const AttnRange& r, const AttnShape& a, int t0, int n)
+{
+    const int tid = threadIdx.x;
+    const int f = tid % a.F, slot = tid / a.F;
 #pragma unroll
-        for (int j = 0; j < kMaxVPT; j++) {
-            const int tl = slot + a.slots * j;
-            const bool ok = slot < a.slots && j < a.vpt && tl < n;
-            const int t = t0 + (ok ? tl : 0);
-            const float* pv = r.vc + (size_t)t * r.kvd + (size_t)r.g * r.hs + 4 * f;
-            b.v[j] = ok ? (t == r.fresh ? ld_dev4(pv) : *(const f32x4*)pv) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int j = 0; j < kMaxVPT; j++) {
+        const int tl = slot + a.slots * j;
+        const bool ok = slot < a.slots && j < a.vpt && tl < n;
+        const int t = t0 + (ok ? tl : 0);
+        const float* pv = r.vc + (size_t)t * r.kvd + (size_t)r.g * r.hs + 4 * f;
+        b.v[j] = ok ? (t == r.fresh ? ld_dev4(pv) : *(const f32x4*)pv) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -160,7 +185,7 @@ struct AttnLds {
     {
         qs = (float*)smem;
         sc = (double*)(smem + ((((size_t)G * hs * 4) + 15) & ~(size_t)15));
-        m_run = sc + (size_t)G * a.sc;
+        m_run = sc + (size_t)G * attn_super_pos(a);
         l_run = m_run + kMaxG;
         alpha = l_run + kMaxG;
         red = alpha + kMaxG;
@@ -186,10 +211,16 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
     const int nsub = (n + a.sc - 1) / a.sc;
     AttnLds<NT> L(smem, G, hs, a);
 
-    // the first two sub-chunks' K/V loads, then q
-    KVBuf A, B;
-    load_kv<NT>(A, r, a, r0, min(a.sc, n));
-    if (nsub > 1) load_kv<NT>(B, r, a, r0 + a.sc, min(a.sc, n - a.sc));
+    const int P = attn_super_pos(a);       // positions per super-chunk
+    const int spc = P / a.sc;               // sub-chunks per super-chunk
+    const int nsup = (n + P - 1) / P;
+    auto sub_n = [&](int s) { return min(a.sc, n - s * a.sc); };
+
+    // the first two sub-chunks' K loads, then q
+    KBuf KA, KB;
+    VBuf VA, VB;
+    load_k<NT>(KA, r, a, r0, sub_n(0));
+    if (nsub > 1) load_k<NT>(KB, r, a, r0 + a.sc, sub_n(1));
     for (int i = tid; i < G * hs; i += NT) {
         const int h = i / hs;
         // q written in this launch (fresh >= 0: the persistent step) needs a
@@ -209,46 +240,86 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
 #pragma unroll
     for (int h = 0; h < KG; h++) ax[h] = ay[h] = az[h] = aw[h] = 0.0;
 
-    auto step = [&](KVBuf& cur, int s) {
+    // scores of sub-chunk s into LDS at its offset in the super-chunk, then
+    // the K buffer takes sub-chunk s + 2
+    auto scores = [&](KBuf& cur, int s, int off) {
         const int t0 = r0 + s * a.sc;
-        const int m = min(a.sc, n - s * a.sc);
-        // scores
-        {
-            const int tl = tid / a.lpk, sub = tid % a.lpk;
-            const f32x4* q4 = (const f32x4*)L.qs;
-            double sv[KG];
+        const int m = sub_n(s);
+        const int tl = tid / a.lpk, sub = tid % a.lpk;
+        const f32x4* q4 = (const f32x4*)L.qs;
+        double sv[KG];
 #pragma unroll
-            for (int h = 0; h < KG; h++) {
-                double acc = 0.0;
+        for (int h = 0; h < KG; h++) {
+            double acc = 0.0;
 #pragma unroll
-                for (int k = 0; k < kMaxKPT; k++) {
-                    if (k < a.kpt) {
-                        const f32x4 qv = q4[(size_t)h * a.F + sub + a.lpk * k];
-                        const f32x4 kv = cur.k[k];
-                        acc += (double)qv.x * (double)kv.x;
-                        acc += (double)qv.y * (double)kv.y;
-                        acc += (double)qv.z * (double)kv.z;
-                        acc += (double)qv.w * (double)kv.w;
+            for (int k = 0; k < kMaxKPT; k++) {
+                if (k < a.kpt) {
+                    const f32x4 qv = q4[(size_t)h * a.F + sub + a.lpk * k];
+                    const f32x4 kv = cur.k[k];
+                    acc += (double)qv.x * (double)kv.x;
+                    acc += (double)qv.y * (double)kv.y;
+                    acc += (double)qv.z * (double)kv.z;
+                    acc += (double)qv.w * (double)kv.w;
+                }
+            }
+            sv[h] = lanes_sum_f64(acc, a.lpk);
+        }
+        if (sub == 0 && tl < m)
+#pragma unroll
+            for (int h = 0; h < KG; h++)
+                L.sc[(size_t)h * P + off + tl] = t0 + tl <= r.last0 + h / r.Gt ? sv[h] * scale : -INFINITY;
+        if (s + 2 < nsub) load_k<NT>(cur, r, a, t0 + 2 * a.sc, sub_n(s + 2));
+    };
+    // values of sub-chunk s (weights at its offset in the super-chunk), then
+    // the V buffer takes sub-chunk s + 2 if it lies in the same super-chunk
+    auto values = [&](VBuf& cur, int s, int off, int s_end) {
+        const int t0 = r0 + s * a.sc;
+        const int m = sub_n(s);
+        if (vslot < a.slots) {
+#pragma unroll
+            for (int j = 0; j < kMaxVPT; j++) {
+                const int tl = vslot + a.slots * j;
+                if (j < a.vpt && tl < m) {
+                    const f32x4 vv = cur.v[j];
+#pragma unroll
+                    for (int h = 0; h < KG; h++) {
+                        const double e = L.sc[(size_t)h * P + off + tl];
+                        ax[h] += e * (double)vv.x;
+                        ay[h] += e * (double)vv.y;
+                        az[h] += e * (double)vv.z;
+                        aw[h] += e * (double)vv.w;
                     }
                 }
-                sv[h] = lanes_sum_f64(acc, a.lpk);
             }
-            if (sub == 0 && tl < m)
-#pragma unroll
-                for (int h = 0; h < KG; h++)
-                    L.sc[(size_t)h * a.sc + tl] = t0 + tl <= r.last0 + h / r.Gt ? sv[h] * scale : -INFINITY;
+        }
+        if (s + 2 < s_end) load_v<NT>(cur, r, a, t0 + 2 * a.sc, sub_n(s + 2));
+    };
+
+    for (int c = 0; c < nsup; c++) {
+        const int s0 = c * spc, s1 = min(nsub, s0 + spc);
+        const int mP = min(P, n - c * P);  // positions of this super-chunk
+        // V rows of its first two sub-chunks, in flight during the scores
+        load_v<NT>(VA, r, a, r0 + s0 * a.sc, sub_n(s0));
+        if (s0 + 1 < s1) load_v<NT>(VB, r, a, r0 + (s0 + 1) * a.sc, sub_n(s0 + 1));
+        // scores; K buffer of sub-chunk s is KA for even s, KB for odd
+        for (int s = s0; s < s1; s++) {
+            if ((s & 1) == 0)
+                scores(KA, s, (s - s0) * a.sc);
+            else
+                scores(KB, s, (s - s0) * a.sc);
         }
         sync();
+        // softmax over the super-chunk, one wave per head
         for (int h = wave; h < G; h += NT / kWave) {
             double mx = -INFINITY;
-            for (int t = lane; t < m; t += kWave) mx = fmax(mx, L.sc[(size_t)h * a.sc + t]);
+            for (int t = lane; t < mP; t += kWave) mx = fmax(mx, L.sc[(size_t)h * P + t]);
             mx = wave_max(mx);
             const double mo = L.m_run[h];
             const double mn = fmax(mo, mx);
             double l = 0.0;
-            for (int t = lane; t < m; t += kWave) {
-                const double e = exp(L.sc[(size_t)h * a.sc + t] - mn);
-                L.sc[(size_t)h * a.sc + t] = e;
+            for (int t = lane; t < mP; t += kWave) {
+                const double e = exp(L.sc[(size_t)h * P + t] - mn);
+                L.sc[(size_t)h * P + t] = e;
                 l += e;
             }
             l = wave_sum(l);
@@ -260,7 +331,6 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
             }
         }
         sync();
-        // values
         if (vslot < a.slots) {
 #pragma unroll
             for (int h = 0; h < KG; h++) {
@@ -270,29 +340,16 @@ __device__ __forceinline__ void attn_range(const AttnRange& r, unsigned char* sm
                 az[h] *= al;
                 aw[h] *= al;
             }
-#pragma unroll
-            for (int j = 0; j < kMaxVPT; j++) {
-                const int tl = vslot + a.slots * j;
-                if (j < a.vpt && tl < m) {
-                    const f32x4 vv = cur.v[j];
-#pragma unroll
-                    for (int h = 0; h < KG; h++) {
-                        const double e = L.sc[(size_t)h * a.sc + tl];
-                        ax[h] += e * (double)vv.x;
-                        ay[h] += e * (double)vv.y;
-                        az[h] += e * (double)vv.z;
-                        aw[h] += e * (double)vv.w;
-                    }
-                }
-            }
         }
-        sync();
-        // refill the buffer just consumed with the sub-chunk after next
-        if (s + 2 < nsub) load_kv<NT>(cur, r, a, t0 + 2 * a.sc, min(a.sc, n - (s + 2) * a.sc));
-    };
-    for (int s = 0; s < nsub; s += 2) {
-        step(A, s);
-        if (s + 1 < nsub) step(B, s + 1);
+        // values; V buffer of the super-chunk's i-th sub-chunk is VA for even
+        // i, VB for odd
+        for (int s = s0; s < s1; s++) {
+            if (((s - s0) & 1) == 0)
+                values(VA, s, (s - s0) * a.sc, s1);
+            else
+                values(VB, s, (s - s0) * a.sc, s1);
+        }
+        sync();  // L.sc is rewritten by the next super-chunk
     }
 
     // the value accumulators of the position slots, into LDS

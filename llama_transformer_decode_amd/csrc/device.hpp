@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace l2d {
 
 constexpr int kWave = 64;
@@ -11,29 +13,6 @@ constexpr int kWave = 64;
 // native clang vectors: 16-byte global loads (plain and nontemporal)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// fp64 sum over the 64 lanes of a wavefront; every lane gets the total.
-// The xor-butterfly order is fixed, so the result is deterministic.
-__device__ __forceinline__ double wave_sum(double v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-__device__ __forceinline__ double wave_max(double v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmax(v, __shfl_xor(v, m, kWave));
-    return v;
-}
-
-__device__ __forceinline__ float wave_maxf(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
-}
 
 // sum of an int over aligned groups of `width` lanes (width a power of two <= 64)
 __device__ __forceinline__ int group_sum_i32(int v, int width)
@@ -128,13 +107,21 @@ __device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_mov_dpp
 
 __device__ __forceinline__ float dpp_xor1f(float v) { return __int_as_float(dpp_xor1(__float_as_int(v))); }
 __device__ __forceinline__ float dpp_xor2f(float v) { return __int_as_float(dpp_xor2(__float_as_int(v))); }
+// row_half_mirror (lane j <-> 7 - j within 8 lanes) and row_mirror (j <-> 15
+// - j within 16): once every lane of a quad (of a half-row) holds the same
+// value, they pair it with the other quad (half-row) as xor 4 (xor 8) would
+__device__ __forceinline__ int dpp_hmirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror(int v) { return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false); }
 
-// sum of an int over aligned groups of `width` lanes (power of two <= 64)
+// sum of an int over aligned groups of `width` lanes (power of two <= 64);
+// DPP up to 16 lanes, lane shuffles beyond
 __device__ __forceinline__ int lanes_sum_i32(int v, int width)
 {
     if (width >= 2) v += dpp_xor1(v);
     if (width >= 4) v += dpp_xor2(v);
-    for (int m = 4; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    if (width >= 8) v += dpp_hmirror(v);
+    if (width >= 16) v += dpp_mirror(v);
+    for (int m = 16; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
     return v;
 }
 
@@ -143,7 +130,9 @@ __device__ __forceinline__ float lanes_max_f32(float v, int width)
 {
     if (width >= 2) v = fmaxf(v, dpp_xor1f(v));
     if (width >= 4) v = fmaxf(v, dpp_xor2f(v));
-    for (int m = 4; m < width; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    if (width >= 8) v = fmaxf(v, __int_as_float(dpp_hmirror(__float_as_int(v))));
+    if (width >= 16) v = fmaxf(v, __int_as_float(dpp_mirror(__float_as_int(v))));
+    for (int m = 16; m < width; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
     return v;
 }
 
@@ -161,6 +150,54 @@ __device__ __forceinline__ double dpp_f64(double v)
     const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, false);
     const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, false);
     return __hiloint2double(hi, lo);
+}
+
+// value of lane l of a double (uniform result)
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+// fp64 sum over the 64 lanes of a wavefront; every lane gets the total. Fixed
+// order, so the result is deterministic: within each row of 16 lanes quad xor
+// 1, quad xor 2, half-row mirror, row mirror (DPP, a few cycles each), then the
+// four row totals read from lanes 0, 16, 32, 48 and added as (r0 + r1) + (r2 +
+// r3).
+__device__ __forceinline__ double wave_sum(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// fp64 maximum over the 64 lanes (every lane gets it), the same steps
+__device__ __forceinline__ double wave_max(double v)
+{
+    v = fmax(v, dpp_f64<0xB1>(v));
+    v = fmax(v, dpp_f64<0x4E>(v));
+    v = fmax(v, dpp_f64<0x141>(v));
+    v = fmax(v, dpp_f64<0x140>(v));
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
+// fp32 maximum over the 64 lanes (every lane gets it)
+__device__ __forceinline__ float wave_maxf(float v)
+{
+    auto mv = [](float x, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    v = fmaxf(v, mv(v, std::integral_constant<int, 0xB1>()));
+    v = fmaxf(v, mv(v, std::integral_constant<int, 0x4E>()));
+    v = fmaxf(v, mv(v, std::integral_constant<int, 0x141>()));
+    v = fmaxf(v, mv(v, std::integral_constant<int, 0x140>()));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // fp64 sum over the 64 lanes with DPP only (fixed order); the total lands in
