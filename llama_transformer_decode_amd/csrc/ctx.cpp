@@ -597,20 +597,38 @@ int setup_stream(l2d_ctx* ctx, int cus)
     HIP_TRY(ctx, hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, ctx->device));
     if (!coop) return L2D_OK;
     const int kg = (int)ctx->G / gsplit;
-    SPlan sp{ctx->d, ctx->h, ctx->L, ctx->kvd, ctx->V, cus, stream_workers(), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    const size_t lds = stream_lds_bytes(sp, kg, (int)ctx->hs);
-    if (stream_blocks_per_cu(kg, (int)ctx->hs, lds) < 1) return L2D_OK;
+    // the workers' weight base is the q/k/v codes; every matrix kind's codes
+    // and scales as byte offsets from it
+    const int8_t* base = (const int8_t*)ctx->wqkv;
+    auto off = [&](const void* q) { return (int64_t)((intptr_t)q - (intptr_t)base); };
+    SPlan sp{ctx->d, ctx->h, ctx->L, ctx->kvd, ctx->V, cus, stream_workers(),
+             off(ctx->wqkv), off(ctx->wo), off(ctx->w13), off(ctx->w2), off(ctx->wcls),
+             off(ctx->wqkv_s), off(ctx->wo_s), off(ctx->w13_s), off(ctx->w2_s), off(ctx->wcls_s)};
+    if (!sd_fits(sp)) return L2D_OK;
+    std::vector<SDesc> tab;
+    std::vector<int32_t> cnt;
+    int64_t stride = 0;
+    stream_tables(sp, tab, cnt, &stride);
+    const size_t lds = stream_lds_bytes(sp, kg, (int)ctx->hs, stride);
+    if (lds > 160 * 1024 || stream_blocks_per_cu(kg, (int)ctx->hs, lds) < 1) return L2D_OK;
     const int64_t cols = ctx->nkv * gsplit;
     const int64_t ns = stream_splits(ctx->nkv, gsplit, cus, ctx->S, (int)ctx->hs);
     ALLOC(ctx->ssync, sizeof(StreamSync));
+    ALLOC(ctx->sflags, (size_t)cus * 4);
     ALLOC(ctx->shead_ctr, (size_t)cols * 32 * 4);
     ALLOC(ctx->spart_o, (size_t)cols * ns * kg * ctx->hs * 8);
     ALLOC(ctx->spart_ml, (size_t)cols * ns * kg * 2 * 8);
     ALLOC(ctx->sdummy, 8192);
+    ALLOC(ctx->swtab, tab.size() * sizeof(SDesc));
+    ALLOC(ctx->swcnt, cnt.size() * sizeof(int32_t));
+    HIP_TRY(ctx, hipMemcpyAsync(ctx->swtab, tab.data(), tab.size() * sizeof(SDesc), hipMemcpyHostToDevice, ctx->stream));
+    HIP_TRY(ctx, hipMemcpyAsync(ctx->swcnt, cnt.data(), cnt.size() * sizeof(int32_t), hipMemcpyHostToDevice, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->ssync, 0, sizeof(StreamSync), ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->sflags, 0, (size_t)cus * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->shead_ctr, 0, (size_t)cols * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->sdummy, 0, 8192, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->swtab_stride = stride;
     ctx->stream_grid = cus;
     ctx->stream_kg = kg;
     ctx->stream_gsplit = gsplit;
@@ -625,10 +643,10 @@ int setup_stream(l2d_ctx* ctx, int cus)
 // One launch of the persistent step kernel for (token, pos).
 hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
 {
-    const uint32_t nb = stream_barriers((int)ctx->L);
-    if (ctx->stream_epoch > (1u << 25) - nb) {
-        // the arrival counters count up across launches: restart them from zero
-        hipError_t e = hipMemsetAsync(ctx->ssync, 0, sizeof(StreamSync), ctx->stream);
+    const uint32_t nb = stream_epochs((int)ctx->L);
+    if (ctx->stream_epoch > (1u << 31) - nb) {
+        // the progress flags count up across launches: restart them from zero
+        hipError_t e = hipMemsetAsync(ctx->sflags, 0, (size_t)ctx->stream_grid * 4, ctx->stream);
         if (e != hipSuccess) return e;
         ctx->stream_epoch = 0;
     }
@@ -677,16 +695,12 @@ hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool gre
     p.part_ml = ctx->spart_ml;
     p.head_ctr = ctx->shead_ctr;
     p.sync = ctx->ssync;
+    p.flags = ctx->sflags;
     p.dummy = ctx->sdummy;
-    {
-        const int8_t* const codes[5] = {p.wqkv, p.wo, p.w13, p.w2, p.wcls};
-        const float* const scales[5] = {p.wqkv_s, p.wo_s, p.w13_s, p.w2_s, p.wcls_s};
-        p.wbase = p.wqkv;
-        for (int k = 0; k < 5; k++) {
-            p.wofs[k] = (int64_t)((intptr_t)codes[k] - (intptr_t)p.wbase);
-            p.sofs[k] = (int64_t)((intptr_t)scales[k] - (intptr_t)p.wbase);
-        }
-    }
+    p.wbase = p.wqkv;
+    p.wtab = ctx->swtab;
+    p.wtab_stride = ctx->swtab_stride;
+    p.wcnt = ctx->swcnt;
     p.token = token;
     p.pos = pos;
     p.greedy = greedy ? 1 : 0;
@@ -715,10 +729,11 @@ int stream_check(l2d_ctx* ctx)
     if (err == 0) return L2D_OK;
     const int64_t cols = ctx->nkv * ctx->stream_gsplit;
     HIP_TRY(ctx, hipMemsetAsync(ctx->ssync, 0, sizeof(StreamSync), ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->sflags, 0, (size_t)ctx->stream_grid * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->shead_ctr, 0, (size_t)cols * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     ctx->stream_epoch = 0;
-    return fail(ctx, L2D_EHIP, "step kernel: a grid barrier wait gave up; the step's results are invalid");
+    return fail(ctx, L2D_EHIP, "step kernel: a wait for another workgroup gave up; the step's results are invalid");
 }
 
 hipError_t begin(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy,

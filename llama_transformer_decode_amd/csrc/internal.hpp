@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace l2d {
 
 // DT_Q4: 4-bit weight codes, two per byte, groups of 32 with an fp32 scale
@@ -203,13 +205,13 @@ hipError_t launch_quantize(const float* x, int64_t n, int32_t gs, int8_t* q, flo
 // (stream.hip): worker waves stream the weights, control waves run the grid
 // barriers, prologues, epilogues and attention.
 
-// Grid barrier state: arrival counters per XCD (workgroup b counts on
-// counter b % 8), each on its own 128-byte line, counting up across
-// launches; and an error word set when a wait gives up.
+// Error word of the step kernel: set when a wait gives up (every wave then
+// leaves, and the host reports the step invalid).
 struct StreamSync {
-    uint32_t arrive[8][32];
     uint32_t err[32];
 };
+
+struct SDesc;
 
 struct StreamParams {
     int32_t d, h, L, nkv, hs, kvd, G, V, S;
@@ -249,16 +251,20 @@ struct StreamParams {
     double* part_ml;     // [nkv * gsplit][nsplit][G / gsplit][2]
     uint32_t* head_ctr;  // [nkv * gsplit][32]: ranges of the column finished (zero between uses)
     StreamSync* sync;
+    // progress of each workgroup: the epoch of the last phase whose outputs it
+    // has stored (each phase of each layer of each launch has its own epoch)
+    uint32_t* flags;
     const int8_t* dummy; // 8 KiB of zeroed device memory: the loads past the end of a worker's stream
-    // the workers' view of the five matrices (q/k/v, output, w1/w3, w2,
-    // classifier; SKind order): byte offsets of each one's codes and scales
-    // from wbase, read with scalar loads by kind
+    // the workers' chunk tables (stream_tables): worker wid's at
+    // wtab[wid * wtab_stride], wcnt[2 wid] items per layer, wcnt[2 wid + 1]
+    // classifier items; offsets from wbase
     const int8_t* wbase;
-    int64_t wofs[5];
-    int64_t sofs[5];
+    const SDesc* wtab;
+    int64_t wtab_stride;
+    const int32_t* wcnt;
     // this launch
     int32_t token, pos, greedy;
-    uint32_t epoch0;     // grid barriers completed by earlier launches
+    uint32_t epoch0;     // epochs used by earlier launches (the first phase of this one is epoch0 + 1)
     double temperature;  // 0: argmax
     uint64_t seed;
     // diagnostics: when set, clock stamps of each workgroup's control events
@@ -270,12 +276,14 @@ struct StreamParams {
 // control events per workgroup in a step kernel trace
 inline int64_t stream_trace_events(int L) { return 1 + 6 * (4 * (int64_t)L + 1); }
 
-// grid barriers one launch of the step kernel performs
-inline uint32_t stream_barriers(int L) { return 5u * (uint32_t)L; }
+// epochs one launch of the step kernel uses: five per layer (q/k/v,
+// attention, output, w1/w3, w2) and one spare
+inline uint32_t stream_epochs(int L) { return 5u * (uint32_t)L + 1u; }
 
 struct SPlan;
+void stream_tables(const SPlan& s, std::vector<SDesc>& tab, std::vector<int32_t>& cnt, int64_t* stride);
 bool stream_supported(int dt, int gs, int64_t d, int64_t h, int G, int gsplit, int hs);
-size_t stream_lds_bytes(const SPlan& s, int kg, int hs);
+size_t stream_lds_bytes(const SPlan& s, int kg, int hs, int64_t tstride);
 int stream_threads();
 int stream_splits(int64_t nkv, int64_t gsplit, int64_t nwg, int64_t S, int hs);
 int stream_workers();

@@ -91,8 +91,12 @@ struct l2d_ctx {
     int stream_nsplit = 1;
     int stream_ymax = 0;
     size_t stream_lds = 0;
-    uint32_t stream_epoch = 0;    // grid barriers completed so far
+    uint32_t stream_epoch = 0;    // progress-flag epochs used so far
     l2d::StreamSync* ssync = nullptr;
+    uint32_t* sflags = nullptr;   // [stream_grid] progress flags
+    l2d::SDesc* swtab = nullptr;  // workers' chunk tables
+    int32_t* swcnt = nullptr;
+    int64_t swtab_stride = 0;
     uint32_t* shead_ctr = nullptr;
     double* spart_o = nullptr;
     double* spart_ml = nullptr;

@@ -9,32 +9,40 @@
 // for the previous phase. So each workgroup is split in two roles:
 //
 //   worker waves (kSNW of them) do nothing but stream weight chunks and dot
-//   them with the matvec input held in LDS. Each keeps kSNB chunks in flight
-//   in registers, and its stream runs through all matvec phases of the step
-//   without a break: the loads of the next phase's rows go out while the
-//   current phase finishes and while the grid synchronises; only the use of
-//   a chunk waits for its phase's input. A worker touches no activation in
-//   global memory (its vector memory queue holds weight loads only, so no
-//   wait of it is held up behind the prefetch); it leaves each row's sum in
-//   LDS.
+//   them with the matvec input held in LDS. Each walks a table of chunk
+//   descriptors built on the host (one scalar load per chunk) and keeps kSNB
+//   chunks in flight in registers; its stream runs through all matvec
+//   phases of the step without a break: the loads of the next phase's rows
+//   go out while the current phase finishes and while the workgroups wait
+//   for each other; only the use of a chunk waits for its phase's input. A
+//   worker touches no activation in global memory; it leaves each row's sum
+//   in LDS.
 //
-//   control waves (kSAW of them, 256 threads) run everything else: the grid
-//   barrier between phases (a counter per XCD, polled with device-scope
-//   loads), the input of each matvec (RMSNorm and Q8_0 quantisation of the
-//   activation vector into LDS, the same arithmetic as the per-phase
-//   kernels), the epilogue of the workgroup's rows (RoPE and the cache
-//   write, residual add, SwiGLU, logits and argmax) and the attention
-//   (split-position GQA ranges with the attn_core computation, the last
-//   range of a kv head merging them).
+//   control waves (kSAW of them, 256 threads) run everything else: the wait
+//   for the previous phase's outputs, the input of each matvec (RMSNorm and
+//   Q8_0 quantisation of the activation vector into LDS, the same arithmetic
+//   as the per-phase kernels), the epilogue of the workgroup's rows (RoPE and
+//   the cache write, residual add, SwiGLU, logits and argmax) and the
+//   attention (split-position GQA ranges with the attn_core computation, the
+//   last range of a kv head merging them).
+//
+// Workgroups hand over through progress flags, not grid barriers: after its
+// epilogue (or its attention items) a workgroup waits until its own stores
+// are complete and then stores the phase's epoch into its flag; a consumer
+// waits until every flag has reached the epoch of the phase it needs, then
+// reads the data. Each phase of each layer of each launch has its own epoch,
+// so flags only grow. A workgroup with no rows in a phase skips the wait and
+// the input: it reads nothing and stores nothing there.
 //
 // Control and workers meet in LDS only: `ready` (the input of phase p is in
 // LDS) and `done` (a worker finished phase p and left its row sums in LDS).
 // Values passed between workgroups within the launch use device-scope
-// loads and stores (ld_dev / st_dev). Every wait is bounded: a grid barrier
-// that waits too long sets an error word and every wave leaves.
+// loads and stores (ld_dev / st_dev). Every wait is bounded: a wait that
+// gives up sets an error word and every wave leaves.
 //
-// Addresses, row ownership and the order of each worker's stream come from
-// stream_plan.hpp, whose functions the host checker runs over every wave.
+// The row ranges, the attention items and the workers' chunk tables come
+// from stream_plan.hpp, whose functions the host checker runs over every
+// wave of a launch.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
@@ -49,7 +57,7 @@ constexpr int kSA = kSAW * kWave;          // control threads per workgroup
 constexpr int kSNW = 4;                    // worker waves per workgroup
 constexpr int kSNB = 10;                   // weight chunks in flight per worker
 constexpr int kST = kSA + kSNW * kWave;    // threads per workgroup
-constexpr uint32_t kGridSpin = 1u << 22;   // grid-barrier polls before giving up
+constexpr uint32_t kGridSpin = 1u << 22;   // polls of the progress flags before giving up
 constexpr int kSMaxSplits = 16;            // attention position splits per kv head column
 constexpr uint32_t kLdsSpin = 1u << 27;    // LDS polls before giving up
 
@@ -68,15 +76,18 @@ struct SCtl {
 
 // dynamic LDS layout (byte offsets)
 struct SLds {
-    size_t runs, rope, y, res, in_q, in_s, attn, total;
+    size_t tab, rope, y, res, in_q, in_s, attn, total;
 };
 
-__host__ __device__ inline SLds stream_lds_layout(int64_t ymax, int64_t kmax, int64_t hs, size_t attn_bytes)
+// tstride: descriptors per worker table (each worker's table is copied to
+// LDS when the kernel starts)
+__host__ __device__ inline SLds stream_lds_layout(int64_t ymax, int64_t kmax, int64_t hs, size_t attn_bytes,
+                                                  int64_t tstride)
 {
     SLds o;
     auto up = [](size_t v) { return (v + 15) & ~(size_t)15; };
-    o.runs = up(sizeof(SCtl));
-    o.rope = o.runs + up((size_t)kSNW * 5 * sizeof(SKindRun));
+    o.tab = up(sizeof(SCtl));
+    o.rope = o.tab + (size_t)kSNW * (size_t)tstride * sizeof(SDesc);
     o.y = o.rope + up((size_t)hs * 4);
     o.res = o.y + up((size_t)ymax * 4);
     o.in_q = o.res + up((size_t)ymax * 4);
@@ -155,51 +166,72 @@ struct SChunk {
     float s;     // the group's weight scale
 };
 
-// The loads of the cursor's chunk (live), or of a cache-resident dummy
-// address (past the end of the stream, or once the step has given up), so
-// every ring slot issues the same loads and the compiler's wait counts stay
-// exact. No select or branch on live around the loads (the compiler turned
-// one into two load paths joined by register copies, each copy waiting for
-// its load): the base moves to the dummy buffer and every offset is
-// multiplied by keep (0 or 1).
-__device__ __forceinline__ void sk_load(SChunk& b, const StreamParams& P, const SCur& u, bool live)
+// Loads of one table item (desc e, layer `layer`): lane j < nb reads the
+// four 16-byte quarters of group j of the chunk at w0 + 16 (nb q + j) and
+// its scale at s0 + 4 j; lanes past the chunk's groups repeat the last one.
+// A phantom item, or no item at all (live false: past the end of the stream,
+// or the step has given up), reads the zeroed dummy buffer instead, so every
+// ring slot issues the same loads and the compiler's wait counts stay exact.
+// The chunk's meta word goes with it for its use.
+__device__ __forceinline__ void sk_issue(SChunk& b, uint32_t& meta, const StreamParams& P, const SDesc& e,
+                                         int32_t layer, bool live)
 {
     const int lane = lane_id();
-    const int64_t keep = live ? 1 : 0;
-    const int32_t nb = sc_groups(u);
-    const int32_t jj = lane < nb ? lane : nb - 1;
-    const int8_t* W = P.dummy + keep * (P.wbase + u.woff + (int64_t)u.c * (64 * kSGS) - P.dummy);
-    const float* Ws = (const float*)(P.dummy + keep * (P.wbase + 4 * (u.soff + 64 * (int64_t)u.c) - P.dummy));
+    const bool real = live && (e.meta & SD_PHANTOM) == 0u;
+    meta = live ? e.meta : SD_PHANTOM;
+    const int nb = real ? sd_nb(e.meta) : 1;
+    const int8_t* cb = real ? P.wbase + e.w0 + (int64_t)layer * e.wl : P.dummy;
+    const int8_t* sb = real ? P.wbase + e.s0 + (int64_t)layer * e.sl : P.dummy;
+    const uint32_t j = lane < nb ? (uint32_t)lane : (uint32_t)(nb - 1);
 #pragma unroll
     for (int q = 0; q < 4; q++)
-        b.w[q] = __builtin_nontemporal_load((const i32x4*)(W + keep * 16 * (nb * q + jj)));
-    b.s = Ws[keep * jj];
+        b.w[q] = __builtin_nontemporal_load((const i32x4*)(cb + 16 * nb * q + 16u * j));
+    b.s = *(const float*)(sb + 4u * j);
 }
 
-// dot of the chunk with the input codes in LDS: lane j's exact int32 group
-// dot, scaled by the weight and input scales in fp64 (the per-phase GEMV's
-// arithmetic and order), added into acc
-__device__ __forceinline__ void sk_use(const SChunk& b, double& acc, const unsigned char* in_q,
-                                       const float* in_s, const SCur& u)
+// Lane j's term of one chunk: the exact int32 dot of group j with the input
+// codes in LDS (two independent partial sums: integer addition is exact, so
+// the order does not matter), scaled by the weight and input scales in fp64
+// (the per-phase GEMV's arithmetic and order); 0 for lanes past the chunk's
+// groups.
+__device__ __forceinline__ double sk_term(const SChunk& b, uint32_t m, const unsigned char* in_q,
+                                          const float* in_s)
 {
     const int lane = lane_id();
-    const int32_t nb = sc_groups(u);
-    const int32_t j = lane < nb ? lane : nb - 1;
-    const i32x4* xq = (const i32x4*)(in_q + u.c * (64 * kSGS));
+    const int nb = sd_nb(m), c = sd_c(m);
+    const int j = lane < nb ? lane : nb - 1;
+    const i32x4* xq = (const i32x4*)(in_q + c * (64 * kSGS));
     i32x4 xv[4];
 #pragma unroll
     for (int q = 0; q < 4; q++) xv[q] = xq[nb * q + j];
-    const double xsg = (double)in_s[64 * u.c + j];
-    int d = 0;
+    const double xsg = (double)in_s[64 * c + j];
+    int d0 = 0, d1 = 0;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        d = dot4_i8(b.w[q].x, xv[q].x, d);
-        d = dot4_i8(b.w[q].y, xv[q].y, d);
-        d = dot4_i8(b.w[q].z, xv[q].z, d);
-        d = dot4_i8(b.w[q].w, xv[q].w, d);
+    for (int q = 0; q < 2; q++) {
+        d0 = dot4_i8(b.w[q].x, xv[q].x, d0);
+        d1 = dot4_i8(b.w[q + 2].x, xv[q + 2].x, d1);
+        d0 = dot4_i8(b.w[q].y, xv[q].y, d0);
+        d1 = dot4_i8(b.w[q + 2].y, xv[q + 2].y, d1);
+        d0 = dot4_i8(b.w[q].z, xv[q].z, d0);
+        d1 = dot4_i8(b.w[q + 2].z, xv[q + 2].z, d1);
+        d0 = dot4_i8(b.w[q].w, xv[q].w, d0);
+        d1 = dot4_i8(b.w[q + 2].w, xv[q + 2].w, d1);
     }
-    const double t = ((double)d * (double)b.s) * xsg;
-    acc += lane < nb ? t : 0.0;
+    const double t = ((double)(d0 + d1) * (double)b.s) * xsg;
+    return lane < nb ? t : 0.0;
+}
+
+// Use of one chunk: its term added into the row's running sum acc; at the
+// row's last chunk the wave sum goes to the row's slot in y.
+__device__ __forceinline__ void sk_use(const SChunk& b, uint32_t m, double& acc, const unsigned char* in_q,
+                                       const float* in_s, float* y)
+{
+    acc += sk_term(b, m, in_q, in_s);
+    if (m & SD_ROWEND) {
+        acc = wave_sum_to_last(acc);
+        if (lane_id() == kWave - 1) y[sd_local(m)] = (float)acc;
+        acc = 0.0;
+    }
 }
 
 // LDS byte address of a pointer into the workgroup's LDS
@@ -258,70 +290,97 @@ __device__ __forceinline__ void trace_worker(const StreamParams& P, int64_t w, i
             __builtin_amdgcn_s_memrealtime();
 }
 
-// Move the worker from phase `from` (-1: none yet) to phase `to` (P: the
+// Move the worker from phase `from` (-1: none yet) to phase `to` (NP: the
 // end): report `from` done, then wait for the input of `to`. Every worker
-// passes through every phase (a phantom row where it has none).
-__device__ __forceinline__ bool sk_transition(SCtl* c, int64_t from, int64_t to, int64_t P)
+// passes through every phase (a phantom item where it has no rows).
+__device__ __forceinline__ bool sk_transition(SCtl* c, int64_t from, int64_t to, int64_t NP)
 {
     if (from >= 0) sk_signal_done(c);
-    return to >= P || sk_wait_ready(c, to);
+    return to >= NP || sk_wait_ready(c, to);
 }
 
-__device__ __forceinline__ void stream_worker(const StreamParams& P, SPlan s, unsigned char* smem,
-                                              const SLds& L, int64_t w)
+__device__ __forceinline__ void stream_worker(const StreamParams& P, unsigned char* smem, const SLds& L,
+                                              int64_t w)
 {
     SCtl* c = (SCtl*)smem;
     float* y = (float*)(smem + L.y);
     const unsigned char* in_q = smem + L.in_q;
     const float* in_s = (const float*)(smem + L.in_s);
-    const int64_t NP = sp_phases(s);
-    // this worker's rows of each matrix kind, once, into its LDS table
-    SKindRun* tab = (SKindRun*)(smem + L.runs) + 5 * w;
+    const int64_t NP = 4 * (int64_t)P.L + 1;
+    const int64_t wid = (int64_t)blockIdx.x * kSNW + w;
+    // this worker's table, copied into its LDS area once (a scalar load per
+    // chunk from global memory waited about 0.5 us behind the weight
+    // stream's traffic in L2; an LDS read does not)
+    const int32_t nL = __builtin_amdgcn_readfirstlane(P.wcnt[2 * wid]);
+    const int32_t nC = __builtin_amdgcn_readfirstlane(P.wcnt[2 * wid + 1]);
+    SDesc* tab = (SDesc*)(smem + L.tab) + w * P.wtab_stride;
     {
-        const SRows rows = sp_rows(s, blockIdx.x);
-        if (lane_id() < 5) tab[lane_id()] = sp_kind_run(s, rows, w, lane_id());
+        const i32x4* src = (const i32x4*)(P.wtab + wid * P.wtab_stride);
+        i32x4* dst = (i32x4*)tab;
+        for (int i = lane_id(); i < 2 * (nL + nC); i += kWave) dst[i] = src[i];
         lds_fence();
     }
-    // A ring of kSNB chunk buffers. Each pass uses the kSNB items the
-    // previous pass loaded (the load cursor is kSNB items ahead of the use
-    // cursor) and refills each buffer as soon as it is used; the first pass
-    // only loads. Every load is issued on every pass (a dummy one past the
-    // end of the stream, for a phantom row, or once the step has given up).
-    // The loop has no early exit: an exit edge inside it made the compiler
-    // wait for every load in flight before each chunk.
-    SCur lc, uc;
-    sc_begin(lc, tab, w);
-    uc = lc;
+    const int32_t total = P.L * nL + nC;  // far below 2^31 chunks per worker
+    // load cursor: table index lt of layer ll; after the last layer (ll ==
+    // L) the classifier's items follow at lt = nL, nL + 1, ...
+    int32_t lt = 0, ll = 0;
+    int32_t issued = 0, used = 0;
+    bool ok = true;
     SChunk buf[kSNB];
-    int64_t cur = -1;
-    bool ok = true, first = true;
+    uint32_t meta[kSNB];
+    // the descriptor of the next chunk to issue, read one refill ahead (a
+    // uniform LDS read, made scalar)
+    auto fetch = [&](int32_t i) {
+        const SDesc* ep = tab + i;
+        const i32x4 a = *(const i32x4*)ep;
+        const i32x4 b2 = *((const i32x4*)ep + 1);
+        SDesc e;
+        e.w0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(a.y) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane(a.x));
+        e.s0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(a.w) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane(a.z));
+        e.wl = __builtin_amdgcn_readfirstlane(b2.x);
+        e.sl = __builtin_amdgcn_readfirstlane(b2.y);
+        e.meta = (uint32_t)__builtin_amdgcn_readfirstlane(b2.z);
+        return e;
+    };
+    SDesc nxt = fetch(0);
+    auto refill = [&](int k) {
+        const bool live = ok && issued < total;
+        sk_issue(buf[k], meta[k], P, nxt, ll, live);
+        if (live) {
+            ++issued;
+            if (++lt == nL && ll < P.L) {
+                ++ll;
+                lt = ll < P.L ? 0 : nL;
+            }
+        }
+        nxt = fetch(ok && issued < total ? lt : 0);
+    };
+#pragma unroll
+    for (int k = 0; k < kSNB; k++) refill(k);
+    // Each pass uses the kSNB chunks the ring holds, in order, and refills
+    // each slot at once with the chunk kSNB ahead. The pass has no early
+    // exit: an exit edge inside it made the compiler wait for every load in
+    // flight before each chunk.
+    int64_t cur = -1;  // the phase being used: every phase starts with a first item
     double acc = 0.0;
     do {
 #pragma unroll
         for (int k = 0; k < kSNB; k++) {
-            if (!first && ok && !uc.end) {
-                const int64_t p = sc_phase(uc, s);
-                if (p != cur) {
+            if (ok && used < total) {
+                const uint32_t m = meta[k];
+                if (m & SD_FIRST) {
                     if (cur >= 0) trace_worker(P, w, cur, NP);
-                    ok = sk_transition(c, cur, p, NP);
-                    cur = p;
+                    ok = sk_transition(c, cur, cur + 1, NP);
+                    ++cur;
                 }
-                if (ok && !uc.phantom) {
-                    sk_use(buf[k], acc, in_q, in_s, uc);
-                    if (uc.c == uc.nch - 1) {
-                        acc = wave_sum_to_last(acc);
-                        if (lane_id() == kWave - 1) y[uc.local] = (float)acc;
-                        acc = 0.0;
-                    }
-                }
-                sc_step(uc, s, tab, w);
+                if (ok && (m & SD_PHANTOM) == 0u) sk_use(buf[k], m, acc, in_q, in_s, y);
+                ++used;
             }
-            const bool live = ok && !lc.end && !lc.phantom;
-            sk_load(buf[k], P, lc, live);
-            sc_step(lc, s, tab, w);
+            refill(k);
         }
-        first = false;
-    } while (ok && !uc.end);
+    } while (ok && used < total);
     if (ok) {
         trace_worker(P, w, cur, NP);
         sk_transition(c, cur, NP, NP);
@@ -330,39 +389,45 @@ __device__ __forceinline__ void stream_worker(const StreamParams& P, SPlan s, un
 
 // ---------------------------------------------------------------- control
 
-// grid barrier: every control wave has its stores complete, then one
-// arrival per workgroup on its XCD's counter; wave 0 polls the eight
-// counters until all workgroups have arrived `epoch` times in total
-__device__ __forceinline__ bool ctl_grid_sync(const StreamParams& P, SCtl* c, ABar& bar, uint32_t epoch)
+// Wait until every workgroup's progress flag has reached `epoch` (wave 0
+// polls them with device-scope loads; the other control waves wait at the
+// control barrier). False when the step gives up.
+__device__ __forceinline__ bool ctl_wait_flags(const StreamParams& P, SCtl* c, ABar& bar, uint32_t epoch)
 {
-    wait_vm_all();
-    bar();
-    StreamSync* S = P.sync;
     if (threadIdx.x < kWave) {
         const int lane = lane_id();
-        if (lane == 0)
-            __hip_atomic_fetch_add(&S->arrive[blockIdx.x & 7][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int yy = lane & 7;
-        const uint32_t members = (uint32_t)(((int)gridDim.x - yy + 7) / 8);
-        const uint32_t target = epoch * members;
+        const int nwg = (int)gridDim.x;
         uint32_t n = 0;
         bool good = true;
         while (true) {
-            const uint32_t v = ld_dev(&S->arrive[yy][0]);
-            if (__all(v >= target)) break;
-            if (++n > kGridSpin || ((n & 63) == 0 && ld_dev(&S->err[0]) != 0u)) {
+            uint32_t lo = 0xFFFFFFFFu;
+            for (int i = lane; i < nwg; i += kWave) {
+                const uint32_t v = ld_dev(P.flags + i);
+                lo = v < lo ? v : lo;
+            }
+            if (__all(lo >= epoch)) break;
+            if (++n > kGridSpin || ((n & 63) == 0 && ld_dev(&P.sync->err[0]) != 0u)) {
                 good = false;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
         if (!good && lane == 0) {
-            st_dev(&S->err[0], 1u);
+            st_dev(&P.sync->err[0], 1u);
             lds_st(&c->abort, 1u);
         }
     }
     bar();
     return lds_ld(&c->abort) == 0u;
+}
+
+// This workgroup's outputs of the phase with this epoch are stored: every
+// control wave waits for its own stores to complete, then the flag moves on.
+__device__ __forceinline__ void ctl_publish(const StreamParams& P, ABar& bar, uint32_t epoch)
+{
+    wait_vm_all();
+    bar();
+    if (threadIdx.x == 0) st_dev(P.flags + blockIdx.x, epoch);
 }
 
 // control-group sum of one double per thread, fixed order (wave butterfly,
@@ -472,20 +537,24 @@ __device__ __forceinline__ void ctl_input_norm(const StreamParams& P, SCtl* c, A
 }
 
 // Matvec input of K values taken as they are (o, or the SwiGLU output):
-// Q8_0 codes into LDS, two chunks per thread at a time
+// Q8_0 codes into LDS. Each thread loads up to four 16-value chunks before it
+// uses any, so a whole input of up to 16384 values costs one round trip.
 __device__ __forceinline__ void ctl_input_plain(const float* u, int64_t K, unsigned char* in_q, float* in_s)
 {
+    constexpr int NJ = 4;
     const int64_t nq = K / 16;
     const int t = threadIdx.x;
-    for (int64_t base = 0; base < nq; base += 2 * kSA) {
-        float v[2][16];
+    for (int64_t base = 0; base < nq; base += NJ * kSA) {
+        float v[NJ][16];
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t k = base + (int64_t)j * kSA + t;
-            ctl_dev16(u, k < nq ? k : nq - 1, v[j]);
+        for (int j = 0; j < NJ; j++) {
+            if (base + (int64_t)j * kSA < nq) {  // uniform
+                const int64_t k = base + (int64_t)j * kSA + t;
+                ctl_dev16(u, k < nq ? k : nq - 1, v[j]);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < NJ; j++)
             if (base + (int64_t)j * kSA < nq) ctl_put(in_q, in_s, base + (int64_t)j * kSA + t, K, v[j]);
     }
 }
@@ -613,6 +682,13 @@ __device__ __forceinline__ void ctl_attention(const StreamParams& P, int l, SCtl
     }
 }
 
+// Epoch of phase k (0 q/k/v, 1 attention, 2 output, 3 w1/w3, 4 w2) of
+// layer l in this launch
+__device__ __forceinline__ uint32_t ep(const StreamParams& P, int l, int k)
+{
+    return P.epoch0 + 1u + 5u * (uint32_t)l + (uint32_t)k;
+}
+
 template <int KG, int HS>
 __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, unsigned char* smem,
                                                const SLds& L)
@@ -621,6 +697,8 @@ __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, u
     float* rcos = (float*)(smem + L.rope);
     float* rsin = rcos + P.hs / 2;
     float* y = (float*)(smem + L.y);
+    // this workgroup's rows of the residual stream x (the rows of the output
+    // and w2 matvecs), kept in LDS for the whole step
     float* res = (float*)(smem + L.res);
     unsigned char* in_q = smem + L.in_q;
     float* in_s = (float*)(smem + L.in_s);
@@ -630,7 +708,6 @@ __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, u
     const int pos = P.pos;
     uint32_t nbar = 0;
     ABar bar{c, nbar};
-    uint32_t epoch = P.epoch0;
     // ---- step start: token, the RoPE table of pos, the embedding row
     if (tid < kWave) {
         int token = P.token;
@@ -657,6 +734,8 @@ __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, u
     bar();
     const int token = c->token;
     if (b == 0) {
+        // the step record, and this step's argmax slots cleared; complete
+        // before this workgroup's first flag, which every classifier waits for
         if (tid == 0) {
             st_dev(P.step + kStepToken, token);
             st_dev(P.step + kStepPos, pos);
@@ -666,42 +745,50 @@ __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, u
         if (tid < kArgmaxSlots) st_dev(P.argmax + ((size_t)(pos & 1) * kArgmaxSlots + tid) * kArgmaxStride, 0ull);
     }
     {
-        // this workgroup's slice of the residual stream x = embedding row
-        const int64_t i0 = (int64_t)P.d * b / gridDim.x, i1 = (int64_t)P.d * (b + 1) / gridDim.x;
-        for (int64_t i = i0 + tid; i < i1; i += kSA) {
+        // this workgroup's rows of x = the embedding row
+        const int64_t r0 = rows.r0[SK_WO], nr = rows.r1[SK_WO] - r0;
+        for (int64_t t = tid; t < nr; t += kSA) {
+            const int64_t i = r0 + t;
             const int8_t code = P.emb[(int64_t)token * P.d + q8_perm_offset(i, P.d, kSGS)];
-            st_dev(P.x + i, (float)((double)code * (double)P.emb_s[((int64_t)token * P.d + i) / kSGS]));
+            res[t] = (float)((double)code * (double)P.emb_s[((int64_t)token * P.d + i) / kSGS]);
         }
     }
 
     trace_ctl(P, 0);
-    for (int64_t p = 0; p < sp_phases(s); p++) {
+    const int64_t NP = sp_phases(s);
+    for (int64_t p = 0; p < NP; p++) {
         const SPhase f = sp_phase(s, p);
         trace_ctl(P, 1 + 6 * p);
         const int l = (int)f.layer;
-        const int64_t r0 = f.kind == SK_QKV ? rows.r0[0] : f.kind == SK_WO ? rows.r0[1] : f.kind == SK_W13 ? rows.r0[2]
-                         : f.kind == SK_W2  ? rows.r0[3] : rows.r0[4];
-        const int64_t r1 = f.kind == SK_QKV ? rows.r1[0] : f.kind == SK_WO ? rows.r1[1] : f.kind == SK_W13 ? rows.r1[2]
-                         : f.kind == SK_W2  ? rows.r1[3] : rows.r1[4];
-        const int64_t nr = r1 - r0;
-        // input of the phase into LDS
-        if (f.kind == SK_QKV)
-            ctl_input_norm(P, c, bar, in_q, in_s, l == 0 ? nullptr : P.x, token, P.rms_att + (size_t)l * P.d);
-        else if (f.kind == SK_W13)
-            ctl_input_norm(P, c, bar, in_q, in_s, P.x, token, P.rms_ffn + (size_t)l * P.d);
-        else if (f.kind == SK_CLS)
-            ctl_input_norm(P, c, bar, in_q, in_s, P.x, token, P.rms_final);
-        else
-            ctl_input_plain(f.kind == SK_WO ? P.o : P.hb, f.K, in_q, in_s);
-        if (f.kind == SK_WO || f.kind == SK_W2)
-            for (int64_t t = tid; t < nr; t += kSA) res[t] = ld_dev(P.x + r0 + t);
+        const int k = f.kind;
+        const int64_t r0 = rows.r0[k], nr = rows.r1[k] - r0;
+        // wait for the phase's input, then prepare it in LDS (nothing when
+        // this workgroup has no rows here)
+        if (nr > 0) {
+            uint32_t need = 0;  // 0: nothing to wait for (the embedding row)
+            if (k == SK_QKV && l > 0) need = ep(P, l - 1, 4);
+            else if (k == SK_WO) need = ep(P, l, 1);
+            else if (k == SK_W13) need = ep(P, l, 2);
+            else if (k == SK_W2) need = ep(P, l, 3);
+            else if (k == SK_CLS) need = ep(P, (int)P.L - 1, 4);
+            if (need != 0 && !ctl_wait_flags(P, c, bar, need)) return;
+            trace_ctl(P, 2 + 6 * p);
+            if (k == SK_QKV)
+                ctl_input_norm(P, c, bar, in_q, in_s, l == 0 ? nullptr : P.x, token, P.rms_att + (size_t)l * P.d);
+            else if (k == SK_W13)
+                ctl_input_norm(P, c, bar, in_q, in_s, P.x, token, P.rms_ffn + (size_t)l * P.d);
+            else if (k == SK_CLS)
+                ctl_input_norm(P, c, bar, in_q, in_s, P.x, token, P.rms_final);
+            else
+                ctl_input_plain(k == SK_WO ? P.o : P.hb, f.K, in_q, in_s);
+        }
         ctl_ready(c, bar, p);
-        trace_ctl(P, 2 + 6 * p);
-        if (!ctl_wait_done(c, (uint32_t)((p + 1) * kSNW))) return;
         trace_ctl(P, 3 + 6 * p);
+        if (!ctl_wait_done(c, (uint32_t)((p + 1) * kSNW))) return;
+        trace_ctl(P, 4 + 6 * p);
         bar();
         // epilogue of this workgroup's rows
-        if (f.kind == SK_QKV) {
+        if (k == SK_QKV) {
             const int64_t d = P.d, kvd = P.kvd;
             float* kslot = P.kc + ((size_t)l * P.S + pos) * kvd;
             float* vslot = P.vc + ((size_t)l * P.S + pos) * kvd;
@@ -724,9 +811,13 @@ __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, u
                     st_dev(dst + 1, bb);
                 }
             }
-        } else if (f.kind == SK_WO || f.kind == SK_W2) {
-            for (int64_t t = tid; t < nr; t += kSA) st_dev(P.x + r0 + t, (float)((double)res[t] + (double)y[t]));
-        } else if (f.kind == SK_W13) {
+        } else if (k == SK_WO || k == SK_W2) {
+            for (int64_t t = tid; t < nr; t += kSA) {
+                const float xn = (float)((double)res[t] + (double)y[t]);
+                res[t] = xn;
+                st_dev(P.x + r0 + t, xn);
+            }
+        } else if (k == SK_W13) {
             // rows (2i, 2i+1) hold w1 row i and w3 row i
             for (int64_t k2 = tid; 2 * k2 + 1 < nr; k2 += kSA) {
                 const double z = (double)y[2 * k2];
@@ -757,17 +848,18 @@ __device__ __forceinline__ void stream_control(const StreamParams& P, SPlan s, u
                 if (bm != 0)
                     atomicMax(P.argmax + ((size_t)(pos & 1) * kArgmaxSlots + b % kArgmaxSlots) * kArgmaxStride, bm);
             }
-            trace_ctl(P, 4 + 6 * p);
+            trace_ctl(P, 5 + 6 * p);
             return;
         }
-        trace_ctl(P, 4 + 6 * p);
-        if (!ctl_grid_sync(P, c, bar, ++epoch)) return;
+        ctl_publish(P, bar, ep(P, l, k == SK_QKV ? 0 : k == SK_WO ? 2 : k == SK_W13 ? 3 : 4));
         trace_ctl(P, 5 + 6 * p);
-        if (f.kind == SK_QKV) {
+        if (k == SK_QKV) {
+            // attention of layer l once every workgroup's q/k/v rows are stored
+            if (!ctl_wait_flags(P, c, bar, ep(P, l, 0))) return;
             ctl_attention<KG, HS>(P, l, c, bar, smem + L.attn);
             if (lds_ld(&c->abort) != 0u) return;
+            ctl_publish(P, bar, ep(P, l, 1));
             trace_ctl(P, 6 + 6 * p);
-            if (!ctl_grid_sync(P, c, bar, ++epoch)) return;
         }
     }
 }
@@ -776,10 +868,9 @@ template <int KG, int HS>
 __global__ __launch_bounds__(kST) void stream_step_kernel(StreamParams P)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const SPlan s{P.d, P.h, P.L, P.kvd, P.V, (int64_t)gridDim.x, kSNW,
-                  P.wofs[0], P.wofs[1], P.wofs[2], P.wofs[3], P.wofs[4],
-                  P.sofs[0] / 4, P.sofs[1] / 4, P.sofs[2] / 4, P.sofs[3] / 4, P.sofs[4] / 4};
-    const SLds L = stream_lds_layout(P.ymax, P.kmax, P.hs, attn_core_lds_bytes<kSA>(KG, HS > 0 ? HS : P.hs));
+    const SPlan s{P.d, P.h, P.L, P.kvd, P.V, (int64_t)gridDim.x, kSNW, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const SLds L = stream_lds_layout(P.ymax, P.kmax, P.hs, attn_core_lds_bytes<kSA>(KG, HS > 0 ? HS : P.hs),
+                                     P.wtab_stride);
     SCtl* c = (SCtl*)smem;
     if (threadIdx.x == 0) {
         c->ready = 0;
@@ -792,7 +883,7 @@ __global__ __launch_bounds__(kST) void stream_step_kernel(StreamParams P)
     if (wave < kSAW)
         stream_control<KG, HS>(P, s, smem, L);
     else
-        stream_worker(P, s, smem, L, wave - kSAW);
+        stream_worker(P, smem, L, wave - kSAW);
 }
 
 // ---------------------------------------------------------------- host side
@@ -807,10 +898,10 @@ bool stream_supported(int dt, int gs, int64_t d, int64_t h, int G, int gsplit, i
     return attn_core_supported<kSA>(kg, hs) && hs / 2 <= kSA;
 }
 
-size_t stream_lds_bytes(const SPlan& s, int kg, int hs)
+size_t stream_lds_bytes(const SPlan& s, int kg, int hs, int64_t tstride)
 {
     const int64_t kmax = s.d > s.h ? s.d : s.h;
-    return stream_lds_layout(sp_max_wg_rows(s), kmax, hs, attn_core_lds_bytes<kSA>(kg, hs)).total;
+    return stream_lds_layout(sp_max_wg_rows(s), kmax, hs, attn_core_lds_bytes<kSA>(kg, hs), tstride).total;
 }
 
 template <int KG>

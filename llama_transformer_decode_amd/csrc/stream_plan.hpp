@@ -28,8 +28,8 @@ struct SPlan {
     int64_t d, h, L, kvd, V;
     int64_t nwg;  // workgroups of the launch
     int64_t nwk;  // worker waves per workgroup
-    // where each matrix kind's codes (bytes) and scales (floats) start, from
-    // one base address (the kernel's); 0 for offsets within each array
+    // where each matrix kind's codes and scales start (bytes), from one base
+    // address (the kernel's); 0 for offsets within each array
     int64_t wo0, wo1, wo2, wo3, wo4;
     int64_t so0, so1, so2, so3, so4;
 };
@@ -218,111 +218,49 @@ __host__ __device__ __forceinline__ SItem sp_item(SPlan s, SWork k, int64_t w, i
     return it;
 }
 
-// The kernel's form of a worker's stream: an incremental cursor over a
-// table of the worker's rows of each matrix kind (kept in LDS by the
-// kernel), cheap to advance: one chunk is a few scalar adds and compares, a
-// new row one more add, a new phase one table entry. A worker with no rows
-// of a kind gets one phantom row there (it loads and computes nothing), so
-// every worker passes through every phase in order. The host checker walks
-// this cursor next to sp_item and requires the same items.
-struct SKindRun {
-    int64_t woff0, soff0;    // code / scale offset of its first row in layer 0 (from the plan's base)
-    int64_t wlayer, slayer;  // offsets from one layer to the next
-    int32_t n;               // rows (1 for a phantom row)
-    int32_t phantom;         // 1: the worker has no rows of this kind
-    int32_t nch, K;
+// The kernel's form of a worker's stream: a table of chunk descriptors,
+// built on the host from the enumeration above (the items of one layer, then
+// the classifier's), so the kernel walks it with one scalar load per chunk
+// and no address arithmetic beyond a layer multiply. A worker with no rows of
+// a kind gets one phantom item there (it loads a dummy address and computes
+// nothing), so every worker passes through every phase in order. The host
+// checker expands each table over the layers and requires the items of
+// sp_item, in order.
+struct SDesc {
+    int64_t w0;  // byte offset (from the kernel's weight base) of the chunk's codes in layer 0
+    int64_t s0;  // byte offset of the chunk's group scales in layer 0
+    int32_t wl;  // code bytes from one layer to the next (0 for the classifier)
+    int32_t sl;  // scale bytes from one layer to the next
+    uint32_t meta;
+    uint32_t pad;
 };
 
-__host__ __device__ __forceinline__ int64_t sp_sel5(int k, int64_t a, int64_t b, int64_t c, int64_t d, int64_t e)
-{
-    return k == 0 ? a : k == 1 ? b : k == 2 ? c : k == 3 ? d : e;
-}
-
-// the table entry of kind k for worker w (r: the workgroup's row ranges)
-__host__ __device__ __forceinline__ SKindRun sp_kind_run(SPlan s, SRows r, int64_t w, int k)
-{
-    const SPhase f = sp_phase(s, k == SK_CLS ? 4 * s.L : k);
-    const int64_t r0 = sp_sel5(k, r.r0[0], r.r0[1], r.r0[2], r.r0[3], r.r0[4]);
-    const int64_t r1 = sp_sel5(k, r.r1[0], r.r1[1], r.r1[2], r.r1[3], r.r1[4]);
-    const int64_t n = sp_worker_rows(r0, r1, w, s.nwk);
-    SKindRun e;
-    e.woff0 = sp_sel5(k, s.wo0, s.wo1, s.wo2, s.wo3, s.wo4) + (r0 + w) * f.K;
-    e.soff0 = sp_sel5(k, s.so0, s.so1, s.so2, s.so3, s.so4) + (r0 + w) * (f.K / kSGS);
-    e.wlayer = f.M * f.K;
-    e.slayer = f.M * (f.K / kSGS);
-    e.n = n > 0 ? (int32_t)n : 1;
-    e.phantom = n > 0 ? 0 : 1;
-    e.nch = (int32_t)sp_chunks(f.K);
-    e.K = (int32_t)f.K;
-    return e;
-}
-
-struct SCur {
-    int32_t kind, layer;  // phase 4 * layer + kind (kind SK_CLS: the classifier)
-    int32_t j, n;         // the worker's j-th row of n in the phase
-    int32_t c, nch;       // chunk c of nch in the row
-    int32_t K;            // row length
-    int32_t local;        // index among the workgroup's rows (w + j * nwk)
-    int32_t phantom;      // the phase's one item is a phantom row
-    int32_t end;          // past the classifier
-    int64_t woff, soff;   // code / scale offset of the row (from the plan's base; layers included)
+// meta word: kind in bits 0-2, flags, groups of the chunk (1..64) in bits
+// 6-12, chunk of the row in bits 13-16, the row's index among the
+// workgroup's rows in bits 17-31
+enum : uint32_t {
+    SD_ROWEND = 1u << 3,   // the row's last chunk: reduce and store its sum
+    SD_FIRST = 1u << 4,    // the worker's first item of its phase
+    SD_PHANTOM = 1u << 5,  // no rows of this kind: load nothing real, compute nothing
 };
 
-__host__ __device__ __forceinline__ void sc_set(SCur& u, const SKindRun* tab, int64_t w, int kind, int32_t layer)
+__host__ __device__ __forceinline__ uint32_t sd_meta(int kind, bool rowend, bool first, bool phantom, int64_t nb,
+                                                     int64_t c, int64_t local)
 {
-    const SKindRun e = tab[kind];
-    u.kind = kind;
-    u.layer = layer;
-    u.j = 0;
-    u.n = e.n;
-    u.c = 0;
-    u.nch = e.phantom ? 1 : e.nch;
-    u.K = e.K;
-    u.local = (int32_t)w;
-    u.phantom = e.phantom;
-    u.woff = e.woff0 + (int64_t)layer * e.wlayer;
-    u.soff = e.soff0 + (int64_t)layer * e.slayer;
+    return (uint32_t)kind | (rowend ? SD_ROWEND : 0u) | (first ? SD_FIRST : 0u) | (phantom ? SD_PHANTOM : 0u) |
+           ((uint32_t)nb << 6) | ((uint32_t)c << 13) | ((uint32_t)local << 17);
 }
+__host__ __device__ __forceinline__ int sd_kind(uint32_t m) { return (int)(m & 7u); }
+__host__ __device__ __forceinline__ int sd_nb(uint32_t m) { return (int)((m >> 6) & 127u); }
+__host__ __device__ __forceinline__ int sd_c(uint32_t m) { return (int)((m >> 13) & 15u); }
+__host__ __device__ __forceinline__ int sd_local(uint32_t m) { return (int)(m >> 17); }
 
-__host__ __device__ __forceinline__ void sc_begin(SCur& u, const SKindRun* tab, int64_t w)
+// limits of the meta fields and of the per-layer strides
+__host__ __device__ __forceinline__ bool sd_fits(SPlan s)
 {
-    u.end = 0;
-    sc_set(u, tab, w, SK_QKV, 0);
-}
-
-// one item on
-__host__ __device__ __forceinline__ void sc_step(SCur& u, SPlan s, const SKindRun* tab, int64_t w)
-{
-    if (u.end) return;
-    if (++u.c < u.nch) return;
-    u.c = 0;
-    if (++u.j < u.n) {
-        u.local += (int32_t)s.nwk;
-        u.woff += s.nwk * u.K;
-        u.soff += s.nwk * (u.K / kSGS);
-        return;
-    }
-    if (u.kind == SK_CLS) {
-        u.end = 1;
-    } else if (u.kind < SK_W2) {
-        sc_set(u, tab, w, u.kind + 1, u.layer);
-    } else if (u.layer + 1 < s.L) {
-        sc_set(u, tab, w, SK_QKV, u.layer + 1);
-    } else {
-        sc_set(u, tab, w, SK_CLS, 0);
-    }
-}
-
-__host__ __device__ __forceinline__ int64_t sc_phase(const SCur& u, SPlan s)
-{
-    return u.kind == SK_CLS ? 4 * s.L : 4 * (int64_t)u.layer + u.kind;
-}
-
-// groups in the cursor's chunk
-__host__ __device__ __forceinline__ int32_t sc_groups(const SCur& u)
-{
-    const int32_t left = u.K / kSGS - 64 * u.c;
-    return left < 64 ? left : 64;
+    const int64_t kmax = s.d > s.h ? s.d : s.h;
+    const int64_t big = 2 * s.h * s.d > s.V * s.d ? 2 * s.h * s.d : s.V * s.d;
+    return sp_chunks(kmax) <= 16 && sp_max_wg_rows(s) < 32768 && big < ((int64_t)1 << 31);
 }
 
 // Attention work items: (kv head g, query-head subset hsub of gsplit, range
