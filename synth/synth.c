@@ -28,9 +28,12 @@
  * index) through the splitmix64 finaliser (Steele, Lea, Flood, "Fast
  * splittable pseudorandom number generators", OOPSLA 2014), so any thread
  * count gives the same bytes.
- *   - fp32 matrices: Irwin-Hall(4) bell variate (sum of the four 16-bit
- *     fields of one 64-bit draw, centred, unit variance), times 0.02, rounded
- *     to fp32 once: an approximately N(0, 0.02) tensor, bounded at 3.46 sd.
+ *   - fp32 matrices, activation vectors and KV-cache fills: a standard
+ *     normal variate from one 64-bit draw by the Box-Muller transform (Box
+ *     and Muller, "A note on the generation of random normal deviates",
+ *     1958): the two 32-bit halves give u1, u2 in (0, 1) as (k + 1/2) 2^-32,
+ *     z = sqrt(-2 ln u1) cos(2 pi u2) in fp64, times the sd (0.02 for
+ *     weights), rounded to fp32 once: N(0, sd) up to |z| of about 6.7.
  *   - Q8_0 matrices: shaped like the codes of a bell-shaped tensor stored
  *     with one scale per group of GS: in every group one element, at a
  *     drawn index and with a drawn sign, is +-127 (the group's largest
@@ -78,6 +81,14 @@ static inline int64_t bell(uint64_t r)
 
 /* standard deviation of bell(): 4 * (65536^2 - 1) / 12 under the root */
 static double bell_sd(void) { return sqrt(4.0 * (65536.0 * 65536.0 - 1.0) / 12.0); }
+
+/* standard normal variate of one 64-bit draw (Box-Muller, cosine branch) */
+static inline double gauss(uint64_t r)
+{
+    const double u1 = ((double)(r & 0xFFFFFFFFull) + 0.5) * 0x1.0p-32;
+    const double u2 = ((double)(r >> 32) + 0.5) * 0x1.0p-32;
+    return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925286766559 * u2);
+}
 
 typedef struct {
     int32_t dim, hidden_dim, n_layers, n_heads, n_kv_heads, vocab_size, seq_len;
@@ -149,10 +160,8 @@ int64_t synth_blob_bytes(const synth_config* c, int dtype, int gs)
 
 static void fill_f32(float* dst, int64_t n, uint64_t seed, int tid)
 {
-    const double k = 0.02 / bell_sd();
     #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; i++)
-        dst[i] = (float)((double)bell(draw(seed, (uint64_t)tid, (uint64_t)i)) * k);
+    for (int64_t i = 0; i < n; i++) dst[i] = (float)(gauss(draw(seed, (uint64_t)tid, (uint64_t)i)) * 0.02);
 }
 
 static void fill_const(float* dst, int64_t n, float v)
@@ -269,11 +278,9 @@ void synth_prompt(uint64_t seed, int32_t n, int32_t vocab, int32_t* out)
         out[i] = (int32_t)((draw(seed, T_PROMPT, (uint64_t)i) >> 11) % (uint64_t)vocab);
 }
 
-/* n fp32 values, approx N(0, sd), for activation vectors and KV-cache fills */
+/* n fp32 values, N(0, sd), for activation vectors and KV-cache fills */
 void synth_normal_f32(uint64_t seed, int32_t tid, int64_t n, double sd, float* out)
 {
-    const double k = sd / bell_sd();
     #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; i++)
-        out[i] = (float)((double)bell(draw(seed, (uint64_t)(1000 + tid), (uint64_t)i)) * k);
+    for (int64_t i = 0; i < n; i++) out[i] = (float)(gauss(draw(seed, (uint64_t)(1000 + tid), (uint64_t)i)) * sd);
 }
