@@ -323,6 +323,60 @@ def kernel_detail(ctx, cfg, dtype, token, pos, reps):
     return kt, kern
 
 
+def stream_trace(ctx, cfg, token: int, pos: int) -> dict:
+    """One step of the persistent step kernel with its clock stamps
+    (l2d_stream_trace, 100 MHz): per matvec phase, the medians over
+    workgroups (averaged over layers 2 .. L-3) of the wait for the phase's
+    inputs (other workgroups' progress flags), the prologue (input into LDS),
+    the workers' part after the input is ready, the epilogue with the flag
+    store, and (q/k/v) the attention items; the latency from the last
+    producer's flag to the median consumer seeing it; the spread of the
+    producers' flag stores; and the step's span per layer."""
+    import numpy as np
+    nwg, nwk = ctx.stream_shape()
+    ctl, _ = ctx.stream_trace(token, pos, nwg, nwk)
+    c = ctl.astype(np.int64)
+    c = c - c[:, 0].min()
+    L = cfg.n_layers
+    names = ["qkv", "wo", "w13", "w2"]
+    ev = lambda p, i: c[:, i + 6 * p]
+    out = {}
+    layers = range(2, L - 2)
+    for k, n in enumerate(names):
+        row = {"wait_us": [], "prologue_us": [], "workers_us": [], "epilogue_us": [], "attention_us": [],
+               "flag_latency_us": [], "publish_spread_us": []}
+        for l in layers:
+            p = 4 * l + k
+            row["wait_us"].append(np.median(ev(p, 2) - ev(p, 1)))
+            row["prologue_us"].append(np.median(ev(p, 3) - ev(p, 2)))
+            row["workers_us"].append(np.median(ev(p, 4) - ev(p, 3)))
+            row["epilogue_us"].append(np.median(ev(p, 5) - ev(p, 4)))
+            if k == 0:
+                row["attention_us"].append(np.median(ev(p, 6) - ev(p, 5)))
+            prev = ev(p - 1, 5) if k != 1 else ev(p - 1, 6)
+            row["flag_latency_us"].append(np.median(ev(p, 2)) - prev.max())
+            row["publish_spread_us"].append(ev(p, 5).max() - np.median(ev(p, 5)))
+        out[n] = {kk: float(np.mean(v)) / 100.0 for kk, v in row.items() if v}
+    per_layer = [np.median(ev(4 * (l + 1), 1) - ev(4 * l, 1)) for l in layers]
+    out["per_layer_us"] = float(np.mean(per_layer)) / 100.0
+    out["step_us"] = float(c[:, :1 + 6 * (4 * L + 1)].max()) / 100.0
+    return out
+
+
+def format_stream_trace(tr: dict, title: str, command: str) -> str:
+    lines = [title, "=" * len(title), "", "Command (repo root on the GPU machine):", "  " + command, "",
+             "Per-layer medians over workgroups (layers 2 .. L-3), microseconds:", "",
+             f"{'phase':<6} {'wait':>7} {'prologue':>9} {'workers':>8} {'epilogue':>9} {'attention':>10} "
+             f"{'flag->seen':>11} {'pub spread':>11}"]
+    for n in ("qkv", "wo", "w13", "w2"):
+        r = tr[n]
+        att = f"{r['attention_us']:.2f}" if "attention_us" in r else "-"
+        lines.append(f"{n:<6} {r['wait_us']:7.2f} {r['prologue_us']:9.2f} {r['workers_us']:8.2f} "
+                     f"{r['epilogue_us']:9.2f} {att:>10} {r['flag_latency_us']:11.2f} {r['publish_spread_us']:11.2f}")
+    lines += ["", f"per_layer_us: {tr['per_layer_us']:.2f}", f"step_us: {tr['step_us']:.1f}", ""]
+    return "\n".join(lines)
+
+
 def time_oracle(m, budget_s: float, seq_len: int, min_steps: int = 2) -> tuple:
     """Greedy decode from pos 0 with the oracle for about budget_s seconds
     (a short model that reaches seq_len starts over from pos 0 with an empty
@@ -551,6 +605,8 @@ def main():
                     help="skip the Q4_0 matvec measurement")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the persistent step kernel measurement")
+    ap.add_argument("--stream-trace-out", metavar="FILE",
+                    help="also write the persistent kernel's per-phase trace summary to FILE")
     ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shape Q8_0 step")
     ap.add_argument("--positions-70b", default="1,2048,4095")
     ap.add_argument("--kernel-reps", type=int, default=10)
@@ -623,6 +679,18 @@ def main():
                     st[str(p)] = {"tok_s": 1.0 / tr["sec"], "ms": tr["sec"] * 1e3, "trials_ms": tr["trials_ms"]}
                     log(f"[bench]   stream kernel pos {p}: {tr['sec'] * 1e3:.3f} ms/step, {1 / tr['sec']:.1f} tok/s")
                 detail["q8_0_stream"] = {"per_pos": st}
+                tr = stream_trace(ctx, cfg, fed[hp], hp)
+                detail["q8_0_stream"]["trace_pos"] = hp
+                detail["q8_0_stream"]["trace"] = tr
+                log(f"[bench]   stream kernel trace at pos {hp}: {tr['per_layer_us']:.1f} us per layer; " +
+                    "; ".join(f"{n} wait {tr[n]['wait_us']:.1f} prologue {tr[n]['prologue_us']:.1f} "
+                              f"workers {tr[n]['workers_us']:.1f}" for n in ("qkv", "wo", "w13", "w2")))
+                if args.stream_trace_out:
+                    with open(args.stream_trace_out, "w") as f:
+                        f.write(format_stream_trace(
+                            tr, f"Persistent step kernel phases, {cfg.name}-shape Llama-2 decode step, Q8_0 GS=64, "
+                                f"batch 1, pos {hp} (l2d_stream_trace clock stamps)",
+                            "python bench.py " + " ".join(sys.argv[1:])))
                 ctx.use_persistent(False)
             except l2d.L2DError as e:
                 detail["q8_0_stream"] = {"unavailable": str(e)}
@@ -688,8 +756,8 @@ def main():
         "vs_baseline": None,
         "dtype": {0: "f32 (fp64 accumulate)", 1: "int8xint8->int32, fp32/fp64",
                   2: "int4xint8->int32, fp32/fp64"}[dt],
-        "data": "synthetic: seeded random weights of the 7B shape (fp32: sums of 4 uniforms scaled to "
-                "sd 0.02; Q8_0: random codes and scales)",
+        "data": "synthetic: seeded random weights of the 7B shape (fp32: N(0, 0.02) by Box-Muller; "
+                "Q8_0: random codes, one +-127 per group, scales giving sd 0.02)",
         "config": {"workload": f"{cfg.name}-shape Llama-2 decode step, "
                                f"{('fp32', 'Q8_0 GS=64', 'Q4_0 GS=32')[dt]}, batch 1, pos {args.headline_pos}",
                    "global_batch": 1, "seq_len": cfg.seq_len, "pos": args.headline_pos,

@@ -360,16 +360,25 @@ int l2d_use_persistent(l2d_ctx* ctx, int32_t enable);
  * workgroup's control events and at each worker's phase reports. *events
  * receives E = 1 + 6 (4 n_layers + 1), the control events per workgroup.
  * host (n uint64) receives, for G workgroups (one per CU) and W worker
- * waves each: [G][E] control stamps (event 0: step start; for phase p, in
- * step order q/k/v, output, w1/w3, w2 per layer, then the classifier:
- * 1 + 6p input preparation starts, 2 + 6p input published, 3 + 6p all
- * workers done, 4 + 6p results stored, 5 + 6p grid barrier passed, 6 + 6p
- * (q/k/v phases) attention done), then [G][W][4 n_layers + 1] worker report
- * stamps; 0 where an event did not occur. host NULL: only *events is set.
- * Synchronous; L2D_EINVAL when n is too small or the kernel is not
- * available.
+ * waves each (l2d_stream_shape): [G][E] control stamps (event 0: step
+ * start; for phase p, in step order q/k/v, output, w1/w3, w2 per layer,
+ * then the classifier: 1 + 6p phase start, 2 + 6p the inputs' producers
+ * seen done (their progress flags), 3 + 6p input in LDS for the workers,
+ * 4 + 6p all workers done, 5 + 6p results stored and this workgroup's flag
+ * published, 6 + 6p (q/k/v phases) attention done and published), then
+ * [G][W][4 n_layers + 1] worker report stamps; 0 where an event did not
+ * occur. host NULL: only *events is set. Synchronous; L2D_EINVAL when n is
+ * too small or the kernel is not available.
  */
 int l2d_stream_trace(l2d_ctx* ctx, int32_t token, int32_t pos, uint64_t* host, int64_t n, int64_t* events);
+
+/*
+ * Launch shape of the persistent step kernel of this context: workgroups
+ * (one per CU) and worker waves per workgroup, the G and W of
+ * l2d_stream_trace's buffer. L2D_EINVAL for null arguments or when the
+ * kernel is not available for the context's model or device.
+ */
+int l2d_stream_shape(const l2d_ctx* ctx, int32_t* workgroups, int32_t* workers);
 
 /* 1 when l2d_forward runs the persistent step kernel, 0 when the per-phase
  * kernels run, L2D_EINVAL for a null context. */

@@ -104,6 +104,7 @@ def lib():
                                                 ctypes.POINTER(ctypes.c_double)]),
             "l2d_stream_plan_check": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_char_p,
                                                      ctypes.c_int32]),
+            "l2d_stream_shape": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
             "l2d_stream_trace": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
                                                 ctypes.POINTER(ctypes.c_int64)]),
         }
@@ -122,7 +123,7 @@ EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l
            "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
            "l2d_set_sampling", "l2d_prefill", "l2d_prefill_combine", "l2d_profile_prefill", "l2d_stream_plan_check",
-           "l2d_stream_trace")
+           "l2d_stream_trace", "l2d_stream_shape")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
 PREFILL_CLASSES = ("prep", "qkv", "attn", "wo", "w13", "w2", "start", "cls")
@@ -293,6 +294,12 @@ class Context:
         """Run each step as the one persistent step kernel (True; Q8_0 with
         group size 64) or as the captured graph of per-phase kernels (False)."""
         _check(lib().l2d_use_persistent(self._h, 1 if enable else 0), self._h)
+
+    def stream_shape(self):
+        """(workgroups, worker waves per workgroup) of the persistent step kernel."""
+        g, w = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().l2d_stream_shape(self._h, ctypes.byref(g), ctypes.byref(w)), self._h)
+        return g.value, w.value
 
     def stream_trace(self, token: int, pos: int, workgroups: int, workers: int):
         """One persistent-kernel step with clock stamps: (control [G][E],

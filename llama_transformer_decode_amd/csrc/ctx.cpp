@@ -1339,6 +1339,15 @@ int l2d_stream_trace(l2d_ctx* ctx, int32_t token, int32_t pos, uint64_t* host, i
     return rc;
 }
 
+int l2d_stream_shape(const l2d_ctx* ctx, int32_t* workgroups, int32_t* workers)
+{
+    if (!ctx || !workgroups || !workers) return fail(nullptr, L2D_EINVAL, "stream_shape: null argument");
+    if (!ctx->stream_ok) return fail(const_cast<l2d_ctx*>(ctx), L2D_EINVAL, "stream_shape: the persistent step kernel is not available");
+    *workgroups = ctx->stream_grid;
+    *workers = stream_workers();
+    return L2D_OK;
+}
+
 int l2d_prefill_combine(l2d_ctx* ctx, int32_t fp32)
 {
     if (!ctx) return fail(nullptr, L2D_EINVAL, "prefill_combine: null context");

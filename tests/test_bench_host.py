@@ -72,3 +72,43 @@ def test_step_bytes_match_the_survey_figures():
     assert b["w13"] == 2 * 11008 * 4096 * 1.0625 == 95813632
     assert b["total"] == pytest.approx(7.56e9, rel=2e-3)
     assert bench.step_bytes(synth.CONFIGS["7B"], 0, 512)["total"] == pytest.approx(26.97e9, rel=2e-3)
+
+
+class _FakeTraceCtx:
+    """Two workgroups, a 5-layer model: every event of phase p at a fixed
+    offset from its phase start, phases 10 us apart (clock of 100 MHz)."""
+
+    L = 5
+
+    def stream_shape(self):
+        return 2, 4
+
+    def stream_trace(self, token, pos, nwg, nwk):
+        import numpy as np
+        NP = 4 * self.L + 1
+        E = 1 + 6 * NP
+        ctl = np.zeros((nwg, E), np.uint64)
+        for b in range(nwg):
+            ctl[b, 0] = 1000
+            for p in range(NP):
+                t0 = 1000 + 1000 * p + 10 * b
+                # start, flags seen +1 us, ready +3, workers +8, published +9, attention +9.5
+                for i, dt in zip(range(1, 7), (0, 100, 300, 800, 900, 950)):
+                    ctl[b, i + 6 * p] = t0 + dt
+        return ctl, np.zeros((nwg, nwk, NP), np.uint64)
+
+
+def test_stream_trace_summary():
+    cfg = type("C", (), {"n_layers": _FakeTraceCtx.L})()
+    tr = bench.stream_trace(_FakeTraceCtx(), cfg, 1, 3)
+    for n in ("qkv", "wo", "w13", "w2"):
+        assert tr[n]["wait_us"] == pytest.approx(1.0)
+        assert tr[n]["prologue_us"] == pytest.approx(2.0)
+        assert tr[n]["workers_us"] == pytest.approx(5.0)
+        assert tr[n]["epilogue_us"] == pytest.approx(1.0)
+        assert tr[n]["publish_spread_us"] == pytest.approx(0.05)
+    assert tr["qkv"]["attention_us"] == pytest.approx(0.5)
+    assert "attention_us" not in tr["wo"]
+    assert tr["per_layer_us"] == pytest.approx(40.0)
+    text = bench.format_stream_trace(tr, "title", "python bench.py")
+    assert "per_layer_us: 40.00" in text and text.startswith("title\n=====")
