@@ -340,17 +340,19 @@ int l2d_use_graph(l2d_ctx* ctx, int32_t enable);
  * The same step as one persistent kernel: a single cooperative launch per
  * l2d_forward / l2d_forward_greedy (the toy forward pass of the mht18 essay,
  * section 2.3, every phase computed as above, with the same arithmetic and
- * order, so the results equal the per-phase kernels' bit for bit). Worker
- * waves stream the weights through all matvec phases without a break;
- * control waves run the grid barriers, prologues, epilogues and attention.
- * Available for Q8_0 with group size 64 on a device with cooperative launch
- * that can hold one workgroup per CU (dim <= 16384, hidden_dim <= 65536,
- * the head sizes l2d_init takes); enable = 1 elsewhere returns L2D_EINVAL.
- * A grid barrier that waits beyond a bounded number of polls (seconds)
- * gives up: every workgroup then ends, and the next l2d_sync,
- * l2d_last_token or l2d_read_logits returns L2D_EHIP and resets the barrier
- * state. Tracing (l2d_trace_layer) uses the per-phase kernels. Off by
- * default.
+ * order; the logits equal the per-phase kernels' bit for bit except where
+ * the attention's position split count differs, which moves only the fp64
+ * merge order). Worker waves stream the weights through all matvec phases
+ * without a break; control waves wait for the other workgroups' progress
+ * flags and run the prologues, epilogues and attention. Available for Q8_0
+ * with group size 64 on a device with cooperative launch that can hold one
+ * workgroup per CU (dim <= 8192, hidden_dim <= 65536, the head sizes
+ * l2d_init takes); enable = 1 elsewhere returns L2D_EINVAL. A wait for
+ * another workgroup that exceeds a bounded number of polls (seconds) gives
+ * up: every workgroup then ends, and the next l2d_sync, l2d_last_token or
+ * l2d_read_logits returns L2D_EHIP and resets the flags. Tracing
+ * (l2d_trace_layer) uses the per-phase kernels. Off by default: on MI355X
+ * the per-phase kernels are faster.
  */
 int l2d_use_persistent(l2d_ctx* ctx, int32_t enable);
 

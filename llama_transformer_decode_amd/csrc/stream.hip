@@ -636,7 +636,7 @@ __device__ __forceinline__ void ctl_attention(const StreamParams& P, int l, SCtl
             uint32_t* ctr = P.head_ctr + (size_t)vg * 32;
             const uint32_t done = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const bool last = done + 1 == (uint32_t)nact;
-            if (last) st_dev(ctr, 0u);  // the next use is a later layer, after grid barriers
+            if (last) st_dev(ctr, 0u);  // the next use is a later layer, after every workgroup's flags moved on
             c->last = last ? 1 : 0;
         }
         bar();

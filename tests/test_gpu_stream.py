@@ -1,7 +1,7 @@
 """The persistent step kernel ("stream": one cooperative launch per decode
 step, worker waves streaming the weights through every matvec phase,
-control waves running the grid barriers, prologues, epilogues and
-attention) against the captured graph of per-phase kernels and the oracle.
+control waves waiting for the other workgroups' progress flags and running
+the prologues, epilogues and attention) against the captured graph of per-phase kernels and the oracle.
 
 It keeps the per-phase kernels' arithmetic and order (same Q8_0 codes of
 every matvec input, same fp64 group combine and lane reduction, same
