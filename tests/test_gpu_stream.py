@@ -11,8 +11,8 @@ CU), which changes the fp64 merge order. The oracle comparison holds it to
 the logits tolerance and the argmax rule at every step; the count of steps
 whose logits equal the graph's bit for bit is reported. Shapes cover one, two, four and eight query heads
 per kv head (eight: two attention items per kv head of four heads each),
-head sizes 32, 64 and 128, an odd vocabulary, the 7B shape at full size with
-deep positions, and decoding with the token taken on the device. The
+head sizes 32, 64 and 128, an odd vocabulary, the 7B and 70B shapes at full
+size with deep positions, and decoding with the token taken on the device. The
 longer Q8_0 trajectories (tiny 64 steps, 110M 1024 steps) run in this mode
 among the decode tests.
 """
@@ -108,35 +108,49 @@ def test_stream_not_available_for_fp32():
             ctx.use_persistent(True)
 
 
-def test_stream_7b_full_size():
-    """7B Q8_0 at full size: pos 0..7 teacher-forced, then deep positions
-    512 and 2048 over identical synthetic caches; stream against the oracle
-    and the graph."""
+def _stream_full_size(name, steps, deep):
+    """A model at full size: pos 0..steps-1 teacher-forced, then deep
+    positions over identical synthetic caches; the persistent kernel against
+    the oracle and the graph. A step the graph misses the logits tolerance
+    at is audited for near-tie code flips, as in the long trajectories
+    (test_gpu_decode): it passes when the first differing quantised input
+    differs at near ties only and the persistent kernel's logits equal the
+    graph's bit for bit; both then continue from the oracle's cache."""
     torch = need_gpu()
+    from gpu_util import copy_cache_from_oracle, near_tie_audit
     from test_gpu_decode import _fill_kv_both
-    cfg = synth.CONFIGS["7B"]
+    cfg = synth.CONFIGS[name]
     blob = synth.make_blob(cfg, synth.Q8_0)
     orc = oracle.Model(blob, synth.Q8_0)
     ctx = l2d.Context(blob, synth.Q8_0)
     try:
         tok = 1
-        for p in list(range(8)) + [512, 2048]:
-            if p >= 512:
+        for p in list(range(steps)) + list(deep):
+            if p >= steps:
                 _fill_kv_both(ctx, orc, p, seed=77 + p)
             r = orc.forward(tok, p)
-            outs = {}
+            outs, stats = {}, {}
             for mode in ("graph", "stream"):
                 ctx.use_persistent(mode == "stream")
                 ctx.forward(tok, p)
                 st = Stats()
                 st.add(p, ctx.logits(), r, ctx.last_token())
-                log(f"  7B pos {p} {mode}: {st.summary()}")
-                st.assert_ok()
-                outs[mode] = ctx.logits()
+                log(f"  {name} pos {p} {mode}: {st.summary()}")
+                outs[mode], stats[mode] = ctx.logits(), st
             sg = Stats()
             sg.add(p, outs["stream"], outs["graph"])
-            log(f"  7B pos {p} stream vs graph: {sg.summary()}")
+            log(f"  {name} pos {p} stream vs graph: {sg.summary()}")
             sg.assert_ok()
+            if stats["graph"].bad:
+                ctx.use_persistent(False)
+                layer, slot, nd, ok = near_tie_audit(ctx, orc, tok, p, cfg.n_layers)
+                log(f"  {name} pos {p}: first differing input layer {layer} slot {slot}, {nd} codes, "
+                    f"near ties only: {ok}")
+                assert ok, f"pos {p}: outside the logits tolerance, not a near tie"
+                assert np.array_equal(outs["stream"], outs["graph"]), f"pos {p}: stream differs from graph"
+                copy_cache_from_oracle(ctx, orc, p)
+            else:
+                stats["stream"].assert_ok()
             tok = int(np.argmax(r))
     finally:
         ctx.close()
@@ -144,3 +158,15 @@ def test_stream_7b_full_size():
         del blob
         gc.collect()
         torch.cuda.empty_cache()
+
+
+def test_stream_7b_full_size():
+    """7B Q8_0 at full size: pos 0..7 teacher-forced, then deep positions
+    512 and 2048."""
+    _stream_full_size("7B", 8, [512, 2048])
+
+
+def test_stream_70b_full_size():
+    """70B Q8_0 at full size (64 query heads over 8 kv heads: attention items
+    of four query heads each): pos 0..3, then deep positions 2048 and 4095."""
+    _stream_full_size("70B", 4, [2048, 4095])
