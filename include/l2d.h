@@ -121,6 +121,9 @@ int l2d_blob_parse(const void* blob, uint64_t nbytes, int32_t dtype, int32_t gro
  *   L2D_ATTN_GSPLIT      workgroups sharing one kv head's query heads
  *                        (default 2 when 8 query heads share one, else 1;
  *                        bit-identical)
+ *   L2D_CHAIN=1          per-phase step with chained launches where
+ *                        available (default off; l2d_use_chain;
+ *                        bit-identical)
  *   L2D_PREFILL_ATTN_VALU=1  batched prefill uses the vector attention kernel
  *                        for every shape (comparison only; read at each
  *                        prefill launch, not here)
@@ -319,7 +322,9 @@ void* l2d_stream(l2d_ctx* ctx);
  * avg_seconds[7] receives the mean duration per launch of each kernel class:
  * 0 q/k/v matvec (+norm, RoPE, cache write), 1 attention, 2 output matvec,
  * 3 w1/w3 matvec (+norm, SwiGLU), 4 w2 matvec, 5 classifier (+norm, argmax),
- * 6 step start (embedding row). Synchronous.
+ * 6 step start (embedding row). With chained launches (l2d_use_chain) class
+ * 1 is the attention + output matvec launch and class 3 the w1/w3 + w2
+ * launch; classes 2 and 4 then read 0. Synchronous.
  */
 int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, double* avg_seconds);
 
@@ -335,6 +340,35 @@ int l2d_profile_prefill(l2d_ctx* ctx, const int32_t* tokens, int32_t n, int32_t 
 /* 1: replay the captured graph (default); 0: launch the step's kernels one by one.
  * Applies when the persistent step kernel is off (l2d_use_persistent). */
 int l2d_use_graph(l2d_ctx* ctx, int32_t enable);
+
+/*
+ * Chained launches of the per-phase step (the layer loop of the mht18
+ * essay, section 2.3, and the Q&A page's question on the KV cache: each
+ * layer's attention over positions 0..pos, then its output projection;
+ * w1/w3 with SwiGLU, then w2), computed as above with the same arithmetic
+ * and order, so the logits equal the kernel-by-kernel step's bit for bit.
+ * enable = 1: each layer takes three launches instead of five: q/k/v; the
+ * attention and the output projection in one launch; w1/w3 and w2 in one
+ * launch. In a chained launch the second phase's workgroups follow the
+ * first's in the grid, issue their weight loads, and wait for flags that
+ * the first phase's workgroups set once their outputs are stored (the
+ * attention's o per kv head column; the Q8_0 codes of the SwiGLU output per
+ * group). Available for Q8_0 with group size 64, up to 4 query heads per
+ * attention workgroup (whose o fills whole 128-byte lines), dim <= 8192 and
+ * the head sizes l2d_init takes; enable = 1 elsewhere returns L2D_EINVAL.
+ * Off by default (L2D_CHAIN=1 in the environment at l2d_init turns it on):
+ * on MI355X the hand-over through device memory costs as much as the launch
+ * boundary it replaces, and the 7B Q8_0 step runs slower chained (449
+ * against 472 tok/s at pos 512). Re-captures the step graph
+ * (synchronous). A wait that exceeds a bounded number of polls (about a
+ * quarter second) gives up, later waits of the step give up at once, and
+ * the next l2d_sync, l2d_last_token or l2d_read_logits returns L2D_EHIP.
+ */
+int l2d_use_chain(l2d_ctx* ctx, int32_t enable);
+
+/* 1 when the per-phase step runs with chained launches, 0 otherwise,
+ * L2D_EINVAL for a null context. */
+int l2d_chained(const l2d_ctx* ctx);
 
 /*
  * The same step as one persistent kernel: a single cooperative launch per

@@ -99,6 +99,8 @@ def lib():
             "l2d_use_persistent": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_set_sampling": (ctypes.c_int, [_vp, ctypes.c_double, ctypes.c_uint64]),
             "l2d_persistent": (ctypes.c_int, [_vp]),
+            "l2d_use_chain": (ctypes.c_int, [_vp, ctypes.c_int32]),
+            "l2d_chained": (ctypes.c_int, [_vp]),
             "l2d_stream": (_vp, [_vp]),
             "l2d_profile_step": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.POINTER(ctypes.c_double)]),
@@ -123,7 +125,7 @@ EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l
            "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
            "l2d_set_sampling", "l2d_prefill", "l2d_prefill_combine", "l2d_profile_prefill", "l2d_stream_plan_check",
-           "l2d_stream_trace", "l2d_stream_shape")
+           "l2d_stream_trace", "l2d_stream_shape", "l2d_use_chain", "l2d_chained")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
 PREFILL_CLASSES = ("prep", "qkv", "attn", "wo", "w13", "w2", "start", "cls")
@@ -294,6 +296,18 @@ class Context:
         """Run each step as the one persistent step kernel (True; Q8_0 with
         group size 64) or as the captured graph of per-phase kernels (False)."""
         _check(lib().l2d_use_persistent(self._h, 1 if enable else 0), self._h)
+
+    def use_chain(self, enable: bool):
+        """Chained launches (True: attention + output projection and w1/w3 +
+        w2 in one launch each; Q8_0 with group size 64) or one launch per
+        phase (False). Re-captures the step graph."""
+        _check(lib().l2d_use_chain(self._h, 1 if enable else 0), self._h)
+
+    @property
+    def chained(self) -> bool:
+        r = lib().l2d_chained(self._h)
+        _check(r if r < 0 else 0, self._h)
+        return r == 1
 
     def stream_shape(self):
         """(workgroups, worker waves per workgroup) of the persistent step kernel."""

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libl2d.so")
 
-SOURCES = ["gemv.hip", "attn.hip", "step.hip", "stream.hip", "prefill.hip", "gemv_noalloc.hip", "ctx.cpp", "blob.cpp", "stream_check.cpp"]
+SOURCES = ["gemv.hip", "chain.hip", "attn.hip", "step.hip", "stream.hip", "prefill.hip", "gemv_noalloc.hip", "ctx.cpp", "blob.cpp", "stream_check.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -44,6 +44,8 @@ CFLAGS = [
 EXTRA = {
     "gemv.hip": ["-mllvm", "-amdgpu-promote-alloca-to-vector-limit=1024",
                  "-mllvm", "-amdgpu-promote-alloca-to-vector-max-regs=64"],
+    "chain.hip": ["-mllvm", "-amdgpu-promote-alloca-to-vector-limit=1024",
+                  "-mllvm", "-amdgpu-promote-alloca-to-vector-max-regs=64"],
 }
 
 

@@ -275,8 +275,20 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         a.G = (int32_t)ctx->G;
         a.nsplit = ctx->nsplit;
         a.gsplit = ctx->gsplit;
-        if (kt) HIP_TRY(ctx, kt->next(KC_ATTN));
-        HIP_TRY(ctx, launch_attention(a, s, kt ? &kt->cur : nullptr));
+        const bool chain = ctx->use_chain && ctx->chain_ok;
+        const int64_t ncol = ctx->nkv * ctx->gsplit;
+        ChainArgs ca;
+        ca.flags = ctx->chain_flags;
+        ca.nflags = (int32_t)ncol;
+        ca.pub = ctx->chain_flags;
+        ca.err = ctx->chain_err;
+        ca.go = ctx->chain_err + 32;
+        ca.layer = (int32_t)l;
+        ca.nlayers = (int32_t)ctx->L;
+        if (!chain) {
+            if (kt) HIP_TRY(ctx, kt->next(KC_ATTN));
+            HIP_TRY(ctx, launch_attention(a, s, kt ? &kt->cur : nullptr));
+        }
 
         // output projection + residual
         p.W = (const uint8_t*)ctx->wo + mat_bytes(dt, l * d * d);
@@ -288,8 +300,14 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.out = ctx->x;
         p.trace_q = tr ? ctx->trace_q[1] : nullptr;
         p.trace_s = tr ? ctx->trace_s[1] : nullptr;
-        if (kt) HIP_TRY(ctx, kt->next(KC_WO));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        if (chain) {
+            // attention and the output projection in one launch
+            if (kt) HIP_TRY(ctx, kt->next(KC_ATTN));
+            HIP_TRY(ctx, launch_attn_wo(a, p, ca, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        } else {
+            if (kt) HIP_TRY(ctx, kt->next(KC_WO));
+            HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        }
 
         // RMSNorm -> w1/w3 matvec -> SwiGLU
         p.W = (const uint8_t*)ctx->w13 + mat_bytes(dt, l * 2 * h * d);
@@ -308,8 +326,12 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.os = hbq ? ctx->hb_s : nullptr;
         p.octr = hbq ? ctx->hb_ctr : nullptr;
         p.ogs = (int32_t)gs;
-        if (kt) HIP_TRY(ctx, kt->next(KC_W13));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        GemvParams p13 = p;
+        if (chain) p13.oq = ctx->chain_hbq;  // one group per 128-byte line
+        if (!chain) {
+            if (kt) HIP_TRY(ctx, kt->next(KC_W13));
+            HIP_TRY(ctx, launch_gemv(ctx->dt, PRO_NORM, EPI_SWIGLU, p, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        }
         p.oq = nullptr;
         p.os = nullptr;
         p.octr = nullptr;
@@ -326,9 +348,23 @@ int enqueue_layers(l2d_ctx* ctx, bool tracing, KernelTimer* kt = nullptr)
         p.out = ctx->x;
         p.trace_q = tr ? ctx->trace_q[3] : nullptr;
         p.trace_s = tr ? ctx->trace_s[3] : nullptr;
-        if (kt) HIP_TRY(ctx, kt->next(KC_W2));
-        HIP_TRY(ctx, launch_gemv(ctx->dt, hbq ? PRO_CODES : PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s,
-                                 kt ? &kt->cur : nullptr));
+        if (chain) {
+            // w1/w3 and w2 in one launch, w2 waiting on the group flags
+            GemvParams p2 = p;
+            p2.xq = ctx->chain_hbq;
+            p2.xs = nullptr;
+            ChainArgs cf = ca;
+            cf.flags = ctx->chain_flags + ncol;
+            cf.nflags = (int32_t)(h / gs);
+            cf.pub = ctx->chain_flags + ncol;
+            cf.go = ctx->chain_err + 64;
+            if (kt) HIP_TRY(ctx, kt->next(KC_W13));
+            HIP_TRY(ctx, launch_ffn_chain(p13, p2, cf, ctx->max_blocks, s, kt ? &kt->cur : nullptr));
+        } else {
+            if (kt) HIP_TRY(ctx, kt->next(KC_W2));
+            HIP_TRY(ctx, launch_gemv(ctx->dt, hbq ? PRO_CODES : PRO_PLAIN, EPI_RESID, p, ctx->max_blocks, s,
+                                     kt ? &kt->cur : nullptr));
+        }
         p.xq = nullptr;
         p.xs = nullptr;
     }
@@ -455,7 +491,20 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
         // fits two per CU, and sizing for three left a second round of
         // workgroups (attention at pos 4095: 41.0 -> 33.3 us per layer)
         int64_t per_cu = 3;
-        const int resident = attention_blocks_per_cu((int)ctx->G, ctx->gsplit, (int)ctx->hs);
+        int resident = attention_blocks_per_cu((int)ctx->G, ctx->gsplit, (int)ctx->hs);
+        // chained launches (off by default: on MI355X the 7B Q8_0 step ran
+        // 449 tok/s chained against 472 kernel by kernel at pos 512;
+        // L2D_CHAIN=1 or l2d_use_chain turns them on). The split count is
+        // sized for the lower occupancy of the two attention instances, so
+        // switching does not change it.
+        ctx->chain_ok = chain_supported(ctx->dt, (int)ctx->gs, ctx->d, ctx->h, (int)ctx->G, ctx->gsplit,
+                                        (int)ctx->hs, ctx->max_blocks);
+        ctx->use_chain = false;
+        if (const char* e = getenv("L2D_CHAIN")) ctx->use_chain = ctx->chain_ok && atoi(e) != 0;
+        if (ctx->chain_ok) {
+            const int rc2 = attn_wo_blocks_per_cu((int)ctx->G, ctx->gsplit, (int)ctx->hs, ctx->d, (int)ctx->gs);
+            if (rc2 > 0 && (resident <= 0 || rc2 < resident)) resident = rc2;
+        }
         if (resident > 0 && resident < per_cu) per_cu = resident;
         if (const char* e = getenv("L2D_ATTN_WG_PER_CU")) per_cu = atoi(e) > 0 ? atoi(e) : per_cu;
         int64_t ns = (per_cu * cus + nv / 2) / nv;
@@ -467,6 +516,10 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     ALLOC(ctx->part_o, nparts * ctx->hs * 8);
     ALLOC(ctx->part_ml, nparts * 2 * 8);
     ALLOC(ctx->attn_ctr, (size_t)ctx->nkv * ctx->gsplit * 32 * 4);
+    const size_t chain_flag_bytes = (size_t)(ctx->nkv * ctx->gsplit + h / gs + 1) * 4;
+    ALLOC(ctx->chain_flags, chain_flag_bytes);
+    ALLOC(ctx->chain_err, 96 * 4);
+    ALLOC(ctx->chain_hbq, (size_t)(h / gs + 1) * 128);
     for (int i = 0; i < 4; i++) {
         const int64_t n = i == 3 ? h : d;
         ALLOC(ctx->trace_q[i], (size_t)n);
@@ -576,6 +629,8 @@ int init_impl(l2d_ctx* ctx, const l2d_config* cfg, const l2d_weights* w, void* s
     HIP_TRY(ctx, hipMemsetAsync(ctx->attn_ctr, 0, (size_t)ctx->nkv * ctx->gsplit * 32 * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->hb_ctr, 0, (size_t)(ctx->h / ctx->gs + 1) * kGroupCtrStride * 4, ctx->stream));
     HIP_TRY(ctx, hipMemsetAsync(ctx->step, 0, 64, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->chain_flags, 0, chain_flag_bytes, ctx->stream));
+    HIP_TRY(ctx, hipMemsetAsync(ctx->chain_err, 0, 96 * 4, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
     rc = capture(ctx);
     if (rc != L2D_OK) return rc;
@@ -719,8 +774,22 @@ hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool gre
 
 // After a synchronisation: did a wait of the step kernel give up? Then the
 // barrier state is reset and the error reported.
+int chain_check(l2d_ctx* ctx)
+{
+    if (!ctx->chain_ok) return L2D_OK;
+    uint32_t err = 0;
+    HIP_TRY(ctx, hipMemcpyAsync(&err, ctx->chain_err, 4, hipMemcpyDeviceToHost, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    if (err == 0) return L2D_OK;
+    HIP_TRY(ctx, hipMemsetAsync(ctx->chain_err, 0, 4, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    return fail(ctx, L2D_EHIP, "chained launch: a wait for the first phase gave up; the step's results are invalid");
+}
+
 int stream_check(l2d_ctx* ctx)
 {
+    const int rc = chain_check(ctx);
+    if (rc != L2D_OK) return rc;
     if (!ctx->stream_pending) return L2D_OK;
     uint32_t err = 0;
     HIP_TRY(ctx, hipMemcpyAsync(&err, ctx->ssync->err, 4, hipMemcpyDeviceToHost, ctx->stream));
@@ -1361,6 +1430,30 @@ int l2d_use_graph(l2d_ctx* ctx, int32_t enable)
     if (!ctx) return fail(nullptr, L2D_EINVAL, "use_graph: null context");
     ctx->use_graph = enable != 0;
     return L2D_OK;
+}
+
+int l2d_use_chain(l2d_ctx* ctx, int32_t enable)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "use_chain: null context");
+    if (enable && !ctx->chain_ok)
+        return fail(ctx, L2D_EINVAL,
+                    "use_chain: chained launches are built for Q8_0 with group size 64, at most 4 query "
+                    "heads per attention workgroup and dim <= 8192; not available for this model");
+    if ((enable != 0) == ctx->use_chain) return L2D_OK;
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->use_chain = enable != 0;
+    // the captured graph holds the launches: capture the step again
+    if (ctx->exec) HIP_TRY(ctx, hipGraphExecDestroy(ctx->exec));
+    if (ctx->graph) HIP_TRY(ctx, hipGraphDestroy(ctx->graph));
+    ctx->exec = nullptr;
+    ctx->graph = nullptr;
+    return capture(ctx);
+}
+
+int l2d_chained(const l2d_ctx* ctx)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "chained: null context");
+    return ctx->use_chain && ctx->chain_ok ? 1 : 0;
 }
 
 }  // extern "C"

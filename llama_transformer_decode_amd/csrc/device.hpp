@@ -332,6 +332,10 @@ __device__ __forceinline__ i32x4 quant16(const float* v, int lpg, float* scale_o
 
 // One wave quantises group y[0, gs) (values read with device-scope loads):
 // lane l takes elements l, l + 64, ...; codes to q[0, gs), the scale to *s.
+// DEV: the codes and scale are stored at device scope (a reader in the same
+// launch on another XCD), codes four to a 32-bit word (gs a multiple of 4);
+// the caller lays the group out in a line of its own.
+template <bool DEV>
 __device__ __forceinline__ void quantize_group_wave(const float* y, int gs, int8_t* q, float* s, int lane)
 {
     constexpr int kMaxPer = 4;  // gs <= 256
@@ -348,9 +352,22 @@ __device__ __forceinline__ void quantize_group_wave(const float* y, int gs, int8
 #pragma unroll
     for (int k = 0; k < kMaxPer; k++) {
         const int i = lane + k * kWave;
-        if (i < gs) q[i] = (int8_t)q80_code(v[k], sc);
+        if constexpr (DEV) {
+            // lanes 4j .. 4j+3 hold elements 4j .. 4j+3 of this pass: OR
+            // their bytes into one word, which lane 4j stores
+            const int c = i < gs ? q80_code(v[k], sc) : 0;
+            int w = (c & 0xFF) << (8 * (lane & 3));
+            w |= dpp_xor1(w);
+            w |= dpp_xor2(w);
+            if ((lane & 3) == 0 && i < gs) st_dev((uint32_t*)(q + i), (uint32_t)w);
+        } else {
+            if (i < gs) q[i] = (int8_t)q80_code(v[k], sc);
+        }
     }
-    if (lane == 0) *s = sc;
+    if (lane == 0) {
+        if constexpr (DEV) st_dev(s, sc);
+        else *s = sc;
+    }
 }
 
 // Called by a whole wave after it has stored y[lo, hi) with device-scope
@@ -360,9 +377,15 @@ __device__ __forceinline__ void quantize_group_wave(const float* y, int gs, int8
 // group back, quantises it into q/s and resets the counter for the next
 // use. A range holding a whole group quantises it without counting.
 // Counter g sits at ctr[g * ctr_stride].
+// PUB (a chained launch, whose second phase reads the codes): group g takes
+// the 128-byte line q + 128 g (its gs <= 64 codes, then its scale at byte
+// 64; s is unused), stored at device scope, and once they are complete the
+// group's flag pub[g] is set to epoch.
+template <bool PUB>
 __device__ __forceinline__ void quantize_completed_groups(const float* y, int64_t lo, int64_t hi, int gs,
                                                           int8_t* q, float* s, uint32_t* ctr,
-                                                          int ctr_stride, int lane)
+                                                          int ctr_stride, int lane, uint32_t* pub,
+                                                          uint32_t epoch)
 {
     if (lo >= hi) return;
     wait_vm_all();
@@ -380,7 +403,16 @@ __device__ __forceinline__ void quantize_completed_groups(const float* y, int64_
             last = old + cnt == (uint32_t)gs;
             if (last && lane == 0) st_dev(ctr + g * ctr_stride, 0u);
         }
-        if (last) quantize_group_wave(y + g * gs, gs, q + g * gs, s + g, lane);
+        if (last) {
+            if constexpr (PUB)
+                quantize_group_wave<true>(y + g * gs, gs, q + g * 128, (float*)(q + g * 128 + 64), lane);
+            else
+                quantize_group_wave<false>(y + g * gs, gs, q + g * gs, s + g, lane);
+            if constexpr (PUB) {
+                wait_vm_all();
+                if (lane == 0) st_dev(pub + g, epoch);
+            }
+        }
     }
 }
 

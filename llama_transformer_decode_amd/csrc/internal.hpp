@@ -15,8 +15,9 @@ enum Dt { DT_F32 = 0, DT_Q8 = 1, DT_Q4 = 2 };
 
 // The device step record (int32 words), written by the step-start kernel:
 // token, pos, then the sampler's seed (uint64) and temperature (fp64; 0 =
-// greedy argmax) at 8-byte aligned word offsets.
-enum { kStepToken = 0, kStepPos = 1, kStepSeed = 2, kStepTemp = 4, kStepWords = 16 };
+// greedy argmax) at 8-byte aligned word offsets, and the step serial, which
+// every step-start kernel advances by one (the epochs of chained launches).
+enum { kStepToken = 0, kStepPos = 1, kStepSeed = 2, kStepTemp = 4, kStepSerial = 6, kStepWords = 16 };
 
 // The classifier's argmax is kept in kArgmaxSlots packed 64-bit slots per
 // step parity (pos & 1), each on its own 128-byte line, so that workgroups
@@ -86,6 +87,22 @@ struct LaunchEvents {
 hipError_t launch_gemv(int dt, int pro, int epi, const GemvParams& p, int max_blocks,
                        hipStream_t s, const LaunchEvents* ev = nullptr);
 
+// A chained launch runs two consecutive phases of a layer (attention and
+// the output projection; w1/w3 and w2): the second phase's workgroups follow
+// the first's in the grid, prefetch their weights, and wait on flags the
+// first phase's workgroups set once their outputs are stored. A flag holds
+// the epoch of the launch that set it (chain_epoch: step serial x layers +
+// layer + 1), so flags need no reset between launches.
+struct ChainArgs {
+    const uint32_t* flags;  // the producer flags the second phase waits on
+    int32_t nflags;
+    uint32_t* pub;          // the flags the first phase sets (the same array)
+    uint32_t* go;           // the second phase's first workgroup sets it to the epoch
+                            // once every flag holds it; the others poll it
+    uint32_t* err;          // set when a wait gives up (zero otherwise)
+    int32_t layer, nlayers;
+};
+
 // dynamic LDS bytes the GEMV needs for an input of K values (+ the RoPE
 // table of a head of hs values for the q/k/v epilogue, else hs = 0)
 size_t gemv_lds_bytes(int dt, int64_t K, int gs, int hs);
@@ -110,6 +127,21 @@ int attention_positions_per_subchunk(int hs);
 // attention workgroups that can be resident on one CU for this shape (the
 // instance the launch would pick), or 0 if the runtime cannot tell
 int attention_blocks_per_cu(int G, int gsplit, int hs);
+
+// ---- chained launches (chain.hip): Q8_0 weights, groups of 64
+
+// true when both chained launches serve this shape (the instances built,
+// and every w1/w3 workgroup owning rows)
+bool chain_supported(int dt, int gs, int64_t d, int64_t h, int G, int gsplit, int hs, int max_blocks);
+// attention, then the output projection + residual (wo: PRO_PLAIN, EPI_RESID)
+hipError_t launch_attn_wo(const AttnParams& a, const GemvParams& wo, const ChainArgs& c, int max_blocks,
+                          hipStream_t s, const LaunchEvents* ev = nullptr);
+// w1/w3 + SwiGLU (PRO_NORM, EPI_SWIGLU, output quantised), then w2 +
+// residual on its codes (PRO_CODES, EPI_RESID)
+hipError_t launch_ffn_chain(const GemvParams& w13, const GemvParams& w2, const ChainArgs& c, int max_blocks,
+                            hipStream_t s, const LaunchEvents* ev = nullptr);
+// attention workgroups of the chained attention launch resident per CU
+int attn_wo_blocks_per_cu(int G, int gsplit, int hs, int64_t d, int gs);
 
 // ---- batched prefill (prefill.hip)
 

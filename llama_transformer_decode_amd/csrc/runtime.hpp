@@ -77,6 +77,15 @@ struct l2d_ctx {
     int nsplit = 0;
     int gsplit = 1;  // workgroups per kv head in decode attention
 
+    // chained launches (attention + output projection, w1/w3 + w2 in one
+    // launch each; Q8_0, group size 64)
+    bool chain_ok = false;             // supported for this model on this device
+    bool use_chain = false;
+    uint32_t* chain_flags = nullptr;   // [nkv * gsplit] attention columns, then [h / gs] FFN groups
+    uint32_t* chain_err = nullptr;     // [0]: set when a wait of a chained launch gives up;
+                                       // [32], [64]: the go words of the two chained launches
+    int8_t* chain_hbq = nullptr;       // [h / gs][128 bytes]: SwiGLU output codes, then scale, per group
+
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     bool use_graph = true;

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void begin_step_kernel(BeginParams p)
         p.step[kStepPos] = p.pos;
         *(uint64_t*)(p.step + kStepSeed) = p.seed;
         *(double*)(p.step + kStepTemp) = p.temperature;
+        p.step[kStepSerial] += 1;  // a new epoch for this step's chained launches
     }
     if (blockIdx.x == 0 && threadIdx.x < kArgmaxSlots)
         p.argmax[((size_t)(p.pos & 1) * kArgmaxSlots + threadIdx.x) * kArgmaxStride] = 0ull;
