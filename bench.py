@@ -52,7 +52,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_7B_decode_step_q8_0.txt")
 STATS_FILE = os.path.join(ROOT, "profiles", "kernels_7B_decode_step.txt")
 # the sources the step's decode kernels are built from: a committed summary
 # counts only while their digest is the one it records
-STEP_SOURCES = ("gemv.hip", "attn.hip", "attn_core.hpp", "device.hpp", "step.hip")
+STEP_SOURCES = ("gemv_core.hpp", "gemv.hip", "attn_decode.hpp", "attn.hip", "attn_core.hpp", "device.hpp",
+                "step.hip")
 
 
 def log(*a):
@@ -507,6 +508,8 @@ _ROLES = [
     (r"gemv_kernel<2,1,4,", "Q4_0 classifier + argmax"),
     (r"gemv_kernel<2,0,0,", "Q4_0 plain matvec (step shapes)"),
     (r"attention_kernel", "attention (splits merged in-kernel)"),
+    (r"attn_wo_kernel", "chained: attention, then Q8_0 wo + residual"),
+    (r"ffn_kernel", "chained: Q8_0 w1/w3 + SwiGLU, then w2 + residual"),
     (r"begin_step_kernel", "step start: embedding row, RoPE table"),
     (r"stream_step_kernel", "whole step, one persistent launch"),
     (r"prefill", "batched prefill"),
@@ -605,9 +608,13 @@ def main():
                     help="skip the Q4_0 matvec measurement")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the persistent step kernel measurement")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the chained-launch step measurement")
     ap.add_argument("--stream-trace-out", metavar="FILE",
                     help="also write the persistent kernel's per-phase trace summary to FILE")
     ap.add_argument("--no-70b", action="store_true", help="skip the 70B-shape Q8_0 step")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not run rocm-smi for the clocks (profiled runs)")
     ap.add_argument("--positions-70b", default="1,2048,4095")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -639,7 +646,7 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    clocks_before = gpu_clocks()
+    clocks_before = {} if args.no_clocks else gpu_clocks()
     if args.calibrate_copy:
         a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -694,6 +701,26 @@ def main():
                 ctx.use_persistent(False)
             except l2d.L2DError as e:
                 detail["q8_0_stream"] = {"unavailable": str(e)}
+        if dt == 1 and not args.no_chain:
+            # chained launches (attention + output projection, w1/w3 + w2 in
+            # one launch each; same arithmetic, off by default)
+            try:
+                ctx.use_chain(True)
+                ch = {}
+                for p in positions:
+                    tr = time_replays(ctx, fed[p], p, args.steps, args.warmup, torch, args.trials)
+                    ch[str(p)] = {"tok_s": 1.0 / tr["sec"], "ms": tr["sec"] * 1e3, "trials_ms": tr["trials_ms"]}
+                    log(f"[bench]   chained launches pos {p}: {tr['sec'] * 1e3:.3f} ms/step, {1 / tr['sec']:.1f} tok/s")
+                kc = kernel_times(ctx, fed[hp], hp, args.kernel_reps)
+                detail["q8_0_chained"] = {
+                    "per_pos": ch,
+                    "kernels_us": {"qkv": kc["qkv"] * 1e6, "attn+wo": kc["attn"] * 1e6,
+                                   "w13+w2": kc["w13"] * 1e6, "cls": kc["cls"] * 1e6}}
+                log(f"[bench]   chained launches at pos {hp}: qkv {kc['qkv'] * 1e6:.1f}us, attention + wo "
+                    f"{kc['attn'] * 1e6:.1f}us, w1/w3 + w2 {kc['w13'] * 1e6:.1f}us")
+                ctx.use_chain(False)
+            except l2d.L2DError as e:
+                detail["q8_0_chained"] = {"unavailable": str(e)}
         if not args.no_prefill and dt != 2:  # no batched prefill for 4-bit weights
             detail["prefill_" + name] = prefill_rates(cfg, ctx, torch, synth, args.prefill_tokens)
             if dt == 1:
@@ -765,7 +792,7 @@ def main():
         "hbm_step_gbs": r["step_gbs"],
         "hbm_step_frac": r["step_gbs"] / PEAK_HBM_GBS,
         "roofline": roof,
-        "clocks": {"before": clocks_before, "after": gpu_clocks()},
+        "clocks": {"before": clocks_before, "after": {} if args.no_clocks else gpu_clocks()},
         "detail": detail,
     }
     if not args.no_q4_gemv:
