@@ -4,7 +4,8 @@ each) against the kernel-by-kernel step and the oracle.
 The chained launches run the same per-phase arithmetic in the same order:
 only where the second phase's workgroups start (they follow the first
 phase's in the grid, prefetch their weights and wait on the first phase's
-flags) and how they read their input (device-scope loads) change. So the
+flags) and where the w2 input's codes sit (one group per 128-byte line)
+change. So the
 logits must equal the kernel-by-kernel step's bit for bit at every step,
 and every step must meet the oracle's logits tolerance and argmax rule.
 Shapes cover one, two, four and eight query heads per kv head (eight: two
