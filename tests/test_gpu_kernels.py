@@ -15,8 +15,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _adversarial(n, gs, rng):
-    """Values whose quotient x/scale sits exactly on k + 1/2, zero groups,
-    +-max, tiny and huge magnitudes."""
+    """Values whose quotient x/scale sits exactly on k + 1/2, within a few
+    ulp of it under a scale other than 1, zero groups, +-max, tiny and huge
+    magnitudes."""
     x = rng.standard_normal(n).astype(np.float32)
     g = x.reshape(-1, gs)
     ng = g.shape[0]
@@ -32,6 +33,14 @@ def _adversarial(n, gs, rng):
         g[i] *= np.float32(1e-30)
     for i in range(4, ng, 19):     # huge magnitudes
         g[i] *= np.float32(1e30)
+    for i in range(5, ng, 23):     # near ties: x / scale within 3 ulp of k + 1/2, scale not 1
+        m = np.float32(rng.uniform(0.5, 3.0))
+        sc = np.float32(m / np.float32(127.0))
+        k = rng.integers(-126, 126, gs).astype(np.float64)
+        base = ((k + 0.5) * np.float64(sc)).astype(np.float32)
+        step = rng.integers(-3, 4, gs).astype(np.float32)
+        g[i] = base + step * np.spacing(base)
+        g[i, 0] = m
     return g.reshape(-1)
 
 
