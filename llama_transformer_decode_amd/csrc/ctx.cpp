@@ -772,11 +772,13 @@ hipError_t launch_step_kernel(l2d_ctx* ctx, int32_t token, int32_t pos, bool gre
     return e;
 }
 
-// After a synchronisation: did a wait of the step kernel give up? Then the
-// barrier state is reset and the error reported.
+// After a synchronisation: did a wait of a chained launch give up? Then
+// the error word is cleared and the error reported (flags need no reset:
+// the next step's epoch differs).
 int chain_check(l2d_ctx* ctx)
 {
-    if (!ctx->chain_ok) return L2D_OK;
+    if (!ctx->chain_pending) return L2D_OK;
+    ctx->chain_pending = false;
     uint32_t err = 0;
     HIP_TRY(ctx, hipMemcpyAsync(&err, ctx->chain_err, 4, hipMemcpyDeviceToHost, ctx->stream));
     HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
@@ -786,6 +788,8 @@ int chain_check(l2d_ctx* ctx)
     return fail(ctx, L2D_EHIP, "chained launch: a wait for the first phase gave up; the step's results are invalid");
 }
 
+// After a synchronisation: did a wait of the step kernel give up? Then the
+// barrier state is reset and the error reported.
 int stream_check(l2d_ctx* ctx)
 {
     const int rc = chain_check(ctx);
@@ -871,6 +875,7 @@ const float* forward_impl(l2d_ctx* ctx, int32_t token, int32_t pos, bool greedy)
     } else if (enqueue_layers(ctx, tracing) != L2D_OK) {
         return nullptr;
     }
+    if (ctx->use_chain && ctx->chain_ok) ctx->chain_pending = true;
     ctx->last_pos = pos;
     return ctx->logits;
 }
@@ -1336,6 +1341,7 @@ int l2d_profile_step(l2d_ctx* ctx, int32_t token, int32_t pos, int32_t reps, dou
     for (int r = 0; r < reps; r++) {
         HIP_TRY(ctx, kt.next(KC_BEGIN));
         HIP_TRY(ctx, begin(ctx, token, pos, false, &kt.cur));
+        if (ctx->use_chain && ctx->chain_ok) ctx->chain_pending = true;
         int rc = enqueue_layers(ctx, false, &kt);
         if (rc != L2D_OK) return rc;
     }

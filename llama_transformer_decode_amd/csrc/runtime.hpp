@@ -81,6 +81,7 @@ struct l2d_ctx {
     // launch each; Q8_0, group size 64)
     bool chain_ok = false;             // supported for this model on this device
     bool use_chain = false;
+    bool chain_pending = false;        // chained launches ran since the error word was last read
     uint32_t* chain_flags = nullptr;   // [nkv * gsplit] attention columns, then [h / gs] FFN groups
     uint32_t* chain_err = nullptr;     // [0]: set when a wait of a chained launch gives up;
                                        // [32], [64]: the go words of the two chained launches
