@@ -10,9 +10,10 @@ logits must equal the kernel-by-kernel step's bit for bit at every step,
 and every step must meet the oracle's logits tolerance and argmax rule.
 Shapes cover one, two, four and eight query heads per kv head (eight: two
 attention workgroups per kv head of four heads each), head sizes 32, 64 and
-128, an odd vocabulary, the 110M and 7B shapes, switching the mode back and
-forth on one context (each switch re-captures the graph), deep positions
-over injected caches, and decoding with the token taken on the device.
+128, an odd vocabulary, the 110M, 7B, 13B and 70B shapes, switching the
+mode back and forth on one context (each switch re-captures the graph),
+deep positions over injected caches, and decoding with the token taken on
+the device.
 """
 import gc
 
@@ -165,5 +166,44 @@ def test_chain_7b_full_size():
         ctx.close()
         orc.close()
         del blob
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,deep", [("13B", 4095), ("70B", 4095)])
+def test_chain_large_shapes_bitwise(name, deep):
+    """13B (dim 5120: two input chunks per thread in the output projection,
+    four in w2) and 70B (eight query heads per kv head in attention
+    workgroups of four; w2's input of 28672 codes loaded in batches from the
+    one-group-per-line layout) at full size: pos 0..2, then a deep position
+    over a random cache, chained against kernel by kernel, bit for bit (the
+    kernel-by-kernel step meets the oracle in the decode tests)."""
+    torch = need_gpu()
+    cfg = synth.CONFIGS[name]
+    blob = synth.make_blob(cfg, synth.Q8_0)
+    ctx = l2d.Context(blob, synth.Q8_0)
+    del blob
+    gc.collect()
+    try:
+        tok = 1
+        for p in [0, 1, 2, deep]:
+            if p == deep:
+                kc, vc = ctx.kv_cache()
+                g = torch.Generator(device="cuda").manual_seed(p)
+                kc[:, :p].normal_(generator=g)
+                vc[:, :p].normal_(generator=g)
+                torch.cuda.synchronize()
+            out = {}
+            for chain in (True, False):
+                ctx.use_chain(chain)
+                assert ctx.chained == chain
+                ctx.forward(tok, p)
+                out[chain] = ctx.logits()
+            log(f"  {name} pos {p}: chained vs kernel by kernel max |d| "
+                f"{float(np.abs(out[True] - out[False]).max()):.3g}")
+            assert np.array_equal(out[True], out[False]), f"{name} pos {p}: chained differs from kernel-by-kernel"
+            tok = int(np.argmax(out[False]))
+    finally:
+        ctx.close()
         gc.collect()
         torch.cuda.empty_cache()
