@@ -145,10 +145,13 @@ def test_bad_arguments_return_errors():
         assert np.isfinite(ctx.logits()).all()
 
 
-def test_q8_activation_codes_match_oracle():
+@pytest.mark.parametrize("chain", [False, True], ids=["per_phase", "chained"])
+def test_q8_activation_codes_match_oracle(chain):
     """Per-layer quantised matvec inputs: codes equal the oracle's except
     where the oracle's |x|/scale lies within 1e-3 of k + 1/2; scales equal
-    within 1e-5 relative."""
+    within 1e-5 relative. Also with chained launches, whose output
+    projection and w2 take their inputs after a wait, the latter from the
+    one-group-per-line codes."""
     need_gpu()
     cfg = synth.CONFIGS["110M"]
     blob = synth.make_blob(cfg, synth.Q8_0)
@@ -158,6 +161,7 @@ def test_q8_activation_codes_match_oracle():
     orc.trace_layer(layer)
     n_ties = n_codes = 0
     with l2d.Context(blob, synth.Q8_0) as ctx:
+        ctx.use_chain(chain)
         ctx.trace_layer(layer)
         for p, t in enumerate(fed):
             ctx.forward(t, p)
