@@ -371,6 +371,17 @@ int l2d_use_chain(l2d_ctx* ctx, int32_t enable);
 int l2d_chained(const l2d_ctx* ctx);
 
 /*
+ * Test hook for the chained launches' failure path, forced from the host:
+ * sets their error word as a wait that gave up would. The next chained
+ * step's waits that find their flags not yet set give up at once (every
+ * workgroup still ends), and the next l2d_sync, l2d_last_token or
+ * l2d_read_logits returns L2D_EHIP and clears the word; steps after that
+ * are valid again. L2D_EINVAL when chained launches are not available for
+ * the context's model. Synchronous.
+ */
+int l2d_test_chain_fault(l2d_ctx* ctx);
+
+/*
  * The same step as one persistent kernel: a single cooperative launch per
  * l2d_forward / l2d_forward_greedy (the toy forward pass of the mht18 essay,
  * section 2.3, every phase computed as above, with the same arithmetic and

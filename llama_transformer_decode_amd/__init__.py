@@ -101,6 +101,7 @@ def lib():
             "l2d_persistent": (ctypes.c_int, [_vp]),
             "l2d_use_chain": (ctypes.c_int, [_vp, ctypes.c_int32]),
             "l2d_chained": (ctypes.c_int, [_vp]),
+            "l2d_test_chain_fault": (ctypes.c_int, [_vp]),
             "l2d_stream": (_vp, [_vp]),
             "l2d_profile_step": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.POINTER(ctypes.c_double)]),
@@ -125,7 +126,8 @@ EXPORTS = ("l2d_blob_parse", "l2d_init", "l2d_forward", "l2d_forward_greedy", "l
            "l2d_gemv_profile", "l2d_trace_layer", "l2d_trace_read",
            "l2d_use_graph", "l2d_stream", "l2d_profile_step", "l2d_use_persistent", "l2d_persistent",
            "l2d_set_sampling", "l2d_prefill", "l2d_prefill_combine", "l2d_profile_prefill", "l2d_stream_plan_check",
-           "l2d_stream_trace", "l2d_stream_shape", "l2d_use_chain", "l2d_chained")
+           "l2d_stream_trace", "l2d_stream_shape", "l2d_use_chain", "l2d_chained",
+           "l2d_test_chain_fault")
 
 KERNEL_CLASSES = ("qkv", "attn", "wo", "w13", "w2", "cls", "begin")
 PREFILL_CLASSES = ("prep", "qkv", "attn", "wo", "w13", "w2", "start", "cls")
@@ -302,6 +304,10 @@ class Context:
         w2 in one launch each; Q8_0 with group size 64) or one launch per
         phase (False). Re-captures the step graph."""
         _check(lib().l2d_use_chain(self._h, 1 if enable else 0), self._h)
+
+    def test_chain_fault(self):
+        """Test hook: set the chained launches' error word from the host."""
+        _check(lib().l2d_test_chain_fault(self._h), self._h)
 
     @property
     def chained(self) -> bool:

@@ -1462,4 +1462,15 @@ int l2d_chained(const l2d_ctx* ctx)
     return ctx->use_chain && ctx->chain_ok ? 1 : 0;
 }
 
+int l2d_test_chain_fault(l2d_ctx* ctx)
+{
+    if (!ctx) return fail(nullptr, L2D_EINVAL, "test_chain_fault: null context");
+    if (!ctx->chain_ok) return fail(ctx, L2D_EINVAL, "test_chain_fault: chained launches are not available");
+    const uint32_t one = 1;
+    HIP_TRY(ctx, hipMemcpyAsync(ctx->chain_err, &one, 4, hipMemcpyHostToDevice, ctx->stream));
+    HIP_TRY(ctx, hipStreamSynchronize(ctx->stream));
+    ctx->chain_pending = true;
+    return L2D_OK;
+}
+
 }  // extern "C"

@@ -207,3 +207,40 @@ def test_chain_large_shapes_bitwise(name, deep):
         ctx.close()
         gc.collect()
         torch.cuda.empty_cache()
+
+
+def test_chain_fault_reported_and_cleared():
+    """The failure path of the bounded waits, forced from the host (no kernel
+    is made to hang or fault): with the error word set before a chained
+    step, its waits give up wherever their flags are not yet set, the next
+    synchronisation reports L2D_EHIP, and the step after that is valid
+    again (equal to the kernel-by-kernel step's logits, and to the oracle's
+    within tolerance)."""
+    need_gpu()
+    cfg = TINY_Q8
+    blob = synth.make_blob(cfg, synth.Q8_0)
+    orc = oracle.Model(blob, synth.Q8_0)
+    with l2d.Context(blob, synth.Q8_0) as ctx:
+        ctx.use_chain(True)
+        tok = 1
+        for p in range(4):
+            ctx.forward(tok, p)
+            r = orc.forward(tok, p)
+            tok = int(np.argmax(r))
+        ctx.sync()
+        ctx.test_chain_fault()
+        ctx.forward(tok, 4)
+        with pytest.raises(l2d.L2DError) as e:
+            ctx.sync()
+        assert "gave up" in str(e.value)
+        ctx.sync()  # the word is clear again
+        # the same step again, chained and then kernel by kernel
+        ctx.forward(tok, 4)
+        chained = ctx.logits()
+        ctx.use_chain(False)
+        ctx.forward(tok, 4)
+        assert np.array_equal(chained, ctx.logits())
+        st = Stats()
+        st.add(4, chained, orc.forward(tok, 4))
+        st.assert_ok()
+    orc.close()
